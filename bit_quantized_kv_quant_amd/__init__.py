@@ -1,0 +1,23 @@
+"""MI355X (gfx950) library for attention over a 2-bit, layer-discriminative KV cache.
+
+The hot path - selective flash attention with per-key window scores,
+heavy-hitter + recent selection, 2-bit quantise-and-pack, and decode attention
+over the packed cache - runs in the HIP kernels of libminikv.so (C ABI in
+include/minikv.h).  This package is the thin Python binding.
+"""
+
+from ._lib import MinikvError, lib, status_string  # noqa: F401
+from .api import (  # noqa: F401
+    PackedCache,
+    decode_attn,
+    decode_ws_bytes,
+    keep_count,
+    packed_bytes,
+    prefill_attn,
+    prefill_attn_scores,
+    window_scores,
+    pyramid_keep,
+    quant_pack,
+    select_topk,
+    split_heavy_recent,
+)

@@ -1,0 +1,201 @@
+"""Torch-facing wrappers of the C ABI (include/minikv.h).
+
+Tensors are torch CUDA (HIP) tensors used as device memory; each wrapper checks
+dtypes / shapes / contiguity, allocates outputs when none are given, and calls
+the library on the current torch stream.  No arithmetic of the method happens
+here.
+"""
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+@dataclass
+class PackedCache:
+    """Packed 2-bit cache (layout of minikv_packed_t) held in torch tensors."""
+
+    k_codes: torch.Tensor  # uint8 [B, Hkv, n, D/4]
+    k_sz: torch.Tensor     # int32 bits of (fp16 s | fp16 z << 16) [B, Hkv, ceil(n/32), D]
+    v_codes: torch.Tensor  # uint8 [B, Hkv, n, D/4]
+    v_sz: torch.Tensor     # int32 [B, Hkv, n, D/32]
+    B: int
+    Hkv: int
+    n_keep: int
+    D: int
+
+    @staticmethod
+    def alloc(B, Hkv, n_keep, D, device="cuda"):
+        G = -(-n_keep // _lib.GROUP)
+        return PackedCache(
+            torch.empty((B, Hkv, n_keep, D // 4), dtype=torch.uint8, device=device),
+            torch.empty((B, Hkv, G, D), dtype=torch.int32, device=device),
+            torch.empty((B, Hkv, n_keep, D // 4), dtype=torch.uint8, device=device),
+            torch.empty((B, Hkv, n_keep, D // _lib.GROUP), dtype=torch.int32, device=device),
+            B, Hkv, n_keep, D)
+
+    def struct(self):
+        return _lib.PackedT(self.k_codes.data_ptr(), self.k_sz.data_ptr(), self.v_codes.data_ptr(),
+                            self.v_sz.data_ptr(), self.B, self.Hkv, self.n_keep, self.D, _lib.GROUP)
+
+    def nbytes(self):
+        return sum(t.numel() * t.element_size() for t in (self.k_codes, self.k_sz, self.v_codes, self.v_sz))
+
+
+def _check_qkv(q, k, v):
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    _need(q, torch.bfloat16, (B, Hq, T, D), "q")
+    _need(k, torch.bfloat16, (B, Hkv, T, D), "k")
+    if v is not None:
+        _need(v, torch.bfloat16, (B, Hkv, T, D), "v")
+    return B, Hq, Hkv, T, D
+
+
+def prefill_attn(q, k, v, sm_scale=None, with_o=True, o=None, lse=None):
+    """Pass 1: causal attention o (bf16, or None) and per-row lse (fp32)."""
+    B, Hq, Hkv, T, D = _check_qkv(q, k, v)
+    if with_o and o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if o is not None:
+        _need(o, torch.bfloat16, (B, Hq, T, D), "o")
+    _need(lse, torch.float32, (B, Hq, T), "lse")
+    st = _lib.lib().minikv_prefill_attn(_ptr(q), _ptr(k), _ptr(v), B, T, Hq, Hkv, D, float(sm_scale or 0.0),
+                                        _ptr(o) if o is not None else None, _ptr(lse), _stream())
+    _lib.check("minikv_prefill_attn", st)
+    return o, lse
+
+
+def window_scores(q, k, lse, window, sm_scale=None, scores=None):
+    """Pass 2 (the second kernel): per-key probability mass from the last `window` rows."""
+    B, Hq, Hkv, T, D = _check_qkv(q, k, None)
+    _need(lse, torch.float32, (B, Hq, T), "lse")
+    if scores is None:
+        scores = torch.empty((B, Hkv, T), dtype=torch.float32, device=q.device)
+    _need(scores, torch.float32, (B, Hkv, T), "scores")
+    st = _lib.lib().minikv_window_scores(_ptr(q), _ptr(k), _ptr(lse), B, T, Hq, Hkv, D, int(window),
+                                         float(sm_scale or 0.0), _ptr(scores), _stream())
+    _lib.check("minikv_window_scores", st)
+    return scores
+
+
+def prefill_attn_scores(q, k, v, window, sm_scale=None, with_o=True, o=None, lse=None, scores=None):
+    """Both passes of selective flash attention: returns (o or None, lse, scores)."""
+    B, Hq, Hkv, T, D = _check_qkv(q, k, v)
+    if with_o and o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if scores is None:
+        scores = torch.empty((B, Hkv, T), dtype=torch.float32, device=q.device)
+    if o is not None:
+        _need(o, torch.bfloat16, (B, Hq, T, D), "o")
+    _need(lse, torch.float32, (B, Hq, T), "lse")
+    _need(scores, torch.float32, (B, Hkv, T), "scores")
+    st = _lib.lib().minikv_prefill_attn_scores(
+        _ptr(q), _ptr(k), _ptr(v), B, T, Hq, Hkv, D, int(window), float(sm_scale or 0.0),
+        _ptr(o) if o is not None else None, _ptr(lse), _ptr(scores), _stream())
+    _lib.check("minikv_prefill_attn_scores", st)
+    return o, lse, scores
+
+
+def select_topk(scores, n_heavy, n_recent, idx=None):
+    B, Hkv, T = scores.shape
+    _need(scores, torch.float32, (B, Hkv, T), "scores")
+    n = n_heavy + n_recent
+    if idx is None:
+        idx = torch.empty((B, Hkv, n), dtype=torch.int32, device=scores.device)
+    _need(idx, torch.int32, (B, Hkv, n), "idx")
+    st = _lib.lib().minikv_select_topk(_ptr(scores), B, Hkv, T, int(n_heavy), int(n_recent), _ptr(idx), _stream())
+    _lib.check("minikv_select_topk", st)
+    return idx
+
+
+def quant_pack(k, v, idx=None, out=None):
+    """Quantise / pack the kept tokens of fp32 or bf16 k, v [B, Hkv, T, D]."""
+    B, Hkv, T, D = k.shape
+    if k.dtype == torch.float32:
+        dt = _lib.F32
+    elif k.dtype == torch.bfloat16:
+        dt = _lib.BF16
+    else:
+        raise TypeError("k, v must be fp32 or bf16")
+    _need(k, k.dtype, (B, Hkv, T, D), "k")
+    _need(v, k.dtype, (B, Hkv, T, D), "v")
+    n = T if idx is None else idx.shape[-1]
+    if idx is not None:
+        _need(idx, torch.int32, (B, Hkv, n), "idx")
+    if out is None:
+        out = PackedCache.alloc(B, Hkv, n, D, k.device)
+    s = out.struct()
+    st = _lib.lib().minikv_quant_pack(_ptr(k), _ptr(v), dt, _ptr(idx) if idx is not None else None,
+                                      B, Hkv, T, D, n, ctypes.byref(s), _stream())
+    _lib.check("minikv_quant_pack", st)
+    return out
+
+
+def decode_ws_bytes(B, Hq, Hkv, n_keep, D):
+    return int(_lib.lib().minikv_decode_ws_bytes(B, Hq, Hkv, n_keep, D))
+
+
+def decode_attn(q, cache, sm_scale=None, out=None, ws=None):
+    """Single-query attention over the packed cache: q bf16 [B, Hq, D] -> bf16 [B, Hq, D]."""
+    B, Hq, D = q.shape
+    _need(q, torch.bfloat16, (B, Hq, D), "q")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, torch.bfloat16, (B, Hq, D), "out")
+    need = decode_ws_bytes(B, Hq, cache.Hkv, cache.n_keep, D)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    s = cache.struct()
+    st = _lib.lib().minikv_decode_attn(_ptr(q), ctypes.byref(s), Hq, float(sm_scale or 0.0), _ptr(out),
+                                       _ptr(ws), ws.numel() * ws.element_size(), _stream())
+    _lib.check("minikv_decode_attn", st)
+    return out
+
+
+def packed_bytes(B, Hkv, n_keep, D):
+    return int(_lib.lib().minikv_packed_bytes(B, Hkv, n_keep, D))
+
+
+def keep_count(T, pct):
+    r = _lib.lib().minikv_keep_count(int(T), int(round(pct * 1000)))
+    _lib.check("minikv_keep_count", 0 if r > 0 else r)
+    return r
+
+
+def pyramid_keep(T, n_layers, layer, first_pct=30, last_pct=5):
+    r = _lib.lib().minikv_pyramid_keep(int(T), int(n_layers), int(layer), int(first_pct), int(last_pct))
+    _lib.check("minikv_pyramid_keep", 0 if r > 0 else r)
+    return r
+
+
+def split_heavy_recent(n_keep):
+    h, r = ctypes.c_int(), ctypes.c_int()
+    _lib.check("minikv_split_heavy_recent", _lib.lib().minikv_split_heavy_recent(int(n_keep), h, r))
+    return h.value, r.value

@@ -1,0 +1,85 @@
+"""Build libminikv.so (HIP, gfx950) in-tree with hipcc.
+
+    python -m bit_quantized_kv_quant_amd.build
+
+Every .hip file under csrc/ is compiled for gfx950 and linked into
+bit_quantized_kv_quant_amd/libminikv.so.  Flags: packed-fp32 instructions are
+disabled (-packed-fp32-ops), fp32 divide / sqrt stay correctly rounded, and the
+quantiser is compiled without multiply-add contraction so its codes match an
+IEEE evaluation bit for bit.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libminikv.so")
+ARCH = "gfx950"
+
+COMMON = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-fPIC",
+    "-std=c++17",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Wno-unused-command-line-argument",
+]
+PER_FILE = {
+    "quant_pack.hip": ["-ffp-contract=off"],
+}
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def sources():
+    return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def build(verbose=False, jobs=None):
+    """Compile every source and link the shared library; returns its path."""
+    cc = hipcc()
+    tmp = tempfile.mkdtemp(prefix="minikv_build_")
+    try:
+        procs, objs = [], []
+        for src in sources():
+            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+            cmd = [cc, *COMMON, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+            objs.append(obj)
+        failed = []
+        for src, p in procs:
+            out = p.communicate()[0].decode(errors="replace")
+            if p.returncode != 0:
+                failed.append((src, out))
+            elif verbose and out.strip():
+                print(out)
+        if failed:
+            msg = "\n".join(f"--- {s} ---\n{o}" for s, o in failed)
+            raise RuntimeError(f"hipcc failed:\n{msg}")
+        tmp_lib = LIB + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+        if res.returncode != 0:
+            raise RuntimeError("link failed:\n" + res.stdout.decode(errors="replace"))
+        os.replace(tmp_lib, LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,167 @@
+// C ABI of the library: argument validation (before any HIP call), launch.
+#include <math.h>
+
+#include "../../include/minikv.h"
+#include "kernels.h"
+
+namespace {
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? MINIKV_OK : MINIKV_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+float resolve_scale(float sm_scale, int D) { return sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)D); }
+
+bool supported_d(int D) { return D == 64 || D == 128; }
+
+}  // namespace
+
+extern "C" {
+
+const char* minikv_status_string(int status) {
+    switch (status) {
+        case MINIKV_OK: return "ok";
+        case MINIKV_ERR_NULL: return "a required pointer is NULL";
+        case MINIKV_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+        case MINIKV_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MINIKV_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case MINIKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case MINIKV_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t minikv_packed_bytes(int B, int Hkv, int n_keep, int D) {
+    if (B < 1 || Hkv < 1 || n_keep < 1 || D < 32 || D % 32) return 0;
+    const size_t n = (size_t)n_keep;
+    const size_t groups = (n + MINIKV_GROUP - 1) / MINIKV_GROUP;
+    const size_t per = n * D / 4 + groups * D * 4 + n * D / 4 + n * (D / MINIKV_GROUP) * 4;
+    return (size_t)B * Hkv * per;
+}
+
+size_t minikv_decode_ws_bytes(int B, int Hq, int Hkv, int n_keep, int D) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || n_keep < 1 || Hq % Hkv || !supported_d(D)) return 0;
+    return minikv::decode_ws_bytes(B, Hq, D, minikv::decode_plan(B, Hkv, n_keep));
+}
+
+int minikv_keep_count(int T, int pct_milli) {
+    if (T < 1 || pct_milli <= 0 || pct_milli > 100000) return MINIKV_ERR_SHAPE;
+    const long long n = (long long)pct_milli * T / 100000;
+    return (int)(n < 1 ? 1 : n);
+}
+
+int minikv_pyramid_keep(int T, int n_layers, int layer, int first_pct, int last_pct) {
+    if (T < 1 || n_layers < 1 || layer < 0 || layer >= n_layers || first_pct <= 0 || first_pct > 100 ||
+        last_pct <= 0 || last_pct > 100)
+        return MINIKV_ERR_SHAPE;
+    long long n;
+    if (n_layers == 1) {
+        n = (long long)first_pct * T / 100;
+    } else {
+        const long long L1 = n_layers - 1;
+        n = ((long long)first_pct * L1 + (long long)(last_pct - first_pct) * layer) * T / (100 * L1);
+    }
+    return (int)(n < 1 ? 1 : n);
+}
+
+int minikv_split_heavy_recent(int n_keep, int* n_heavy, int* n_recent) {
+    if (!n_heavy || !n_recent) return MINIKV_ERR_NULL;
+    if (n_keep < 1) return MINIKV_ERR_SHAPE;
+    *n_recent = n_keep / 5;
+    *n_heavy = n_keep - *n_recent;
+    return MINIKV_OK;
+}
+
+namespace {
+int check_prefill_args(const void* q, const void* k, const void* v, int B, int T, int Hq, int Hkv, int D) {
+    if (!q || !k || !v) return MINIKV_ERR_NULL;
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return MINIKV_ERR_SHAPE;
+    if (!supported_d(D)) return MINIKV_ERR_UNSUPPORTED;
+    if (misaligned(q) || misaligned(k) || misaligned(v)) return MINIKV_ERR_ALIGN;
+    return MINIKV_OK;
+}
+}  // namespace
+
+int minikv_prefill_attn(const void* q, const void* k, const void* v, int B, int T, int Hq, int Hkv, int D,
+                        float sm_scale, void* o, float* lse, void* stream) {
+    if (!lse) return MINIKV_ERR_NULL;
+    const int st = check_prefill_args(q, k, v, B, T, Hq, Hkv, D);
+    if (st != MINIKV_OK) return st;
+    if (misaligned(lse) || (o && misaligned(o))) return MINIKV_ERR_ALIGN;
+    return status_of(minikv::launch_prefill(q, k, v, B, T, Hq, Hkv, D, resolve_scale(sm_scale, D), o, lse,
+                                            as_stream(stream)));
+}
+
+int minikv_window_scores(const void* q, const void* k, const float* lse, int B, int T, int Hq, int Hkv, int D,
+                         int window, float sm_scale, float* scores, void* stream) {
+    if (!lse || !scores) return MINIKV_ERR_NULL;
+    const int st = check_prefill_args(q, k, k, B, T, Hq, Hkv, D);
+    if (st != MINIKV_OK) return st;
+    if (window < 1 || window > T) return MINIKV_ERR_SHAPE;
+    if (misaligned(lse) || misaligned(scores)) return MINIKV_ERR_ALIGN;
+    return status_of(minikv::launch_window_scores(q, k, lse, B, T, Hq, Hkv, D, window,
+                                                  resolve_scale(sm_scale, D), scores, as_stream(stream)));
+}
+
+int minikv_prefill_attn_scores(const void* q, const void* k, const void* v, int B, int T, int Hq, int Hkv,
+                               int D, int window, float sm_scale, void* o, float* lse, float* scores,
+                               void* stream) {
+    if (!lse || !scores) return MINIKV_ERR_NULL;
+    int st = check_prefill_args(q, k, v, B, T, Hq, Hkv, D);
+    if (st != MINIKV_OK) return st;
+    if (window < 1 || window > T) return MINIKV_ERR_SHAPE;
+    if (misaligned(lse) || misaligned(scores) || (o && misaligned(o))) return MINIKV_ERR_ALIGN;
+    st = minikv_prefill_attn(q, k, v, B, T, Hq, Hkv, D, sm_scale, o, lse, stream);
+    if (st != MINIKV_OK) return st;
+    return minikv_window_scores(q, k, lse, B, T, Hq, Hkv, D, window, sm_scale, scores, stream);
+}
+
+int minikv_select_topk(const float* scores, int B, int Hkv, int T, int n_heavy, int n_recent, int32_t* idx,
+                       void* stream) {
+    if (!scores || !idx) return MINIKV_ERR_NULL;
+    if (B < 1 || Hkv < 1 || T < 1 || n_heavy < 0 || n_recent < 0 || n_heavy + n_recent < 1 ||
+        n_heavy + n_recent > T)
+        return MINIKV_ERR_SHAPE;
+    if (T - n_recent > 65536) return MINIKV_ERR_UNSUPPORTED;
+    if (misaligned(scores) || misaligned(idx)) return MINIKV_ERR_ALIGN;
+    return status_of(minikv::launch_select_topk(scores, B, Hkv, T, n_heavy, n_recent, idx, as_stream(stream)));
+}
+
+int minikv_quant_pack(const void* k, const void* v, int in_dtype, const int32_t* idx, int B, int Hkv, int T,
+                      int D, int n_keep, const minikv_packed_t* out, void* stream) {
+    if (!k || !v || !out || !out->k_codes || !out->k_sz || !out->v_codes || !out->v_sz) return MINIKV_ERR_NULL;
+    if (B < 1 || Hkv < 1 || T < 1 || n_keep < 1 || n_keep > T) return MINIKV_ERR_SHAPE;
+    if (out->B != B || out->Hkv != Hkv || out->n_keep != n_keep || out->D != D) return MINIKV_ERR_SHAPE;
+    if (!idx && n_keep != T) return MINIKV_ERR_SHAPE;
+    if (!supported_d(D) || out->group != MINIKV_GROUP) return MINIKV_ERR_UNSUPPORTED;
+    if (in_dtype != MINIKV_F32 && in_dtype != MINIKV_BF16) return MINIKV_ERR_UNSUPPORTED;
+    if (misaligned(k) || misaligned(v) || (idx && misaligned(idx)) || misaligned(out->k_codes) ||
+        misaligned(out->k_sz) || misaligned(out->v_codes) || misaligned(out->v_sz))
+        return MINIKV_ERR_ALIGN;
+    return status_of(minikv::launch_quant_pack(k, v, in_dtype == MINIKV_BF16, idx, B, Hkv, T, D, n_keep,
+                                               out->k_codes, out->k_sz, out->v_codes, out->v_sz,
+                                               as_stream(stream)));
+}
+
+int minikv_decode_attn(const void* q, const minikv_packed_t* cache, int Hq, float sm_scale, void* out, void* ws,
+                       size_t ws_bytes, void* stream) {
+    if (!q || !cache || !out || !cache->k_codes || !cache->k_sz || !cache->v_codes || !cache->v_sz)
+        return MINIKV_ERR_NULL;
+    const int B = cache->B, Hkv = cache->Hkv, n = cache->n_keep, D = cache->D;
+    if (B < 1 || Hkv < 1 || n < 1 || Hq < 1 || Hq % Hkv) return MINIKV_ERR_SHAPE;
+    if (!supported_d(D) || cache->group != MINIKV_GROUP) return MINIKV_ERR_UNSUPPORTED;
+    const int R = Hq / Hkv;
+    if (R != 1 && R != 2 && R != 4) return MINIKV_ERR_UNSUPPORTED;
+    if (misaligned(q) || misaligned(out) || misaligned(cache->k_codes) || misaligned(cache->k_sz) ||
+        misaligned(cache->v_codes) || misaligned(cache->v_sz) || (ws && misaligned(ws)))
+        return MINIKV_ERR_ALIGN;
+    const minikv::DecodePlan plan = minikv::decode_plan(B, Hkv, n);
+    if (!ws || ws_bytes < minikv::decode_ws_bytes(B, Hq, D, plan)) return MINIKV_ERR_WORKSPACE;
+    return status_of(minikv::launch_decode(q, cache->k_codes, cache->k_sz, cache->v_codes, cache->v_sz, B, Hq,
+                                           Hkv, n, D, resolve_scale(sm_scale, D), out, ws, plan,
+                                           as_stream(stream)));
+}
+
+}  // extern "C"

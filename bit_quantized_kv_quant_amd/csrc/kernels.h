@@ -1,0 +1,38 @@
+// Internal launchers, one per kernel file.  Arguments are validated by the
+// C-ABI layer (api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace minikv {
+
+hipError_t launch_quant_pack(const void* k, const void* v, bool bf16, const int32_t* idx, int B,
+                             int Hkv, int T_ctx, int D, int n_keep, uint8_t* k_codes, uint32_t* k_sz,
+                             uint8_t* v_codes, uint32_t* v_sz, hipStream_t stream);
+
+hipError_t launch_select_topk(const float* scores, int B, int Hkv, int T_ctx, int n_heavy,
+                              int n_recent, int32_t* idx, hipStream_t stream);
+
+// Decode: split plan shared by the workspace-size query and the launcher.
+struct DecodePlan {
+    int splits;  // token ranges per (sequence, KV head)
+    int chunk;   // tokens per split (multiple of 32)
+};
+DecodePlan decode_plan(int B, int Hkv, int n_keep);
+size_t decode_ws_bytes(int B, int Hq, int D, const DecodePlan& plan);
+
+hipError_t launch_decode(const void* q, const uint8_t* k_codes, const uint32_t* k_sz,
+                         const uint8_t* v_codes, const uint32_t* v_sz, int B, int Hq, int Hkv,
+                         int n_keep, int D, float sm_scale, void* out, void* ws,
+                         const DecodePlan& plan, hipStream_t stream);
+
+hipError_t launch_prefill(const void* q, const void* k, const void* v, int B, int T_ctx, int Hq,
+                          int Hkv, int D, float sm_scale, void* o, float* lse, hipStream_t stream);
+
+hipError_t launch_window_scores(const void* q, const void* k, const float* lse, int B, int T_ctx,
+                                int Hq, int Hkv, int D, int window, float sm_scale, float* scores,
+                                hipStream_t stream);
+
+}  // namespace minikv

@@ -1,0 +1,176 @@
+// 2-bit asymmetric min/max quantise-and-pack of the kept tokens.
+//
+// Method: gptget.net summary of arXiv 2411.18077, sections 方法论 / 方法详解
+// (2-bit KV quantisation; keys quantised per channel, values per token; a
+// compact cache layout).  Group rule of this library, in IEEE fp32 with
+// round-half-even and the stored fp16 parameters:
+//   s = fp16(fl32(max - min) / 3), z = fp16(min),
+//   code = s == 0 ? 0 : clamp(rint(fl32(x - z) / s), 0, 3)
+// The file is compiled with -ffp-contract=off so no multiply-add is fused and
+// the divides stay correctly rounded; the codes then match a plain IEEE
+// evaluation bit for bit.
+//
+// HBM-bound gather: each kept row is read once (coalesced 4-byte lane loads of
+// two channels), each packed byte written once (dword stores assembled with
+// lane shuffles).
+#include "common.h"
+#include "kernels.h"
+
+#pragma clang fp contract(off)
+
+namespace minikv {
+namespace {
+
+struct Pair { float a, b; };
+
+template <typename T> __device__ __forceinline__ Pair load_pair(const T* row, int c);
+
+template <> __device__ __forceinline__ Pair load_pair<float>(const float* row, int c) {
+    float2 f = *reinterpret_cast<const float2*>(row + c);
+    return {f.x, f.y};
+}
+template <> __device__ __forceinline__ Pair load_pair<uint16_t>(const uint16_t* row, int c) {
+    uint32_t w = *reinterpret_cast<const uint32_t*>(row + c);
+    return {bf16_bits_to_f32(w & 0xFFFFu), bf16_bits_to_f32(w >> 16)};
+}
+
+struct GroupParams {
+    float s, z;
+    uint32_t word;  // fp16 s in bits 0..15, fp16 z in bits 16..31
+};
+
+__device__ __forceinline__ GroupParams group_params(float mn, float mx) {
+    float rng = mx - mn;
+    float s32 = rng / 3.0f;
+    uint32_t sb = f32_to_half_bits_rn(s32);
+    uint32_t zb = f32_to_half_bits_rn(mn);
+    return {half_bits_to_f32(sb), half_bits_to_f32(zb), sb | (zb << 16)};
+}
+
+__device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
+    if (p.s == 0.0f) return 0u;
+    float u = (x - p.z) / p.s;
+    float r = __builtin_rintf(u);
+    r = fminf(fmaxf(r, 0.0f), 3.0f);
+    return (uint32_t)r;
+}
+
+// Keys: one wave per (group of 32 kept tokens, KV head, sequence).
+// Lane l owns channels 2l, 2l+1 (D/2 active lanes).
+template <typename T, int D>
+__global__ __launch_bounds__(64) void quant_pack_k_kernel(
+    const T* __restrict__ k, const int32_t* __restrict__ idx, int T_ctx, int n_keep, int Hkv,
+    uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz) {
+    const int gi = blockIdx.x;
+    const int unit = blockIdx.z * Hkv + blockIdx.y;
+    const int lane = threadIdx.x;
+    const bool active = lane < D / 2;
+    const int c = 2 * (active ? lane : 0);
+    const int G = (n_keep + kGroup - 1) / kGroup;
+    const int t0 = gi * kGroup;
+    const int cnt = min(kGroup, n_keep - t0);
+    const T* base = k + (size_t)unit * T_ctx * D;
+    const int32_t* ids = idx ? idx + (size_t)unit * n_keep + t0 : nullptr;
+
+    Pair x[kGroup];
+    float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) {
+        if (t < cnt) {
+            const int pos = ids ? ids[t] : t0 + t;
+            x[t] = load_pair<T>(base + (size_t)pos * D, c);
+            mn0 = fminf(mn0, x[t].a); mx0 = fmaxf(mx0, x[t].a);
+            mn1 = fminf(mn1, x[t].b); mx1 = fmaxf(mx1, x[t].b);
+        } else {
+            x[t] = {0.0f, 0.0f};
+        }
+    }
+    const GroupParams p0 = group_params(mn0, mx0);
+    const GroupParams p1 = group_params(mn1, mx1);
+    if (active) {
+        uint2 w = make_uint2(p0.word, p1.word);
+        *reinterpret_cast<uint2*>(k_sz + ((size_t)unit * G + gi) * D + c) = w;
+    }
+    uint8_t* crow = k_codes + ((size_t)unit * n_keep + t0) * (D / 4);
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) {
+        if (t < cnt) {  // uniform across the wave
+            uint32_t nib = active ? (code_of(x[t].a, p0) | (code_of(x[t].b, p1) << 2)) : 0u;
+            uint32_t word = group_or<8>(nib << (4 * (lane & 7)));
+            if (active && (lane & 7) == 0)
+                *reinterpret_cast<uint32_t*>(crow + (size_t)t * (D / 4) + 4 * (lane >> 3)) = word;
+        }
+    }
+}
+
+// Values: each wave handles TW = 128/D tokens per step; lane owns two channels,
+// 16 lanes form one 32-channel group.
+template <typename T, int D, int kTokPerWave>
+__global__ __launch_bounds__(256) void quant_pack_v_kernel(
+    const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, int n_keep, int Hkv,
+    uint8_t* __restrict__ v_codes, uint32_t* __restrict__ v_sz) {
+    constexpr int LT = D / 2;         // lanes per token
+    constexpr int TW = kWave / LT;    // tokens per wave step
+    const int unit = blockIdx.z * Hkv + blockIdx.y;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int slot = lane / LT;
+    const int lt = lane % LT;
+    const int c = 2 * lt;
+    const T* base = v + (size_t)unit * T_ctx * D;
+    const int tb = (blockIdx.x * 4 + wave) * kTokPerWave;
+#pragma unroll 2
+    for (int s = 0; s < kTokPerWave; s += TW) {
+        const int t = tb + s + slot;
+        const bool valid = t < n_keep;
+        Pair x = {0.0f, 0.0f};
+        if (valid) {
+            const int pos = idx ? idx[(size_t)unit * n_keep + t] : t;
+            x = load_pair<T>(base + (size_t)pos * D, c);
+        }
+        float mn = group_min<16>(fminf(x.a, x.b));
+        float mx = group_max<16>(fmaxf(x.a, x.b));
+        const GroupParams p = group_params(mn, mx);
+        uint32_t nib = code_of(x.a, p) | (code_of(x.b, p) << 2);
+        uint32_t word = group_or<8>(nib << (4 * (lane & 7)));
+        if (valid) {
+            if ((lt & 15) == 0)
+                v_sz[((size_t)unit * n_keep + t) * (D / 32) + (lt >> 4)] = p.word;
+            if ((lt & 7) == 0)
+                *reinterpret_cast<uint32_t*>(v_codes + ((size_t)unit * n_keep + t) * (D / 4) + 4 * (lt >> 3)) = word;
+        }
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const void* k, const void* v, const int32_t* idx, int B, int Hkv, int T_ctx,
+                        int n_keep, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes, uint32_t* v_sz,
+                        hipStream_t stream) {
+    const int G = (n_keep + kGroup - 1) / kGroup;
+    dim3 gk(G, Hkv, B);
+    hipLaunchKernelGGL((quant_pack_k_kernel<T, D>), gk, dim3(64), 0, stream,
+                       static_cast<const T*>(k), idx, T_ctx, n_keep, Hkv, k_codes, k_sz);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int kTokPerWave = 8;
+    const int per_block = 4 * kTokPerWave;
+    dim3 gv((n_keep + per_block - 1) / per_block, Hkv, B);
+    hipLaunchKernelGGL((quant_pack_v_kernel<T, D, kTokPerWave>), gv, dim3(256), 0, stream,
+                       static_cast<const T*>(v), idx, T_ctx, n_keep, Hkv, v_codes, v_sz);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_pack(const void* k, const void* v, bool bf16, const int32_t* idx, int B,
+                             int Hkv, int T_ctx, int D, int n_keep, uint8_t* k_codes, uint32_t* k_sz,
+                             uint8_t* v_codes, uint32_t* v_sz, hipStream_t stream) {
+    if (bf16) {
+        if (D == 128) return launch_typed<uint16_t, 128>(k, v, idx, B, Hkv, T_ctx, n_keep, k_codes, k_sz, v_codes, v_sz, stream);
+        return launch_typed<uint16_t, 64>(k, v, idx, B, Hkv, T_ctx, n_keep, k_codes, k_sz, v_codes, v_sz, stream);
+    }
+    if (D == 128) return launch_typed<float, 128>(k, v, idx, B, Hkv, T_ctx, n_keep, k_codes, k_sz, v_codes, v_sz, stream);
+    return launch_typed<float, 64>(k, v, idx, B, Hkv, T_ctx, n_keep, k_codes, k_sz, v_codes, v_sz, stream);
+}
+
+}  // namespace minikv

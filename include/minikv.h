@@ -1,0 +1,184 @@
+/*
+ * minikv.h - C ABI of the MI355X (gfx950) library for attention over a 2-bit,
+ * layer-discriminative KV cache.
+ *
+ * The method: "MiniKV: Pushing the Limits of LLM Inference via 2-Bit
+ * Layer-Discriminative KV Cache" (paper-listing page, abstract: a 2-bit
+ * layer-discriminative KV cache kept usable by FlashAttention-style kernels),
+ * and the gptget.net summary of arXiv 2411.18077, sections 方法论 (methodology)
+ * and 方法详解 (method details): 2-bit quantisation with an adaptive
+ * (importance-based) KV policy, per-channel key quantisation, per-token value
+ * quantisation, a compact cache layout, and "selective flash attention" built
+ * from a second kernel.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, row-major, with the shapes given per call.  Shape
+ *    letters: B batch, T context tokens, Hq query heads, Hkv key/value heads
+ *    (Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv)), D head dim
+ *    (64 or 128), W observation-window rows, n_keep kept tokens.
+ *  - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *    never allocates, frees or synchronises.  Pointers must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream); every
+ *    call only enqueues work on it and returns.
+ *  - Return value: MINIKV_OK (0) or a negative MINIKV_ERR_* status.  All
+ *    argument checks run before any HIP call, so a rejected call has no effect
+ *    and needs no GPU.  Faults inside kernels surface at the caller's next
+ *    synchronisation of `stream`.
+ *  - Stateless and reentrant; calls that write the same buffers must not
+ *    overlap.
+ *  - Preconditions not checked on the device: inputs are finite and
+ *    |x| < 65504 (scales and zeros are stored in fp16).
+ */
+#ifndef MINIKV_H
+#define MINIKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MINIKV_OK = 0,
+    MINIKV_ERR_NULL = -1,        /* a required pointer is NULL */
+    MINIKV_ERR_SHAPE = -2,       /* inconsistent or out-of-range sizes */
+    MINIKV_ERR_UNSUPPORTED = -3, /* valid but not supported (D, group, dtype, T limit) */
+    MINIKV_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+    MINIKV_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+    MINIKV_ERR_LAUNCH = -6       /* the HIP runtime rejected a kernel launch */
+};
+
+enum { MINIKV_F32 = 0, MINIKV_BF16 = 1 };
+
+enum { MINIKV_GROUP = 32 };  /* quantisation group: 32 kept tokens (K) or 32 channels (V) */
+
+/*
+ * Packed 2-bit cache of n_keep tokens per (sequence, KV head): the "compact
+ * layout" of the method-details section.  All four arrays are caller-owned
+ * device buffers:
+ *   k_codes  uint8 [B][Hkv][n_keep][D/4]         4 codes per byte: channel 4m+j in bits 2j..2j+1
+ *   k_sz     uint32[B][Hkv][ceil(n_keep/32)][D]  per channel, per group of 32 kept tokens
+ *   v_codes  uint8 [B][Hkv][n_keep][D/4]
+ *   v_sz     uint32[B][Hkv][n_keep][D/32]        per token, per group of 32 channels
+ * A k_sz / v_sz word holds fp16 scale s in bits 0..15 and fp16 zero z in bits
+ * 16..31; a code c stands for c*s + z.  Kept tokens are stored in ascending
+ * position order; the last key group of a row may hold fewer than 32 tokens.
+ */
+typedef struct {
+    uint8_t *k_codes;
+    uint32_t *k_sz;
+    uint8_t *v_codes;
+    uint32_t *v_sz;
+    int32_t B, Hkv, n_keep, D, group; /* group must be MINIKV_GROUP */
+} minikv_packed_t;
+
+/*
+ * Selective flash attention (method-details section: selective flash
+ * attention from a second kernel; abstract: FlashAttention compatibility).
+ *
+ * Pass 1 - minikv_prefill_attn: causal attention over bf16 q [B][Hq][T][D],
+ * k, v [B][Hkv][T][D]:
+ *   o[b,h,i,:] = sum_{j<=i} softmax_j(q_i . k_j * sm_scale) v_j   (bf16 out, fp32 math)
+ *   lse[b,h,i] = log sum_{j<=i} exp(q_i . k_j * sm_scale)            (fp32, natural log)
+ * `o` may be NULL: only lse is written (the PV product is skipped).
+ *
+ * Pass 2 - minikv_window_scores (the second kernel): per-key probability mass
+ * from the last W rows, summed over the query heads sharing a KV head:
+ *   scores[b,g,j] = sum_{h: h/(Hq/Hkv)=g} sum_{i=T-W}^{T-1} [j<=i] exp(q_i . k_j * sm_scale - lse[b,h,i])
+ * (fp32 [B][Hkv][T]); it needs lse only for rows T-W..T-1.  No T x T matrix is
+ * stored by either pass.
+ *
+ * minikv_prefill_attn_scores enqueues pass 1 then pass 2.
+ * sm_scale <= 0 means 1/sqrt(D).
+ * Errors: NULL q/k/v/lse/scores; SHAPE if any size < 1, Hq % Hkv, W > T;
+ * UNSUPPORTED if D is not 64 or 128; ALIGN; LAUNCH.
+ */
+int minikv_prefill_attn(const void *q, const void *k, const void *v,
+                        int B, int T, int Hq, int Hkv, int D, float sm_scale,
+                        void *o, float *lse, void *stream);
+
+int minikv_window_scores(const void *q, const void *k, const float *lse,
+                         int B, int T, int Hq, int Hkv, int D, int window,
+                         float sm_scale, float *scores, void *stream);
+
+int minikv_prefill_attn_scores(const void *q, const void *k, const void *v,
+                               int B, int T, int Hq, int Hkv, int D, int window,
+                               float sm_scale, void *o, float *lse, float *scores,
+                               void *stream);
+
+/*
+ * Heavy-hitter + recent-window selection (gptget.net summary, 术语表 "adaptive
+ * KV": keep the KV states chosen by importance).
+ * scores fp32 [B][Hkv][T] (non-negative) -> idx int32 [B][Hkv][n_heavy+n_recent]:
+ * positions T-n_recent..T-1 plus the n_heavy largest scores among positions
+ * < T-n_recent (equal scores: the lower position first), ascending.
+ * Errors: NULL; SHAPE if n_heavy<0, n_recent<0, n_heavy+n_recent<1 or > T;
+ * UNSUPPORTED if T - n_recent > 65536; ALIGN; LAUNCH.
+ */
+int minikv_select_topk(const float *scores, int B, int Hkv, int T,
+                       int n_heavy, int n_recent, int32_t *idx, void *stream);
+
+/*
+ * 2-bit asymmetric min/max quantise-and-pack of the kept tokens (method
+ * details: per-channel key and per-token value quantisation, compact layout).
+ * k, v [B][Hkv][T][D] in fp32 (in_dtype MINIKV_F32) or bf16 (MINIKV_BF16);
+ * idx int32 [B][Hkv][n_keep] ascending positions (NULL keeps every token,
+ * n_keep must then equal T).  Per group (32 kept tokens x 1 channel for K,
+ * 1 token x 32 channels for V), in IEEE fp32 with round-half-even:
+ *   s = fp16(fl32(max - min) / 3), z = fp16(min),
+ *   code = s == 0 ? 0 : clamp(rint(fl32(x - z) / s), 0, 3)
+ * with the stored fp16 s, z; a short last K group uses its valid tokens only.
+ * Errors: NULL; SHAPE (sizes < 1, n_keep > T, out->B/Hkv/n_keep/D mismatch,
+ * idx NULL with n_keep != T); UNSUPPORTED (D, group != 32, in_dtype); ALIGN;
+ * LAUNCH.  idx entries outside [0, T) are not checked on the device.
+ */
+int minikv_quant_pack(const void *k, const void *v, int in_dtype, const int32_t *idx,
+                      int B, int Hkv, int T, int D, int n_keep,
+                      const minikv_packed_t *out, void *stream);
+
+/*
+ * Single-query decode attention over the packed cache, dequantising in
+ * registers (abstract: the compressed cache serves inference).
+ * q bf16 [B][Hq][D] -> out bf16 [B][Hq][D]:
+ *   out[b,h] = sum_t softmax_t(q . khat_t * sm_scale) vhat_t over the n_keep packed tokens,
+ * khat / vhat = code * s + z.  ws: device workspace of at least
+ * minikv_decode_ws_bytes(B, Hq, Hkv, n_keep, D) bytes (split partial results).
+ * sm_scale <= 0 means 1/sqrt(D).
+ * Errors: NULL; SHAPE (Hq % cache->Hkv, sizes < 1); UNSUPPORTED (D, group,
+ * Hq/Hkv not 1, 2 or 4); ALIGN; WORKSPACE; LAUNCH.
+ */
+int minikv_decode_attn(const void *q, const minikv_packed_t *cache, int Hq, float sm_scale,
+                       void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- host helpers (no GPU work) ---- */
+
+/* Bytes of the packed cache: per (sequence, KV head) n*D/4 + ceil(n/32)*D*4 +
+ * n*D/4 + n*(D/32)*4.  Returns 0 for invalid sizes. */
+size_t minikv_packed_bytes(int B, int Hkv, int n_keep, int D);
+
+/* Workspace bytes minikv_decode_attn needs for this shape (0 for invalid sizes). */
+size_t minikv_decode_ws_bytes(int B, int Hq, int Hkv, int n_keep, int D);
+
+/* Kept tokens at a budget of pct_milli/1000 percent of T: floor(pct*T/100), at least 1.
+ * (Glossary "adaptive KV".)  Returns a negative status for T < 1 or pct outside (0, 100]. */
+int minikv_keep_count(int T, int pct_milli);
+
+/* Kept tokens of `layer` of an n_layers-deep layer-discriminative ("Pyramid",
+ * notesum.ai LongBench table) cache whose budget falls linearly from first_pct %
+ * at layer 0 to last_pct % at the last layer:
+ * floor((first*(L-1) + (last-first)*layer) * T / (100*(L-1))), at least 1. */
+int minikv_pyramid_keep(int T, int n_layers, int layer, int first_pct, int last_pct);
+
+/* Split a budget into heavy and recent parts: recent = floor(n_keep/5). */
+int minikv_split_heavy_recent(int n_keep, int *n_heavy, int *n_recent);
+
+/* Static description of a status code. */
+const char *minikv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MINIKV_H */

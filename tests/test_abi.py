@@ -1,0 +1,142 @@
+"""C-ABI checks that need no GPU: exported symbols, argument validation, host helpers.
+
+Every rejected call returns its status before any HIP call, so these run on a
+machine without a GPU; no call here reaches a kernel launch.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from bit_quantized_kv_quant_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "minikv.h")
+
+A = 0x10000  # an aligned, never-dereferenced stand-in for a device pointer
+MIS = 0x10004  # misaligned stand-in
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(minikv_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_header_symbols_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_status_strings(L):
+    for st in range(0, -7, -1):
+        assert _lib.status_string(st)
+    assert _lib.status_string(-99) == "unknown status"
+
+
+def packed(B=1, Hkv=1, n=64, D=128, group=32, ptr=A):
+    return _lib.PackedT(ptr, ptr, ptr, ptr, B, Hkv, n, D, group)
+
+
+def test_prefill_validation(L):
+    f = L.minikv_prefill_attn_scores
+    args = dict(q=A, k=A, v=A, B=1, T=256, Hq=2, Hkv=2, D=64, W=16, scale=0.0, o=A, lse=A, scores=A)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(a["q"], a["k"], a["v"], a["B"], a["T"], a["Hq"], a["Hkv"], a["D"], a["W"], a["scale"],
+                 a["o"], a["lse"], a["scores"], None)
+
+    assert call(q=None) == _lib.ERR_NULL
+    assert call(lse=None) == _lib.ERR_NULL
+    assert call(scores=None) == _lib.ERR_NULL
+    assert call(B=0) == _lib.ERR_SHAPE
+    assert call(Hq=3) == _lib.ERR_SHAPE
+    assert call(W=257) == _lib.ERR_SHAPE
+    assert call(W=0) == _lib.ERR_SHAPE
+    assert call(D=96) == _lib.ERR_UNSUPPORTED
+    assert call(k=MIS) == _lib.ERR_ALIGN
+    assert call(o=MIS) == _lib.ERR_ALIGN
+
+
+def test_select_validation(L):
+    f = L.minikv_select_topk
+    assert f(None, 1, 1, 100, 10, 5, A, None) == _lib.ERR_NULL
+    assert f(A, 1, 1, 100, 10, 5, None, None) == _lib.ERR_NULL
+    assert f(A, 1, 1, 100, 90, 11, A, None) == _lib.ERR_SHAPE
+    assert f(A, 1, 1, 100, -1, 5, A, None) == _lib.ERR_SHAPE
+    assert f(A, 1, 1, 100, 0, 0, A, None) == _lib.ERR_SHAPE
+    assert f(A, 1, 1, 70000, 10, 10, A, None) == _lib.ERR_UNSUPPORTED
+    assert f(MIS, 1, 1, 100, 10, 5, A, None) == _lib.ERR_ALIGN
+
+
+def test_quant_pack_validation(L):
+    f = L.minikv_quant_pack
+    p = packed(n=64, D=128)
+    byref = ctypes.byref
+    assert f(None, A, _lib.BF16, A, 1, 1, 256, 128, 64, byref(p), None) == _lib.ERR_NULL
+    assert f(A, A, _lib.BF16, A, 1, 1, 256, 128, 64, None, None) == _lib.ERR_NULL
+    pn = packed(ptr=None)
+    assert f(A, A, _lib.BF16, A, 1, 1, 256, 128, 64, byref(pn), None) == _lib.ERR_NULL
+    assert f(A, A, _lib.BF16, A, 1, 1, 32, 128, 64, byref(p), None) == _lib.ERR_SHAPE     # n_keep > T
+    assert f(A, A, _lib.BF16, A, 2, 1, 256, 128, 64, byref(p), None) == _lib.ERR_SHAPE    # B mismatch
+    assert f(A, A, _lib.BF16, None, 1, 1, 256, 128, 64, byref(p), None) == _lib.ERR_SHAPE  # idx NULL, n != T
+    p96 = packed(D=96)
+    assert f(A, A, _lib.BF16, A, 1, 1, 256, 96, 64, byref(p96), None) == _lib.ERR_UNSUPPORTED
+    pg = packed(group=16)
+    assert f(A, A, _lib.BF16, A, 1, 1, 256, 128, 64, byref(pg), None) == _lib.ERR_UNSUPPORTED
+    assert f(A, A, 7, A, 1, 1, 256, 128, 64, byref(p), None) == _lib.ERR_UNSUPPORTED
+    assert f(A, MIS, _lib.BF16, A, 1, 1, 256, 128, 64, byref(p), None) == _lib.ERR_ALIGN
+    pm = packed(ptr=MIS)
+    assert f(A, A, _lib.BF16, A, 1, 1, 256, 128, 64, byref(pm), None) == _lib.ERR_ALIGN
+
+
+def test_decode_validation(L):
+    f = L.minikv_decode_attn
+    byref = ctypes.byref
+    p = packed(B=2, Hkv=4, n=100, D=128)
+    need = L.minikv_decode_ws_bytes(2, 8, 4, 100, 128)
+    assert need > 0
+    assert f(None, byref(p), 8, 0.0, A, A, need, None) == _lib.ERR_NULL
+    assert f(A, None, 8, 0.0, A, A, need, None) == _lib.ERR_NULL
+    assert f(A, byref(p), 8, 0.0, None, A, need, None) == _lib.ERR_NULL
+    assert f(A, byref(p), 6, 0.0, A, A, need, None) == _lib.ERR_SHAPE    # Hq % Hkv
+    assert f(A, byref(p), 32, 0.0, A, A, need, None) == _lib.ERR_UNSUPPORTED  # 8 query heads per KV head
+    p64 = packed(B=2, Hkv=4, n=100, D=96)
+    assert f(A, byref(p64), 8, 0.0, A, A, need, None) == _lib.ERR_UNSUPPORTED
+    assert f(MIS, byref(p), 8, 0.0, A, A, need, None) == _lib.ERR_ALIGN
+    assert f(A, byref(p), 8, 0.0, A, A, need - 4, None) == _lib.ERR_WORKSPACE
+    assert f(A, byref(p), 8, 0.0, A, None, need, None) == _lib.ERR_WORKSPACE
+
+
+def test_host_budget_helpers_match_oracle(L):
+    for T in (1, 7, 256, 4096, 8192, 16384, 44000, 65536):
+        for pct in (5, 15, 30, 100):
+            assert L.minikv_keep_count(T, pct * 1000) == oracle.keep_count(T, pct)
+    for L_ in (1, 2, 32, 40):
+        for layer in range(L_):
+            assert L.minikv_pyramid_keep(8192, L_, layer, 30, 5) == oracle.pyramid_keep(8192, L_, layer)
+    h, r = ctypes.c_int(), ctypes.c_int()
+    for n in (1, 4, 5, 64, 614, 2457, 6600):
+        assert L.minikv_split_heavy_recent(n, h, r) == 0
+        assert (h.value, r.value) == oracle.split_heavy_recent(n)
+    assert L.minikv_keep_count(0, 15000) == _lib.ERR_SHAPE
+    assert L.minikv_pyramid_keep(100, 4, 4, 30, 5) == _lib.ERR_SHAPE
+
+
+def test_packed_bytes_matches_oracle(L):
+    for n in (1, 31, 32, 33, 64, 614, 2457, 6600):
+        for D in (64, 128):
+            assert L.minikv_packed_bytes(3, 5, n, D) == oracle.packed_bytes_ref(3, 5, n, D)
+    assert L.minikv_packed_bytes(0, 1, 1, 128) == 0

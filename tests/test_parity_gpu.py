@@ -1,0 +1,318 @@
+"""GPU parity: every step of the HIP path against the CPU oracle on the same inputs.
+
+Integer / byte outputs (codes, fp16 scale / zero words, selected indices) must
+be bit-exact; attention outputs within max(2e-3, 1 bf16 ulp) elementwise of
+the fp64 oracle; window scores within a relative 1e-4 (fp32 logits vs fp64).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import bit_quantized_kv_quant_amd as mk
+from gpu_util import (assert_attn_close, assert_packed_equal, packed_to_np, require_gpu, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# quantise + pack
+# ---------------------------------------------------------------------------
+
+def _pack_and_compare(k, v, idx, dev):
+    kd = torch.from_numpy(k).to(dev) if isinstance(k, np.ndarray) else k
+    vd = torch.from_numpy(v).to(dev) if isinstance(v, np.ndarray) else v
+    idd = None if idx is None else torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to(dev)
+    cache = mk.quant_pack(kd, vd, idd)
+    torch.cuda.synchronize()
+    got = packed_to_np(cache)
+    ref = oracle.quant_pack_ref(to_np(kd), to_np(vd), idx)
+    assert_packed_equal(got, ref)
+    return cache
+
+
+def test_quant_pack_tiny_all_tokens(dev):
+    say("quant_pack tiny fp32 D64 T256 all tokens")
+    d = synth.tiny_inputs(0)
+    _pack_and_compare(d["k"], d["v"], None, dev)
+
+
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 77, 256])
+def test_quant_pack_bf16_ragged(dev, n):
+    say("quant_pack bf16 D128 B2 Hkv3 T300 n", n)
+    rng = np.random.default_rng(n)
+    k = synth.bf16_round(rng.standard_normal((2, 3, 300, 128)).astype(np.float32) * 3)
+    v = synth.bf16_round(rng.standard_normal((2, 3, 300, 128)).astype(np.float32))
+    idx = np.sort(np.stack([[rng.choice(300, n, replace=False) for _ in range(3)] for _ in range(2)]), -1)
+    kd = torch.from_numpy(k).to(dev).to(torch.bfloat16)
+    vd = torch.from_numpy(v).to(dev).to(torch.bfloat16)
+    _pack_and_compare(kd, vd, idx, dev)
+
+
+def test_quant_pack_special_groups(dev):
+    """Constant groups, exact ties, fp16 zero rounding up, subnormal and vanishing scales."""
+    say("quant_pack special groups fp32 D64")
+    T, D = 64, 64
+    k = np.zeros((1, 2, T, D), np.float32)
+    v = np.zeros((1, 2, T, D), np.float32)
+    k[0, 0, :, 0] = 1.25                                       # constant key group
+    k[0, 0, :, 1] = np.tile([0, 0.5, 1.5, 2.5, 3.0, 1.0, 2.0, 0.25], 8)  # ties at 0.5, 1.5, 2.5
+    k[0, 0, :, 2] = np.tile([1000.75, 1001.0], 32)             # z rounds up past the range
+    k[0, 0, :, 3] = np.tile([0.0, 2.0 ** -20], 32)             # subnormal fp16 scale
+    k[0, 0, :, 4] = np.tile([0.0, 2.0 ** -26], 32)             # scale underflows to 0
+    k[0, 0, :, 5] = np.tile([1 + 2.0 ** -11, 4.0], 32)         # z ties down to even
+    k[0, 1] = np.random.default_rng(3).standard_normal((T, D)).astype(np.float32) * 1e-6
+    v[0, 0, :, :32] = np.tile([-3.0, -2.5, -1.5, -0.5, 0.0, -1.0, -2.0, -0.75], 4)
+    v[0, 0, :, 32:] = 7.5                                      # constant value group
+    v[0, 1] = np.random.default_rng(4).standard_normal((T, D)).astype(np.float32) * 100
+    _pack_and_compare(k, v, None, dev)
+
+
+def test_quant_pack_llama7b_shape(dev):
+    """8 x 32 heads x 4096 tokens, 614 kept (bf16), every byte compared."""
+    wl = synth.WORKLOADS["llama7b_decode"]
+    say("quant_pack llama7b B8 H32 T4096 n614")
+    _, k, v, _ = synth.make_qkv(wl, dev, q_rows=1)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    idx = torch.sort(torch.rand((wl.B, wl.Hkv, wl.T), generator=g).argsort(-1)[..., :614], -1).values
+    _pack_and_compare(k, v, idx.numpy().astype(np.int32), dev)
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,n_heavy,n_recent,levels", [
+    (256, 48, 16, 0), (256, 48, 16, 5), (4096, 492, 122, 0), (4096, 492, 122, 64),
+    (1000, 0, 10, 0), (1000, 990, 10, 0), (16384, 1966, 491, 0), (44000, 5280, 1320, 0),
+    (44000, 5280, 1320, 1000), (65000, 100, 7, 0), (33, 32, 1, 3),
+])
+def test_select_matches_oracle(dev, T, n_heavy, n_recent, levels):
+    say("select T", T, "heavy", n_heavy, "recent", n_recent, "levels", levels)
+    rng = np.random.default_rng(T + n_heavy)
+    rows = 3
+    if levels:
+        s = (rng.integers(0, levels, (1, rows, T)) / levels).astype(np.float32)
+    else:
+        s = rng.random((1, rows, T), dtype=np.float32) * 0.01
+    s[0, 0, : T // 3] = 0.0 if levels else s[0, 0, : T // 3]
+    got = mk.select_topk(torch.from_numpy(s).to(dev), n_heavy, n_recent)
+    torch.cuda.synchronize()
+    ref = oracle.select_ref(s, n_heavy, n_recent)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def test_select_all_equal_and_negative_zero(dev):
+    say("select all-equal / signed zeros")
+    T = 500
+    s = np.zeros((2, 2, T), np.float32)
+    s[0, 1, ::2] = -0.0
+    s[1] = 0.125
+    got = mk.select_topk(torch.from_numpy(s).to(dev), 40, 10).cpu().numpy()
+    ref = oracle.select_ref(s, 40, 10)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(got[0, 0, :40], np.arange(40))
+
+
+# ---------------------------------------------------------------------------
+# decode over the packed cache
+# ---------------------------------------------------------------------------
+
+def _decode_case(dev, B, Hq, Hkv, n, D, seed, kmul=3.0, vstd=1.0):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, Hkv, n, D)).astype(np.float32) * kmul
+    k[..., :4] *= 8
+    v = rng.standard_normal((B, Hkv, n, D)).astype(np.float32) * vstd
+    q = synth.bf16_round(rng.standard_normal((B, Hq, D)).astype(np.float32))
+    kd = torch.from_numpy(k).to(dev).to(torch.bfloat16)
+    vd = torch.from_numpy(v).to(dev).to(torch.bfloat16)
+    cache = mk.quant_pack(kd, vd)
+    qd = torch.from_numpy(q).to(dev).to(torch.bfloat16)
+    out = mk.decode_attn(qd, cache)
+    torch.cuda.synchronize()
+    ref = oracle.decode_ref(q, packed_to_np(cache))
+    return to_np(out), ref
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,n,D", [
+    (1, 2, 2, 64, 64), (1, 1, 1, 1, 128), (2, 4, 4, 45, 128), (3, 8, 4, 300, 128), (2, 8, 2, 1000, 128),
+    (1, 4, 1, 6600, 128), (4, 2, 1, 129, 64), (8, 32, 32, 614, 128),
+])
+def test_decode_matches_oracle(dev, B, Hq, Hkv, n, D):
+    say("decode B", B, "Hq", Hq, "Hkv", Hkv, "n", n, "D", D)
+    got, ref = _decode_case(dev, B, Hq, Hkv, n, D, seed=B * 1000 + n)
+    assert_attn_close(got, ref, "decode out")
+
+
+def test_decode_single_token_is_vhat(dev):
+    say("decode single token")
+    rng = np.random.default_rng(1)
+    k = torch.from_numpy(rng.standard_normal((2, 2, 1, 128)).astype(np.float32)).to(dev)
+    v = torch.from_numpy(rng.standard_normal((2, 2, 1, 128)).astype(np.float32)).to(dev)
+    cache = mk.quant_pack(k, v)
+    q = torch.randn((2, 4, 128), device=dev).to(torch.bfloat16)
+    out = to_np(mk.decode_attn(q, cache))
+    _, vh = oracle.dequant_ref(packed_to_np(cache))
+    for h in range(4):
+        assert_attn_close(out[:, h], vh[:, h // 2, 0], "single-token decode")
+
+
+# ---------------------------------------------------------------------------
+# selective flash attention: pass 1 (o, lse) and pass 2 (window scores)
+# ---------------------------------------------------------------------------
+
+def _prefill_case(dev, q, k, v, W, rows=None, with_o=True):
+    qd, kd, vd = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v))
+    o, lse, sc = mk.prefill_attn_scores(qd, kd, vd, W, with_o=with_o)
+    torch.cuda.synchronize()
+    qb, kb, vb = (to_np(x) for x in (qd, kd, vd))
+    o_ref, lse_ref = oracle.prefill_ref(qb, kb, vb, rows=rows)
+    sc_ref = oracle.window_scores_ref(qb, kb, W)
+    sel = slice(None) if rows is None else rows
+    lse_g = to_np(lse)[:, :, sel]
+    assert np.abs(lse_g - lse_ref).max() < 2e-5 * max(1.0, np.abs(lse_ref).max())
+    if with_o:
+        assert_attn_close(to_np(o)[:, :, sel], o_ref, "prefill o")
+    scg = to_np(sc)
+    rel = np.abs(scg - sc_ref) / np.maximum(np.abs(sc_ref), 1e-6)
+    assert rel.max() < 1e-4, f"scores rel err {rel.max()}"
+    r = q.shape[1] // k.shape[1]
+    assert np.allclose(scg.sum(-1), W * r, rtol=1e-4)
+    return o, lse, sc
+
+
+def test_prefill_tiny(dev):
+    say("prefill tiny T256 H2 D64 W16")
+    d = synth.tiny_inputs(0)
+    _prefill_case(dev, d["q"], d["k"], d["v"], 16)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,D,W", [
+    (2, 4, 2, 333, 128, 40), (1, 2, 2, 1, 64, 1), (1, 8, 2, 200, 128, 32), (1, 1, 1, 129, 128, 129),
+])
+def test_prefill_ragged_gqa(dev, B, Hq, Hkv, T, D, W):
+    say("prefill B", B, "Hq", Hq, "Hkv", Hkv, "T", T, "D", D, "W", W)
+    rng = np.random.default_rng(T)
+    q = rng.standard_normal((B, Hq, T, D)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+    k[..., :4] *= 8
+    v = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+    _prefill_case(dev, q, k, v, W)
+
+
+def test_prefill_lse_only_matches(dev):
+    say("prefill without o")
+    rng = np.random.default_rng(9)
+    q, k, v = (rng.standard_normal((1, 2, 300, 128)).astype(np.float32) for _ in range(3))
+    _, lse1, sc1 = _prefill_case(dev, q, k, v, 32, with_o=True)
+    _, lse2, sc2 = _prefill_case(dev, q, k, v, 32, with_o=False)
+    assert torch.equal(lse1, lse2) and torch.equal(sc1, sc2)
+
+
+def test_prefill_16k_sampled(dev):
+    """32 heads x 16384 causal tokens: o / lse on sampled rows, every window score."""
+    wl = synth.WORKLOADS["prefill_16k"]
+    say("prefill 16k H32 D128 sampled rows")
+    q, k, v, _ = synth.make_qkv(wl, dev)
+    o, lse, sc = mk.prefill_attn_scores(q, k, v, wl.window)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, 127, 128, 129, 4095, 8191, 8192, 12345, 16256, 16383])
+    qb, kb, vb = (to_np(x) for x in (q, k, v))
+    o_ref, lse_ref = oracle.prefill_ref(qb, kb, vb, rows=rows)
+    assert_attn_close(to_np(o)[:, :, rows], o_ref, "prefill 16k o")
+    assert np.abs(to_np(lse)[:, :, rows] - lse_ref).max() < 1e-4
+    sc_ref = oracle.window_scores_ref(qb, kb, wl.window)
+    rel = np.abs(to_np(sc) - sc_ref) / np.maximum(sc_ref, 1e-6)
+    assert rel.max() < 1e-4
+
+
+# ---------------------------------------------------------------------------
+# the whole chain
+# ---------------------------------------------------------------------------
+
+def _chain(dev, q, k, v, qdec, W, n_heavy, n_recent, k_pack=None, v_pack=None):
+    """GPU chain; each step compared with the oracle fed the GPU's own inputs to that step."""
+    qd, kd, vd = (torch.from_numpy(x).to(dev).to(torch.bfloat16) if isinstance(x, np.ndarray) else x
+                  for x in (q, k, v))
+    _, _, sc = mk.prefill_attn_scores(qd, kd, vd, W, with_o=False)
+    idx = mk.select_topk(sc, n_heavy, n_recent)
+    kp = kd if k_pack is None else torch.from_numpy(k_pack).to(dev)
+    vp = vd if v_pack is None else torch.from_numpy(v_pack).to(dev)
+    cache = mk.quant_pack(kp, vp, idx)
+    qdd = torch.from_numpy(qdec).to(dev).to(torch.bfloat16) if isinstance(qdec, np.ndarray) else qdec
+    out = mk.decode_attn(qdd, cache)
+    torch.cuda.synchronize()
+    # selection: exact against the oracle run on the GPU's fp32 scores ...
+    sc_np = to_np(sc)
+    idx_np = idx.cpu().numpy()
+    assert np.array_equal(idx_np, oracle.select_ref(sc_np, n_heavy, n_recent))
+    # ... and, against the oracle's own fp64 scores, different only on near-ties
+    sc_ref = oracle.window_scores_ref(to_np(qd), to_np(kd), W)
+    idx_ref = oracle.select_ref(sc_ref, n_heavy, n_recent)
+    near = oracle.index_near_ties(sc_ref, n_heavy, n_recent)
+    flat_g = idx_np.reshape(-1, idx_np.shape[-1])
+    flat_r = idx_ref.reshape(-1, idx_ref.shape[-1])
+    n_diff = 0
+    for row in range(flat_g.shape[0]):
+        sym = set(flat_g[row].tolist()) ^ set(flat_r[row].tolist())
+        assert sym <= set(near[row].tolist()), f"row {row}: {sorted(sym)[:8]} not near-ties"
+        n_diff += len(sym)
+    # packing of the GPU's selection: bit-exact
+    ref_pack = oracle.quant_pack_ref(to_np(kp), to_np(vp), idx_np)
+    got_pack = packed_to_np(cache)
+    assert_packed_equal(got_pack, ref_pack)
+    # decode on the packed cache
+    ref_out = oracle.decode_ref(to_np(qdd), got_pack)
+    err = assert_attn_close(to_np(out), ref_out, "chain decode")
+    return n_diff, err
+
+
+def test_chain_tiny(dev):
+    say("chain tiny")
+    d = synth.tiny_inputs(0)
+    _chain(dev, synth.bf16_round(d["q"]), synth.bf16_round(d["k"]), synth.bf16_round(d["v"]),
+           synth.bf16_round(d["q_dec"]), 16, 48, 16, k_pack=d["k"], v_pack=d["v"])
+
+
+def test_chain_llama7b(dev):
+    wl = synth.WORKLOADS["llama7b_decode"]
+    say("chain llama7b B8 H32 T4096")
+    q, k, v, _ = synth.make_qkv(wl, dev)
+    qdec = synth.make_decode_q(wl, dev)
+    n_keep = oracle.keep_count(wl.T, wl.budget_pct)
+    nh, nr = oracle.split_heavy_recent(n_keep)
+    n_diff, err = _chain(dev, q, k, v, qdec, wl.window, nh, nr)
+    say("near-tie index differences:", n_diff, "decode max err:", err)
+
+
+# ---------------------------------------------------------------------------
+# determinism (races show up as run-to-run differences)
+# ---------------------------------------------------------------------------
+
+def test_repeat_runs_bit_identical(dev):
+    say("determinism")
+    wl = synth.WORKLOADS["llama7b_decode"]
+    q, k, v, _ = synth.make_qkv(wl, dev, seed=11)
+    qdec = synth.make_decode_q(wl, dev, seed=11)
+    res = []
+    for _ in range(2):
+        o, lse, sc = mk.prefill_attn_scores(q, k, v, wl.window)
+        idx = mk.select_topk(sc, 492, 122)
+        cache = mk.quant_pack(k, v, idx)
+        out = mk.decode_attn(qdec, cache)
+        torch.cuda.synchronize()
+        res.append([o.clone(), lse.clone(), sc.clone(), idx.clone(), cache.k_codes.clone(), cache.v_sz.clone(),
+                    out.clone()])
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
