@@ -1,0 +1,248 @@
+"""Benchmark of the 2-bit layer-discriminative KV-cache hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of the LLaMA2-7B-shaped
+workload (8 sequences x 32 heads x 4096 tokens, head dim 128, 15 % budget):
+
+  selective flash attention pass 1 (o, lse)  ->  pass 2 (window scores, W = 32)
+  ->  heavy-hitter + recent selection (492 + 122 tokens)
+  ->  2-bit quantise-and-pack of the kept K / V
+  ->  decode attention of one new query per sequence over the packed cache
+
+Inputs are seeded synthetic tensors already resident in HBM.  `value` is the
+whole job's token throughput: B * (T + 1) tokens (prompt plus the decoded
+token) per step.  Per-kernel durations come from HIP events recorded on the
+stream the kernels run on, over the timed steps.  Decode is additionally timed
+alone while rotating over >= 1 GB of distinct packed caches, so its HBM figure
+is not served from the 256 MB Infinity Cache.  The CPU oracle is timed on a
+bounded sample of the same work (cpu_baseline).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "2-bit KV decode-attn tokens/s + achieved HBM GB/s (% peak); prefill MFMA %"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--decode-rotation-gb", type=float, default=1.2)
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="after the timed region, run one device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+class StageTimer:
+    """HIP events around each call on the current stream; per-stage totals in ms."""
+
+    def __init__(self, torch, names):
+        self.torch = torch
+        self.names = names
+        self.events = []
+
+    def mark(self):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.events.append(ev)
+
+    def totals(self, steps):
+        n = len(self.names)
+        tot = {k: 0.0 for k in self.names}
+        for s in range(steps):
+            evs = self.events[s * (n + 1):(s + 1) * (n + 1)]
+            for i, k in enumerate(self.names):
+                tot[k] += evs[i].elapsed_time(evs[i + 1])
+        return {k: v / steps for k, v in tot.items()}
+
+
+def cpu_baseline(wl, n_heads_sample=2):
+    """Time the oracle on one sequence x a few heads of the same chain; scale to tokens/s."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    q, k, v, _ = synth.make_qkv(wl, "cpu")
+    qd = synth.make_decode_q(wl, "cpu")
+    h = n_heads_sample
+    qs = q[:1, :h].float().numpy()
+    ks = k[:1, :h].float().numpy()
+    vs = v[:1, :h].float().numpy()
+    qds = qd[:1, :h].float().numpy()
+    n_keep = oracle.keep_count(wl.T, wl.budget_pct)
+    nh, nr = oracle.split_heavy_recent(n_keep)
+    t0 = time.perf_counter()
+    oracle.prefill_ref(qs, ks, vs)
+    sc = oracle.window_scores_ref(qs, ks, wl.window)
+    idx = oracle.select_ref(sc, nh, nr)
+    packed = oracle.quant_pack_ref(ks, vs, idx)
+    oracle.decode_ref(qds, packed)
+    dt = time.perf_counter() - t0
+    per_seq = dt * wl.Hq / h            # all heads of one sequence
+    tokens = (wl.T + 1) / per_seq
+    return {"value": tokens, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 sequence x {h} of {wl.Hq} heads of the same chain ({dt:.1f} s), "
+                      f"scaled by {wl.Hq // h} to all heads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards per "
+              "(sequence, KV head) with no exchange, but this build measures a single GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_quantized_kv_quant_amd as mk
+    import synth
+
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS["llama7b_decode"]
+    B, Hq, Hkv, T, D, W = wl.B, wl.Hq, wl.Hkv, wl.T, wl.D, wl.window
+    n_keep = mk.keep_count(T, wl.budget_pct)
+    n_heavy, n_recent = mk.split_heavy_recent(n_keep)
+
+    q, k, v, _ = synth.make_qkv(wl, dev)
+    qdec = synth.make_decode_q(wl, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    scores = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Hkv, n_keep), dtype=torch.int32, device=dev)
+    cache = mk.PackedCache.alloc(B, Hkv, n_keep, D, dev)
+    out = torch.empty_like(qdec)
+    ws = torch.empty(mk.decode_ws_bytes(B, Hq, Hkv, n_keep, D), dtype=torch.uint8, device=dev)
+
+    stages = ["prefill_attn", "window_scores", "select_topk", "quant_pack", "decode_attn"]
+    timer = StageTimer(torch, stages)
+
+    def step(t=None):
+        if t:
+            t.mark()
+        mk.prefill_attn(q, k, v, o=o, lse=lse)
+        if t:
+            t.mark()
+        mk.window_scores(q, k, lse, W, scores=scores)
+        if t:
+            t.mark()
+        mk.select_topk(scores, n_heavy, n_recent, idx=idx)
+        if t:
+            t.mark()
+        mk.quant_pack(k, v, idx, out=cache)
+        if t:
+            t.mark()
+        mk.decode_attn(qdec, cache, out=out, ws=ws)
+        if t:
+            t.mark()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: whole steps, bracketed by device synchronisation
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_all0.record()
+    for _ in range(args.steps):
+        step(timer)
+    t_all1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_all0.elapsed_time(t_all1) / args.steps
+    per_stage = timer.totals(args.steps)
+    print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
+          file=sys.stderr, flush=True)
+
+    # ---- decode alone, rotating over >= 1 GB of distinct packed caches ----
+    cache_bytes = cache.nbytes()
+    n_rot = max(2, int(args.decode_rotation_gb * 1e9 / cache_bytes) + 1)
+    g = torch.Generator(device=dev).manual_seed(77)
+    rot = []
+    for i in range(n_rot):
+        perm = torch.rand((B, Hkv, T), generator=g, device=dev).argsort(-1)[..., :n_keep]
+        ridx = torch.sort(perm, -1).values.to(torch.int32).contiguous()
+        rot.append(mk.quant_pack(k, v, ridx))
+    torch.cuda.synchronize()
+    dec_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for c in rot[:2]:
+        mk.decode_attn(qdec, c, out=out, ws=ws)
+    reps = 3
+    dec_ev[0].record()
+    for _ in range(reps):
+        for c in rot:
+            mk.decode_attn(qdec, c, out=out, ws=ws)
+    dec_ev[1].record()
+    torch.cuda.synchronize()
+    dec_ms = dec_ev[0].elapsed_time(dec_ev[1]) / (reps * n_rot)
+    q_out_bytes = 2 * B * Hq * D * 2
+    dec_bytes = cache_bytes + q_out_bytes
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    del rot
+
+    if args.calibrate_copy_mb:
+        src = torch.empty(args.calibrate_copy_mb * (1 << 20), dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# calibration copy: {src.numel()} bytes read, {dst.numel()} written", file=sys.stderr)
+
+    # ---- roofline of the dominant kernel (prefill pass 1, MFMA-bound) ----
+    flops = 2.0 * D * T * (T + 1) * Hq * B   # causal pairs only: QK^T and PV
+    k1_ms = per_stage["prefill_attn"]
+    achieved = flops / (k1_ms * 1e-3) / 1e12
+    tokens_per_step = B * (T + 1)
+    value = tokens_per_step / (ms_per_step * 1e-3)
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama7b_decode chain: prefill + window scores + select + 2-bit pack + decode",
+                   "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "context": T, "window": W,
+                   "n_keep": n_keep, "n_heavy": n_heavy, "n_recent": n_recent, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_attn (fa_fwd_kernel)", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": None, "flops_per_launch": flops},
+        "stages_ms": per_stage,
+        "decode": {"tokens_per_s": B / (dec_ms * 1e-3), "ms": dec_ms, "bytes": dec_bytes,
+                   "achieved_GBs": dec_gbs, "hbm_frac": dec_gbs / PEAK_HBM_GBS, "rotated_caches": n_rot,
+                   "rotation_bytes": n_rot * cache_bytes},
+        "output_tokens_per_s": B / (ms_per_step * 1e-3),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

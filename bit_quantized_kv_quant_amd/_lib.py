@@ -8,7 +8,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libminikv.so")
+# MINIKV_LIB may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("MINIKV_LIB") or os.path.join(_HERE, "libminikv.so")
 
 OK = 0
 ERR_NULL = -1

@@ -45,40 +45,41 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose=False, jobs=None):
+def build(verbose=False, extra_flags=(), out=None):
     """Compile every source and link the shared library; returns its path."""
     cc = hipcc()
+    lib_path = out or LIB
     tmp = tempfile.mkdtemp(prefix="minikv_build_")
     try:
         procs, objs = [], []
         for src in sources():
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
-            cmd = [cc, *COMMON, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *COMMON, *extra_flags, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
             objs.append(obj)
         failed = []
         for src, p in procs:
-            out = p.communicate()[0].decode(errors="replace")
+            log = p.communicate()[0].decode(errors="replace")
             if p.returncode != 0:
-                failed.append((src, out))
-            elif verbose and out.strip():
-                print(out)
+                failed.append((src, log))
+            elif verbose and log.strip():
+                print(log)
         if failed:
             msg = "\n".join(f"--- {s} ---\n{o}" for s, o in failed)
             raise RuntimeError(f"hipcc failed:\n{msg}")
-        tmp_lib = LIB + ".tmp"
+        tmp_lib = lib_path + ".tmp"
         cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         if verbose:
             print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
         if res.returncode != 0:
             raise RuntimeError("link failed:\n" + res.stdout.decode(errors="replace"))
-        os.replace(tmp_lib, LIB)
+        os.replace(tmp_lib, lib_path)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return lib_path
 
 
 if __name__ == "__main__":
