@@ -68,9 +68,8 @@ class StageTimer:
         return {k: v / steps for k, v in tot.items()}
 
 
-def cpu_baseline(wl, n_heads_sample=2):
-    """Time the oracle on one sequence x a few heads of the same chain; scale to tokens/s."""
-    import numpy as np
+def cpu_baseline(wl, n_seq=2):
+    """Time the oracle on n_seq sequences (all heads) of the same chain; report tokens/s."""
     import torch
 
     import oracle
@@ -83,11 +82,9 @@ def cpu_baseline(wl, n_heads_sample=2):
         threads = os.cpu_count()
     q, k, v, _ = synth.make_qkv(wl, "cpu")
     qd = synth.make_decode_q(wl, "cpu")
-    h = n_heads_sample
-    qs = q[:1, :h].float().numpy()
-    ks = k[:1, :h].float().numpy()
-    vs = v[:1, :h].float().numpy()
-    qds = qd[:1, :h].float().numpy()
+    qs, ks, vs = (x[:n_seq].float().numpy() for x in (q, k, v))
+    qds = qd[:n_seq].float().numpy()
+    del q, k, v
     n_keep = oracle.keep_count(wl.T, wl.budget_pct)
     nh, nr = oracle.split_heavy_recent(n_keep)
     t0 = time.perf_counter()
@@ -97,11 +94,35 @@ def cpu_baseline(wl, n_heads_sample=2):
     packed = oracle.quant_pack_ref(ks, vs, idx)
     oracle.decode_ref(qds, packed)
     dt = time.perf_counter() - t0
-    per_seq = dt * wl.Hq / h            # all heads of one sequence
-    tokens = (wl.T + 1) / per_seq
-    return {"value": tokens, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"1 sequence x {h} of {wl.Hq} heads of the same chain ({dt:.1f} s), "
-                      f"scaled by {wl.Hq // h} to all heads"}
+    return {"value": n_seq * (wl.T + 1) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_seq} of {wl.B} sequences (all {wl.Hq} heads) of the same chain: prefill o/lse, "
+                      f"window scores, selection, quantise-pack, decode; {dt:.1f} s; BLAS threads = cores"}
+
+
+def load_traffic(path, kernel_src):
+    """HBM bytes per launch of the dominant kernel from a committed counter summary.
+
+    The summary records a hash of the kernel source it was measured on; a
+    different source means the figure is stale and None is returned.
+    """
+    import hashlib
+
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    want = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            key, val = line[2:].split(":", 1)
+            vals[key.strip()] = val.strip().strip("`")
+    if vals.get("kernel_source_sha256_16") != want:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -232,7 +253,10 @@ def main():
                    "n_keep": n_keep, "n_heavy": n_heavy, "n_recent": n_recent, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "prefill_attn (fa_fwd_kernel)", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None, "flops_per_launch": flops},
+                     "traffic": load_traffic(os.path.join(ROOT, "profiles", "fa_fwd_llama7b_hbm_traffic.md"),
+                                             os.path.join(ROOT, "bit_quantized_kv_quant_amd", "csrc",
+                                                          "prefill.hip")),
+                     "flops_per_launch": flops},
         "stages_ms": per_stage,
         "decode": {"tokens_per_s": B / (dec_ms * 1e-3), "ms": dec_ms, "bytes": dec_bytes,
                    "achieved_GBs": dec_gbs, "hbm_frac": dec_gbs / PEAK_HBM_GBS, "rotated_caches": n_rot,
