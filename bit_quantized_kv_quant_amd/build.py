@@ -16,6 +16,7 @@ import sys
 import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libminikv.so")
 ARCH = "gfx950"
@@ -28,6 +29,7 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Wno-unused-command-line-argument",
+    f"-I{INCLUDE}",
 ]
 PER_FILE = {
     "quant_pack.hip": ["-ffp-contract=off"],

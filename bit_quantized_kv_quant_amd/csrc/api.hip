@@ -1,7 +1,7 @@
 // C ABI of the library: argument validation (before any HIP call), launch.
 #include <math.h>
 
-#include "../../include/minikv.h"
+#include "minikv.h"
 #include "kernels.h"
 
 namespace {

@@ -9,9 +9,12 @@
 // (window_scores.hip) reuses lse to turn the last rows' logits into
 // probabilities without storing any T x T matrix.
 //
-// gfx950 design: a workgroup of 4 waves owns 128 query rows (32 per wave) and
+// gfx950 design: a workgroup of 8 waves owns 256 query rows (32 per wave) and
 // streams 64-key tiles of K and V through two LDS stages (XOR-swizzled 16-byte
-// chunks, register-prefetched; one barrier per tile).  Each wave computes S^T = K Q^T with
+// chunks, register-prefetched one tile ahead for V and two for K; one barrier
+// per tile).  Workgroups are ordered XCD-aware so the K/V prefix a head's query
+// blocks share stays in one L2.  Each wave software-pipelines its tiles: the
+// QK^T MFMAs of tile t+1 are issued while the softmax of tile t runs.  Each wave computes S^T = K Q^T with
 // bf16 MFMA 32x32x16, so an accumulator column is one query: a lane owns the
 // softmax state (running max, partial sum) of its query, and the row max needs
 // one permlane32 swap.  P^T is already in the B-operand layout of the second
@@ -33,6 +36,7 @@ namespace {
 #define MINIKV_FA_WAVES 8
 #endif
 constexpr int kFaWaves = MINIKV_FA_WAVES;  // waves per workgroup, 32 query rows each
+constexpr int kXcds = 8;                    // MI355X: 8 XCDs of 32 CUs, each with its own L2
 constexpr int kBN = 64;   // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -53,8 +57,8 @@ __device__ __forceinline__ int swz_v(int r) {
 
 template <int D, bool kWithO, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int T_ctx,
-    int Hq, int Hkv, float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse) {
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int B_,
+    int T_ctx, int Hq, int Hkv, int nqb, float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse) {
     constexpr int NT = 64 * WAVES;          // threads
     constexpr int BM = 32 * WAVES;          // query rows per workgroup
     constexpr int CH = D / 8;               // 16-byte chunks per row
@@ -66,10 +70,18 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sK[2 * TILE];
     __shared__ __attribute__((aligned(16))) uint16_t sV[kWithO ? 2 * TILE : 8];
 
-    const int nqb = gridDim.x;
-    const int qb = nqb - 1 - blockIdx.x;  // longest rows first
-    const int h = blockIdx.y;
-    const int b = blockIdx.z;
+    // XCD-aware order: workgroup L is dispatched to XCD L % 8.  Work item W =
+    // (L % 8) * per + L / 8 gives each XCD a contiguous run of (sequence, head)
+    // pairs, all query blocks of a head back to back (longest first), so the
+    // K/V prefix a head's blocks re-read stays in that XCD's L2.
+    const int nwork = nqb * Hq * B_;
+    const int per = (nwork + kXcds - 1) / kXcds;
+    const int W = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+    if (W >= nwork) return;
+    const int hs = W / nqb;
+    const int qb = nqb - 1 - W % nqb;
+    const int b = hs / Hq;
+    const int h = hs % Hq;
     const int g = h / (Hq / Hkv);
     const int q0 = qb * BM;
     const int wave = threadIdx.x / kWave;
@@ -94,22 +106,29 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     const int kv_end = min(T_ctx, q0 + BM);  // keys this workgroup needs
     const int ntiles = (kv_end + kBN - 1) / kBN;
 
-    // K tiles go global -> LDS directly (global_load_lds_dwordx4: lane l of an
-    // instruction fills the l-th 16-byte slot of a 1 KB run); the lane fetches the
-    // chunk that belongs in its slot under the XOR swizzle.  Rows past the end
-    // are clamped to the last row: those keys are always masked.
-    auto dma_k = [&](int n0, int buf) {
-        constexpr int kInstr = kBN * CH / kWave / WAVES;  // per wave
+    // K tiles are register-staged (global -> VGPR -> LDS, XOR-swizzled 16-byte
+    // chunks).  Rows past the end are clamped to the last row: those keys are
+    // always masked.  (A global_load_lds path would skip the VGPR hop, but the
+    // compiler then waits for every outstanding load before any LDS read.)
+    u32x4 pk[LOADS];
+    // Row and chunk of the first 16-byte chunk this thread stages; its later
+    // chunks are kRowStep rows further down.  Signed row arithmetic throughout.
+    const int row0 = (int)(threadIdx.x / CH);
+    const int col0 = 8 * (int)(threadIdx.x % CH);
+    constexpr int kRowStep = NT / CH;
+    auto tile_row = [&](int n0, int i) -> int {  // clamped source row of chunk i
+        return min(n0 + row0 + kRowStep * i, T_ctx - 1);
+    };
+    auto load_k = [&](int n0) {
 #pragma unroll
-        for (int i = 0; i < kInstr; ++i) {
-            const int run = WAVES * i + wave;
-            const int sidx = run * kWave + lane;
-            const int r = sidx / CH, pc = sidx % CH;
-            const int j = min(n0 + r, T_ctx - 1);
-            const uint16_t* src = k + (kvbase + j) * D + 8 * (pc ^ swz_k<D>(r));
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                             (__attribute__((address_space(3))) void*)(sK + buf * TILE + run * kWave * 8),
-                                             16, 0, 0);
+        for (int i = 0; i < LOADS; ++i)
+            pk[i] = *reinterpret_cast<const u32x4*>(k + (kvbase + (size_t)tile_row(n0, i)) * D + col0);
+    };
+    auto store_k = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int r = row0 + kRowStep * i, c = col0 / 8;
+            *reinterpret_cast<u32x4*>(sK + buf * TILE + r * D + 8 * (c ^ swz_k<D>(r))) = pk[i];
         }
     };
     // V tiles are register-staged so they can be converted to fp16 on the way in.
@@ -117,20 +136,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     auto load_v = [&](int n0) {
         if constexpr (kWithO) {
 #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                const int e = threadIdx.x + NT * i;
-                const int r = e / CH, c = e % CH;
-                const int j = min(n0 + r, T_ctx - 1);
-                pv[i] = *reinterpret_cast<const u32x4*>(v + (kvbase + j) * D + 8 * c);
-            }
+            for (int i = 0; i < LOADS; ++i)
+                pv[i] = *reinterpret_cast<const u32x4*>(v + (kvbase + (size_t)tile_row(n0, i)) * D + col0);
         }
     };
     auto store_v = [&](int buf) {
         if constexpr (kWithO) {
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
-                const int e = threadIdx.x + NT * i;
-                const int r = e / CH, c = e % CH;
+                const int r = row0 + kRowStep * i, c = col0 / 8;
                 f16x8 hv;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
@@ -169,12 +183,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
         voff[d] = (16 * (grp >> 1) + tj) * D + 8 * (4 * (d ^ (tj & (DB - 1))) + 2 * (grp & 1) + (tc >> 1)) +
                   4 * (tc & 1);
 
-    auto process = [&](int buf, int n0, auto mask_tag) {
-        constexpr bool kMask = decltype(mask_tag)::value;
+    // S^T = K Q^T of the tile in stage `buf`, one 32-key block at a time; a
+    // block's K operands are all requested before its MFMA chain.
+    auto qk = [&](int buf, f32x16 (&sacc)[2]) {
         const uint16_t* tk = sK + buf * TILE;
-        // S^T = K Q^T, one 32-key block at a time; the block's K operands are
-        // all requested before its MFMA chain so LDS latency overlaps
-        f32x16 sacc[2];
 #pragma unroll
         for (int bk = 0; bk < 2; ++bk) {
             bf16x8 a[KS];
@@ -186,6 +198,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
             for (int kk = 0; kk < KS; ++kk)
                 sacc[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], qreg[kk], sacc[bk], 0, 0, 0);
         }
+    };
+    // Online softmax of one tile: returns the fp16 probabilities (PV operand)
+    // and folds the fp32 row sum into lsum; rescales O when the reference max
+    // moves.  Branch-free except the (rare, wave-uniform) rescale.
+    auto softmax = [&](f32x16 (&sacc)[2], int n0, auto mask_tag, f16x8 (&pb)[2][2]) {
+        constexpr bool kMask = decltype(mask_tag)::value;
         float tmax = -INFINITY;
 #pragma unroll
         for (int bk = 0; bk < 2; ++bk) {
@@ -198,22 +216,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
             }
         }
         const float tm = fmaxf(tmax, swap_halves(tmax)) * scale_log2;
-        const bool need = tm > m_ref + 8.0f;
-        if (__ballot(need)) {  // wave-uniform
-            const float m_new = need ? tm : m_ref;
-            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-            lsum *= alpha;
-            if constexpr (kWithO) {
-#pragma unroll
-                for (int d = 0; d < DB; ++d)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
-            }
-            m_ref = m_new;
-        }
-        // probabilities: fp32 for the row sum (it defines lse, which the second
-        // kernel turns back into probabilities), fp16 for the PV operand
-        f16x8 pb[2][2];
+        const float m_new = tm > m_ref + 8.0f ? tm : m_ref;
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 1 unless the max moved
+        const bool moved = m_new != m_ref;
+        m_ref = m_new;
         float psum = 0.0f;
 #pragma unroll
         for (int bk = 0; bk < 2; ++bk) {
@@ -224,63 +230,91 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
                 pb[bk][e >> 3][e & 7] = (_Float16)p;
             }
         }
-        lsum += psum;
-        if constexpr (kWithO) {
-            // O^T += V^T P^T, one 32-wide block of the head dim at a time; the
-            // next block's V^T operands are requested before this block's MFMAs
-            // (the scheduling barrier keeps the compiler from hoisting more).
-            const _Float16* tv = reinterpret_cast<const _Float16*>(sV + buf * TILE);
-            auto read_v = [&](int d, f16x8 (&av)[2][2]) {
+        lsum = fmaf(lsum, alpha, psum);
+        return moved;
+    };
+    // O^T += V^T P^T, one 32-wide block of the head dim at a time; the next
+    // block's V^T operands are requested before this block's MFMAs.
+    auto pv_mma = [&](int buf, const f16x8 (&pb)[2][2]) {
+        const _Float16* tv = reinterpret_cast<const _Float16*>(sV + buf * TILE);
+        auto read_v = [&](int d, f16x8 (&av)[2][2]) {
 #pragma unroll
-                for (int bk = 0; bk < 2; ++bk) {
+            for (int bk = 0; bk < 2; ++bk) {
 #pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        const _Float16* p0 = tv + voff[d] + (32 * bk + 8 * s) * D;
-                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(p0));
-                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(p0 + 4 * D));
-                        const i16x4 both[2] = {lo, hi};
-                        __builtin_memcpy(&av[bk][s], both, 16);
-                    }
+                for (int s = 0; s < 2; ++s) {
+                    const _Float16* p0 = tv + voff[d] + (32 * bk + 8 * s) * D;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4*)(p0));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4*)(p0 + 4 * D));
+                    const i16x4 both[2] = {lo, hi};
+                    __builtin_memcpy(&av[bk][s], both, 16);
                 }
-            };
-            f16x8 va[2][2][2];
-            read_v(0, va[0]);
-#pragma unroll
-            for (int d = 0; d < DB; ++d) {
-                if (d + 1 < DB) read_v(d + 1, va[(d + 1) & 1]);
-#pragma unroll
-                for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-                    for (int s = 0; s < 2; ++s)
-                        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[d & 1][bk][s], pb[bk][s], oacc[d], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
             }
+        };
+        f16x8 va[2][2][2];
+        read_v(0, va[0]);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+            if (d + 1 < DB) read_v(d + 1, va[(d + 1) & 1]);
+#pragma unroll
+            for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[d & 1][bk][s], pb[bk][s], oacc[d], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    dma_k(0, 0);
+    // Software pipeline over the key tiles of this wave: while the softmax of
+    // tile t runs on the VALU, the QK^T MFMAs of tile t+1 are already issued
+    // (they read the other K stage), then tile t's PV MFMAs follow.  K is staged
+    // two tiles ahead, V one tile ahead.
+    const int t_last = __builtin_amdgcn_readfirstlane(min(qw0 / kBN, ntiles - 1));  // wave-uniform
+    load_k(0);
     load_v(0);
+    store_k(0);
     store_v(0);
-    __builtin_amdgcn_s_waitcnt(0);
+    if (ntiles > 1) {
+        load_k(kBN);
+        store_k(1);
+    }
     __syncthreads();
+    f32x16 sacc[2];
+    qk(0, sacc);
     for (int t = 0; t < ntiles; ++t) {
         const int n0 = t * kBN;
         const int buf = t & 1;
-        const bool more = t + 1 < ntiles;
-        if (more) {  // next tile into the other stage while this one is consumed
-            dma_k(n0 + kBN, buf ^ 1);
-            load_v(n0 + kBN);
+        if (t + 2 < ntiles) load_k(n0 + 2 * kBN);  // into registers; stored after this tile
+        if (t + 1 < ntiles) load_v(n0 + kBN);
+        if (t <= t_last) {
+            f16x8 pb[2][2];
+            bool moved;
+            float m_old = m_ref;
+            if (t < t_last) {
+                f32x16 snext[2];
+                qk(buf ^ 1, snext);
+                moved = softmax(sacc, n0, std::false_type{}, pb);
+                sacc[0] = snext[0];
+                sacc[1] = snext[1];
+            } else {
+                moved = softmax(sacc, n0, std::true_type{}, pb);
+            }
+            if constexpr (kWithO) {
+                if (__ballot(moved)) {  // wave-uniform, rare
+                    const float alpha = __builtin_amdgcn_exp2f(m_old - m_ref);
+#pragma unroll
+                    for (int d = 0; d < DB; ++d)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+                }
+                pv_mma(buf, pb);
+            }
         }
-        if (n0 <= qw0 + 31) {  // the wave has unmasked keys in this tile (then n0 <= qw0)
-            if (n0 + kBN - 1 > qw0)
-                process(buf, n0, std::true_type{});
-            else
-                process(buf, n0, std::false_type{});
-        }
-        if (more) store_v(buf ^ 1);
-        __builtin_amdgcn_s_waitcnt(0);
+        // K(t)'s stage was consumed by the previous iteration's QK and V(t-1)'s
+        // stage by the previous PV, so both are free: one barrier per tile.
+        if (t + 2 < ntiles) store_k(buf);
+        if (t + 1 < ntiles) store_v(buf ^ 1);
         __syncthreads();
     }
 
@@ -308,9 +342,11 @@ hipError_t launch_fa(const void* q, const void* k, const void* v, int B, int T_c
                      float sm_scale, void* o, float* lse, hipStream_t stream) {
     constexpr int WAVES = kFaWaves;
     const int nqb = (T_ctx + 32 * WAVES - 1) / (32 * WAVES);
-    hipLaunchKernelGGL((fa_fwd_kernel<D, kWithO, WAVES>), dim3(nqb, Hq, B), dim3(64 * WAVES), 0, stream,
+    const int nwork = nqb * Hq * B;
+    const int grid = (nwork + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((fa_fwd_kernel<D, kWithO, WAVES>), dim3(grid), dim3(64 * WAVES), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), T_ctx, Hq, Hkv, sm_scale * kLog2e,
+                       static_cast<const uint16_t*>(v), B, T_ctx, Hq, Hkv, nqb, sm_scale * kLog2e,
                        static_cast<__bf16*>(o), lse);
     return hipGetLastError();
 }
