@@ -8,17 +8,33 @@
 //
 // HBM-bound: the packed bytes of every kept token are read exactly once and
 // dequantised in registers; the R query heads of a KV head share each read.
-// Keys: the fp16 scale / zero of a 32-token group are folded into the query
-// once per group (qs_c = q_c * s_c * scale * log2 e, bias = sum_c q_c z_c ...),
-// so a token costs one multiply-add per channel on top of the unpack.
-// Values: w = p_t * s is formed once per (token, 32-channel group) and the zero
-// term is accumulated per group.  Softmax runs in the log2 domain (exp2).
+//
+// Unpacking: a 32-bit code word holds 16 channels.  One v_and_or puts the two
+// codes at bit position s of the word's 16-bit halves into the mantissas of two
+// fp16 numbers whose exponent is chosen so that each equals exactly
+// 2^(10-s) + code (s = 4, 6 or 8, i.e. offsets 64, 16, 4; the codes at other
+// positions are first shifted there).  Ten instructions give eight fp16 pairs
+// (channel j, channel j+8); v_dot2_f32_f16 then multiplies-and-adds two
+// channels per instruction in fp32, and the known offsets are taken out again
+// with the very same fp16 multipliers, so nothing but the multipliers is
+// rounded.
+// Keys: per 32-token group the wave folds the fp16 scale into the query,
+// x = q * scale * log2 e * s, once per channel, splits it into two fp16 parts
+// (hi = fp16(x), lo = fp16(x - hi): a single fp16 would put scores with large
+// outlier channels outside the output tolerance) and shares them through LDS;
+// a token then costs one unpack and two dot2 per channel pair, plus the fp32
+// zero-point term sum_c q_c z_c computed once per group.
+// Values: the code words of two tokens are interleaved with v_perm so that a
+// dot2 with (p1 s1, p2 s2) accumulates both tokens into one channel; the zero
+// term p z is accumulated per token.  Softmax runs in the log2 domain.
 //
 // Work split: grid (splits, Hkv, B); a workgroup of 4 waves owns a range of
-// `chunk` tokens (a multiple of 128) and walks it 128 tokens at a time, one
-// 32-token group per wave.  A lane owns 16 channels (one 32-bit code word) of a
-// token.  Partial (m, l, acc) per split go to the workspace; a small second
-// kernel merges the splits by log-sum-exp and writes bf16.
+// `chunk` tokens (a multiple of 128).  Each wave runs its own online softmax
+// over the 32-token groups wave, wave + 4, ..., with every HBM load of the
+// next group issued before the current group is processed (no workgroup
+// barrier until the end); the 4 waves then merge by log-sum-exp.  Partial
+// (m, l, acc) per split go to the workspace; a small second kernel merges the
+// splits and writes bf16.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,9 +44,38 @@ namespace {
 constexpr int kSub = 128;  // tokens per workgroup step: 4 waves x one 32-token group
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ float code_at(uint32_t word, int c) {
-    // channel c (0..15) of a 16-channel word: byte c/4, bits 2*(c%4)
-    return (float)((word >> (8 * (c >> 2) + 2 * (c & 3))) & 3u);
+// masks / exponent patterns for bit positions 4, 6, 8 of both 16-bit halves
+constexpr uint32_t kM4 = 0x00300030u, kM6 = 0x00C000C0u, kM8 = 0x03000300u;
+constexpr uint32_t kG4 = (21u << 10) | (21u << 26);  // 2^6  = 64
+constexpr uint32_t kG6 = (19u << 10) | (19u << 26);  // 2^4  = 16
+constexpr uint32_t kG8 = (17u << 10) | (17u << 26);  // 2^2  = 4
+// offset carried by pair j (channels j and j+8 of a word)
+__device__ __forceinline__ constexpr float pair_offset(int j) {
+    return (j == 4 || j == 7) ? 4.0f : ((j == 1 || j == 3 || j == 6) ? 16.0f : 64.0f);
+}
+
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t g) { return (x & m) | g; }
+
+// Eight fp16 pairs of a 16-channel code word: pair j = (off_j + code[j], off_j + code[j + 8]).
+__device__ __forceinline__ void unpack16(uint32_t w, uint32_t (&h)[8]) {
+    const uint32_t xl = w << 4, xr = w >> 6;
+    h[0] = and_or(xl, kM4, kG4);
+    h[1] = and_or(xl, kM6, kG6);
+    h[2] = and_or(w, kM4, kG4);
+    h[3] = and_or(w, kM6, kG6);
+    h[4] = and_or(w, kM8, kG8);
+    h[5] = and_or(xr, kM4, kG4);
+    h[6] = and_or(xr, kM6, kG6);
+    h[7] = and_or(xr, kM8, kG8);
+}
+
+__device__ __forceinline__ f16x2 as_h2(uint32_t u) {
+    f16x2 r;
+    __builtin_memcpy(&r, &u, 4);
+    return r;
+}
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
 }
 
 template <int D, int R>
@@ -38,13 +83,15 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes, const uint32_t* __restrict__ k_sz,
     const uint8_t* __restrict__ v_codes, const uint32_t* __restrict__ v_sz, int Hkv, int n, int chunk,
     float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
-    constexpr int LPT = D / 16;      // lanes per token
-    constexpr int TPW = kWave / LPT;  // tokens per wave step
-    constexpr int G32 = kGroup / TPW;  // steps per 32-token group
-    __shared__ float s_p[R][kSub];
-    __shared__ float s_wmax[4][R];
+    constexpr int W16 = D / 16;          // 16-channel code words per token
+    constexpr int KLPT = D / 32;         // keys: lanes per token (two words each)
+    constexpr int KTPW = kWave / KLPT;   // keys: tokens per wave step
+    constexpr int KSTEPS = kGroup / KTPW;
+    constexpr int VITEMS = (kGroup / 2) * W16 / kWave;  // values: (token pair, word) items per lane
+    __shared__ uint32_t s_qp[4][R][2][D / 2];  // per wave: q s as hi / lo fp16 pairs (channel j, j+8) per word
+    __shared__ float s_p[4][R][kGroup];        // per wave: scores, then probabilities, of its group
     __shared__ float s_red[4][R][D];
-    __shared__ float s_l[4][R];
+    __shared__ float s_ml[4][R][2];
 
     const int split = blockIdx.x;
     const int g = blockIdx.y;
@@ -53,179 +100,270 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const int splits = gridDim.x;
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-    const int slot = lane / LPT;
-    const int cc = lane % LPT;
-    const int c0 = 16 * cc;
     const int G = (n + kGroup - 1) / kGroup;
     const int t_begin = split * chunk;
     const int t_end = min(n, t_begin + chunk);
+    const int gi_begin = t_begin / kGroup;
+    const int gi_end = (t_end + kGroup - 1) / kGroup;
 
-    // query slice of this lane, pre-scaled into the log2 domain
-    float qv[R][16];
+    // query channels 2 lane, 2 lane + 1 (lanes >= D/2 idle here), pre-scaled to log2 units
+    const bool qlane = lane < D / 2;
+    const int qc = qlane ? 2 * lane : 0;
+    float qs[R][2];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const uint16_t* qp = q + ((size_t)(b * Hkv + g) * R + r) * D + c0;
-        const u32x4 w0 = *reinterpret_cast<const u32x4*>(qp);
-        const u32x4 w1 = *reinterpret_cast<const u32x4*>(qp + 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qv[r][2 * i] = bf16_bits_to_f32(w0[i] & 0xFFFFu) * scale_log2;
-            qv[r][2 * i + 1] = bf16_bits_to_f32(w0[i] >> 16) * scale_log2;
-            qv[r][8 + 2 * i] = bf16_bits_to_f32(w1[i] & 0xFFFFu) * scale_log2;
-            qv[r][8 + 2 * i + 1] = bf16_bits_to_f32(w1[i] >> 16) * scale_log2;
-        }
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(q + ((size_t)(b * Hkv + g) * R + r) * D + qc);
+        qs[r][0] = qlane ? bf16_bits_to_f32(w & 0xFFFFu) * scale_log2 : 0.0f;
+        qs[r][1] = qlane ? bf16_bits_to_f32(w >> 16) * scale_log2 : 0.0f;
     }
+    // where this lane's two multipliers live in the pair layout: word qc/16, pair (qc%16)%8, half (qc%16)/8
+    const int qword = qc / 16, qj = (qc % 16) % 8, qhalf = (qc % 16) / 8;
+    const int kcc = lane % KLPT;   // keys: the lane's two code words are 2 kcc, 2 kcc + 1
+    const int kslot = lane / KLPT;  // keys: token slot
 
-    float m_run[R], acc[R][16], zacc[R], lacc[R];
+    // Everything one 32-token group needs from HBM, loaded one group ahead.
+    struct Stage {
+        uint2 kc[KSTEPS];
+        uint2 ksz;
+        uint32_t vc[VITEMS][2];
+        uint32_t vsz[VITEMS][2];
+    };
+    auto load_stage = [&](int gi, Stage& st) {
+        const int grp0 = gi * kGroup;
+        st.ksz = *reinterpret_cast<const uint2*>(k_sz + ((size_t)unit * G + gi) * D + qc);
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            const int t = grp0 + kslot + KTPW * s;
+            st.kc[s] = t < t_end ? *reinterpret_cast<const uint2*>(k_codes + ((size_t)unit * n + t) * (D / 4) + 8 * kcc)
+                                 : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int it = 0; it < VITEMS; ++it) {
+            const int item = lane + kWave * it;
+            const int cc = item % W16, pr = item / W16;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int t = grp0 + 2 * pr + e;
+                if (t < t_end) {
+                    const size_t row = (size_t)unit * n + t;
+                    st.vc[it][e] = *reinterpret_cast<const uint32_t*>(v_codes + row * (D / 4) + 4 * cc);
+                    st.vsz[it][e] = v_sz[row * (D / 32) + (cc >> 1)];
+                } else {
+                    st.vc[it][e] = 0u;
+                    st.vsz[it][e] = 0u;  // s = z = 0: contributes nothing
+                }
+            }
+        }
+    };
+
+    // online-softmax state of this wave (m wave-uniform; l, acc per lane)
+    float m_run[R], lacc[R], acc[VITEMS][R][16], wsum[VITEMS][R], zacc[VITEMS][R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         m_run[r] = -INFINITY;
-        zacc[r] = 0.0f;
         lacc[r] = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) acc[r][c] = 0.0f;
+        for (int it = 0; it < VITEMS; ++it) {
+            wsum[it][r] = 0.0f;
+            zacc[it][r] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[it][r][c] = 0.0f;
+        }
     }
 
-    for (int sub0 = t_begin; sub0 < t_end; sub0 += kSub) {
-        // ---- keys: scores of this wave's 32-token group ----
-        const int grp0 = sub0 + kGroup * wave;  // first token of the wave's group
-        float wmax[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) wmax[r] = -INFINITY;
-        if (grp0 < t_end) {
-            const int gi = grp0 / kGroup;
-            const uint32_t* szp = k_sz + ((size_t)unit * G + gi) * D + c0;
-            float qs[R][16], bias[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) bias[r] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4 w = *reinterpret_cast<const u32x4*>(szp + 4 * i);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float s = half_bits_to_f32(w[e] & 0xFFFFu);
-                    const float z = half_bits_to_f32(w[e] >> 16);
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        qs[r][4 * i + e] = qv[r][4 * i + e] * s;
-                        bias[r] = fmaf(qv[r][4 * i + e], z, bias[r]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int st = 0; st < G32; ++st) {
-                const int tl = slot + TPW * st;  // token within the group
-                const int t = grp0 + tl;
-                const bool valid = t < t_end;
-                uint32_t word = 0;
-                if (valid) word = *reinterpret_cast<const uint32_t*>(k_codes + ((size_t)unit * n + t) * (D / 4) + 4 * cc);
-                float part[R];
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    float a = bias[r];
-#pragma unroll
-                    for (int c = 0; c < 16; ++c) a = fmaf(qs[r][c], code_at(word, c), a);
-                    part[r] = a;
-                }
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    float sc = group_sum<LPT>(part[r]);  // every lane takes part in the shuffle
-                    sc = valid ? sc : -INFINITY;
-                    if (cc == 0) s_p[r][kGroup * wave + tl] = sc;
-                    wmax[r] = fmaxf(wmax[r], sc);
-                }
-            }
-        } else {
-            // no tokens for this wave: mark its slice empty
-            for (int i = lane; i < kGroup; i += kWave)
-#pragma unroll
-                for (int r = 0; r < R; ++r) s_p[r][kGroup * wave + i] = -INFINITY;
-        }
+    auto process = [&](int gi, const Stage& st) {
+        const int grp0 = gi * kGroup;
+        // ---- keys: fold the group's fp16 scales into the query (hi / lo parts) ----
+        const float s0 = half_bits_to_f32(st.ksz.x & 0xFFFFu), z0 = half_bits_to_f32(st.ksz.x >> 16);
+        const float s1 = half_bits_to_f32(st.ksz.y & 0xFFFFu), z1 = half_bits_to_f32(st.ksz.y >> 16);
+        float bias[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            float mx = wmax[r];
-#pragma unroll
-            for (int o = LPT; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-            if (lane == 0) s_wmax[wave][r] = mx;
+            const float x0 = qs[r][0] * s0, x1 = qs[r][1] * s1;
+            const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+            const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+            float part = fmaf(qs[r][0], z0, qs[r][1] * z1);
+            part = fmaf(-((float)h0 + (float)l0), pair_offset(qj), part);
+            part = fmaf(-((float)h1 + (float)l1), pair_offset(qj + 1), part);
+            if (qlane) {
+                _Float16* ph = reinterpret_cast<_Float16*>(&s_qp[wave][r][0][qword * 8]);
+                _Float16* pl = reinterpret_cast<_Float16*>(&s_qp[wave][r][1][qword * 8]);
+                ph[2 * qj + qhalf] = h0;
+                ph[2 * (qj + 1) + qhalf] = h1;
+                pl[2 * qj + qhalf] = l0;
+                pl[2 * (qj + 1) + qhalf] = l1;
+            }
+            bias[r] = group_sum<kWave>(qlane ? part : 0.0f);
         }
-        __syncthreads();
-        // ---- softmax bookkeeping (block-uniform) ----
-        float alpha[R], m_new[R];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // ---- keys: scores of the group's 32 tokens ----
+        float gmax[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            uint32_t qp[2][16];
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const u32x4 x = *reinterpret_cast<const u32x4*>(&s_qp[wave][r][part][16 * kcc + 4 * i]);
+                    qp[part][4 * i] = x[0];
+                    qp[part][4 * i + 1] = x[1];
+                    qp[part][4 * i + 2] = x[2];
+                    qp[part][4 * i + 3] = x[3];
+                }
+            }
+            gmax[r] = -INFINITY;
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                const int tl = kslot + KTPW * s;
+                uint32_t h0[8], h1[8];
+                unpack16(st.kc[s].x, h0);
+                unpack16(st.kc[s].y, h1);
+                float a = 0.0f, al = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    a = dot2(qp[0][j], h0[j], a);
+                    al = dot2(qp[1][j], h0[j], al);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    a = dot2(qp[0][8 + j], h1[j], a);
+                    al = dot2(qp[1][8 + j], h1[j], al);
+                }
+                float sc = group_sum<KLPT>(a + al) + bias[r];
+                sc = grp0 + tl < t_end ? sc : -INFINITY;
+                if (kcc == 0) s_p[wave][r][tl] = sc;
+                gmax[r] = fmaxf(gmax[r], sc);
+            }
+        }
+        // ---- softmax bookkeeping for this wave (wave-uniform) ----
+        float m_new[R];
         bool rescale = false;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float ms = fmaxf(fmaxf(s_wmax[0][r], s_wmax[1][r]), fmaxf(s_wmax[2][r], s_wmax[3][r]));
-            m_new[r] = fmaxf(m_run[r], ms);
-            alpha[r] = exp2f(m_run[r] - m_new[r]);  // 0 on the first step (m_run = -inf)
+            float mx = gmax[r];
+#pragma unroll
+            for (int o = KLPT; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+            m_new[r] = fmaxf(m_run[r], mx);
             rescale |= m_new[r] != m_run[r];
-            m_run[r] = m_new[r];
         }
-        // probabilities of the 128 tokens
-        for (int i = threadIdx.x; i < R * kSub; i += blockDim.x) {
-            const int r = i / kSub, t = i % kSub;
-            s_p[r][t] = exp2f(s_p[r][t] - m_new[r]);
-        }
-        if (rescale) {
+        // probabilities of the group's tokens, once per token (0 for masked tokens)
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                zacc[r] *= alpha[r];
-                lacc[r] *= alpha[r];
+        for (int r = 0; r < R; ++r) {
 #pragma unroll
-                for (int c = 0; c < 16; ++c) acc[r][c] *= alpha[r];
+            for (int s = 0; s < KSTEPS; ++s) {
+                const int tl = kslot + KTPW * s;
+                if (kcc == 0) s_p[wave][r][tl] = __builtin_amdgcn_exp2f(s_p[wave][r][tl] - m_new[r]);
             }
         }
-        __syncthreads();
-        // ---- values ----
-        if (grp0 < t_end) {
+        if (rescale) {  // wave-uniform
 #pragma unroll
-            for (int st = 0; st < G32; ++st) {
-                const int tl = slot + TPW * st;
-                const int t = grp0 + tl;
-                if (t < t_end) {
-                    const size_t row = (size_t)unit * n + t;
-                    const uint32_t word = *reinterpret_cast<const uint32_t*>(v_codes + row * (D / 4) + 4 * cc);
-                    const uint32_t szw = v_sz[row * (D / 32) + (cc >> 1)];
-                    const float s = half_bits_to_f32(szw & 0xFFFFu);
-                    const float z = half_bits_to_f32(szw >> 16);
+            for (int r = 0; r < R; ++r) {
+                const float alpha = exp2f(m_run[r] - m_new[r]);  // 0 on the first group (m_run = -inf)
+                lacc[r] *= alpha;
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const float p = s_p[r][kGroup * wave + tl];
-                        const float w = p * s;
-                        zacc[r] = fmaf(p, z, zacc[r]);
-                        if (cc == 0) lacc[r] += p;
+                for (int it = 0; it < VITEMS; ++it) {
+                    wsum[it][r] *= alpha;
+                    zacc[it][r] *= alpha;
 #pragma unroll
-                        for (int c = 0; c < 16; ++c) acc[r][c] = fmaf(w, code_at(word, c), acc[r][c]);
-                    }
+                    for (int c = 0; c < 16; ++c) acc[it][r][c] *= alpha;
+                }
+                m_run[r] = m_new[r];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // ---- values: token pairs ----
+#pragma unroll
+        for (int it = 0; it < VITEMS; ++it) {
+            const int item = lane + kWave * it;
+            const int cc = item % W16, pr = item / W16;
+            const uint32_t plo = __builtin_amdgcn_perm(st.vc[it][1], st.vc[it][0], 0x05040100u);
+            const uint32_t phi = __builtin_amdgcn_perm(st.vc[it][1], st.vc[it][0], 0x07060302u);
+            uint32_t hl[8], hh[8];
+            unpack16(plo, hl);  // pair j: (token 0 channel j, token 1 channel j)
+            unpack16(phi, hh);  // pair j: (token 0 channel j+8, token 1 channel j+8)
+            const float sA = half_bits_to_f32(st.vsz[it][0] & 0xFFFFu), zA = half_bits_to_f32(st.vsz[it][0] >> 16);
+            const float sB = half_bits_to_f32(st.vsz[it][1] & 0xFFFFu), zB = half_bits_to_f32(st.vsz[it][1] >> 16);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float pA = s_p[wave][r][2 * pr];
+                const float pB = s_p[wave][r][2 * pr + 1];
+                f16x2 wv;
+                wv[0] = (_Float16)(pA * sA);
+                wv[1] = (_Float16)(pB * sB);
+                uint32_t wu;
+                __builtin_memcpy(&wu, &wv, 4);
+                wsum[it][r] = dot2(wu, 0x3C003C00u, wsum[it][r]);  // exact sum of the fp16 weights
+                zacc[it][r] = fmaf(pA, zA, fmaf(pB, zB, zacc[it][r]));
+                if (cc == 0) lacc[r] += pA + pB;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    acc[it][r][j] = dot2(wu, hl[j], acc[it][r][j]);
+                    acc[it][r][8 + j] = dot2(wu, hh[j], acc[it][r][8 + j]);
                 }
             }
         }
-        __syncthreads();
+    };
+
+    // each wave walks groups wave, wave + 4, ... of this split, one group prefetched
+    // (a second prefetched group costs more in occupancy than it gains)
+    {
+        Stage A, Bst;
+        int gi = gi_begin + wave;
+        if (gi < gi_end) load_stage(gi, A);
+        while (gi < gi_end) {
+            if (gi + 4 < gi_end) load_stage(gi + 4, Bst);
+            process(gi, A);
+            gi += 4;
+            if (gi >= gi_end) break;
+            if (gi + 4 < gi_end) load_stage(gi + 4, A);
+            process(gi, Bst);
+            gi += 4;
+        }
     }
 
-    // ---- reduce the token slots of each wave, then the 4 waves ----
+    // ---- this wave's partial: remove the unpack offsets, reduce lanes holding the same word ----
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            float x = acc[r][c] + zacc[r];
-#pragma unroll
-            for (int o = LPT; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
-            if (slot == 0) s_red[wave][r][c0 + c] = x;
-        }
         float l = lacc[r];
 #pragma unroll
-        for (int o = LPT; o < kWave; o <<= 1) l += __shfl_xor(l, o, kWave);
-        if (lane == 0) s_l[wave][r] = l;
+        for (int o = 1; o < kWave; o <<= 1) l += __shfl_xor(l, o, kWave);
+        if (lane == 0) {
+            s_ml[wave][r][0] = m_run[r];
+            s_ml[wave][r][1] = l;
+        }
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            float x = 0.0f;
+#pragma unroll
+            for (int it = 0; it < VITEMS; ++it)
+                x += acc[it][r][c] - pair_offset(c & 7) * wsum[it][r] + zacc[it][r];
+#pragma unroll
+            for (int o = W16; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
+            if (lane < W16) s_red[wave][r][16 * lane + c] = x;
+        }
     }
     __syncthreads();
+    // ---- merge the 4 waves (log-sum-exp) into this split's partial ----
     for (int i = threadIdx.x; i < R * D; i += blockDim.x) {
         const int r = i / D, d = i % D;
-        const float x = s_red[0][r][d] + s_red[1][r][d] + s_red[2][r][d] + s_red[3][r][d];
+        const float M = fmaxf(fmaxf(s_ml[0][r][0], s_ml[1][r][0]), fmaxf(s_ml[2][r][0], s_ml[3][r][0]));
+        float x = 0.0f, L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float f = exp2f(s_ml[w][r][0] - M);  // 0 for a wave that saw no tokens
+            x = fmaf(s_red[w][r][d], f, x);
+            L = fmaf(s_ml[w][r][1], f, L);
+        }
         const size_t o = (((size_t)(b * Hkv + g) * R + r) * splits + split);
         ws_acc[o * D + d] = x;
         if (d == 0) {
-            ws_ml[o * 2 + 0] = m_run[r];
-            ws_ml[o * 2 + 1] = s_l[0][r] + s_l[1][r] + s_l[2][r] + s_l[3][r];
+            ws_ml[o * 2 + 0] = M;
+            ws_ml[o * 2 + 1] = L;
         }
     }
 }
