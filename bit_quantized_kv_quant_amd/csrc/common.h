@@ -45,6 +45,43 @@ __device__ __forceinline__ float swap_halves(float x) {
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// Sum over aligned groups of W lanes (W = 2, 4, 8, 16, 32 or 64) with DPP and
+// permlane swaps: each step is one VALU op, no LDS crossbar traffic.
+template <int W>
+__device__ __forceinline__ float dpp_sum(float x) {
+    if constexpr (W >= 2)   // xor 1: quad_perm [1,0,3,2]
+        x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    if constexpr (W >= 4)   // xor 2: quad_perm [2,3,0,1]
+        x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    if constexpr (W >= 8)   // other quad of the 8-lane half row: row_half_mirror
+        x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+    if constexpr (W >= 16)  // other half of the 16-lane row: row_mirror
+        x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+    if constexpr (W >= 32) {  // other 16-lane row of the 32-lane half
+        auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+        x += __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
+    }
+    if constexpr (W >= 64) x += swap_halves(x);
+    return x;
+}
+template <int W>
+__device__ __forceinline__ float dpp_max(float x) {
+    if constexpr (W >= 2)
+        x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
+    if constexpr (W >= 4)
+        x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
+    if constexpr (W >= 8)
+        x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)));
+    if constexpr (W >= 16)
+        x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)));
+    if constexpr (W >= 32) {
+        auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+        x = fmaxf(x, __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]));
+    }
+    if constexpr (W >= 64) x = fmaxf(x, swap_halves(x));
+    return x;
+}
+
 // Butterfly reductions over aligned lane groups of width W (W <= 32), via ds_swizzle-free shuffles.
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {

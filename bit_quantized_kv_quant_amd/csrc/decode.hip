@@ -56,17 +56,28 @@ __device__ __forceinline__ constexpr float pair_offset(int j) {
 
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t g) { return (x & m) | g; }
 
+// The six mask / exponent constants, held in registers: VOP3 on gfx9 takes no
+// literal, so with literals the compiler splits each v_and_or_b32 in two.
+struct UnpackConsts {
+    uint32_t m4, m6, m8, g4, g6, g8;
+};
+__device__ __forceinline__ UnpackConsts unpack_consts() {
+    uint32_t zero;  // a VGPR 0 the compiler cannot see through, so the constants stay in VGPRs
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    return {kM4 | zero, kM6 | zero, kM8 | zero, kG4 | zero, kG6 | zero, kG8 | zero};
+}
+
 // Eight fp16 pairs of a 16-channel code word: pair j = (off_j + code[j], off_j + code[j + 8]).
-__device__ __forceinline__ void unpack16(uint32_t w, uint32_t (&h)[8]) {
+__device__ __forceinline__ void unpack16(uint32_t w, const UnpackConsts& k, uint32_t (&h)[8]) {
     const uint32_t xl = w << 4, xr = w >> 6;
-    h[0] = and_or(xl, kM4, kG4);
-    h[1] = and_or(xl, kM6, kG6);
-    h[2] = and_or(w, kM4, kG4);
-    h[3] = and_or(w, kM6, kG6);
-    h[4] = and_or(w, kM8, kG8);
-    h[5] = and_or(xr, kM4, kG4);
-    h[6] = and_or(xr, kM6, kG6);
-    h[7] = and_or(xr, kM8, kG8);
+    h[0] = and_or(xl, k.m4, k.g4);
+    h[1] = and_or(xl, k.m6, k.g6);
+    h[2] = and_or(w, k.m4, k.g4);
+    h[3] = and_or(w, k.m6, k.g6);
+    h[4] = and_or(w, k.m8, k.g8);
+    h[5] = and_or(xr, k.m4, k.g4);
+    h[6] = and_or(xr, k.m6, k.g6);
+    h[7] = and_or(xr, k.m8, k.g8);
 }
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) {
@@ -84,7 +95,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const uint8_t* __restrict__ v_codes, const uint32_t* __restrict__ v_sz, int Hkv, int n, int chunk,
     float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
     constexpr int W16 = D / 16;          // 16-channel code words per token
-    constexpr int KLPT = D / 32;         // keys: lanes per token (two words each)
+    constexpr int KLPT = D / 16;         // keys: lanes per token (one code word each)
     constexpr int KTPW = kWave / KLPT;   // keys: tokens per wave step
     constexpr int KSTEPS = kGroup / KTPW;
     constexpr int VITEMS = (kGroup / 2) * W16 / kWave;  // values: (token pair, word) items per lane
@@ -118,24 +129,46 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     }
     // where this lane's two multipliers live in the pair layout: word qc/16, pair (qc%16)%8, half (qc%16)/8
     const int qword = qc / 16, qj = (qc % 16) % 8, qhalf = (qc % 16) / 8;
-    const int kcc = lane % KLPT;   // keys: the lane's two code words are 2 kcc, 2 kcc + 1
+    const int kcc = lane % KLPT;   // keys: the lane's code word
+    const UnpackConsts uk = unpack_consts();
     const int kslot = lane / KLPT;  // keys: token slot
 
     // Everything one 32-token group needs from HBM, loaded one group ahead.
     struct Stage {
-        uint2 kc[KSTEPS];
+        uint32_t kc[KSTEPS];
         uint2 ksz;
         uint32_t vc[VITEMS][2];
         uint32_t vsz[VITEMS][2];
     };
+    // lane offsets inside a group (constant); the group bases below are wave-uniform
+    const int koff = kslot * (D / 4) + 4 * kcc;
     auto load_stage = [&](int gi, Stage& st) {
         const int grp0 = gi * kGroup;
+        const size_t row0 = (size_t)unit * n + grp0;
+        const uint8_t* kcb = k_codes + row0 * (D / 4);
+        const uint8_t* vcb = v_codes + row0 * (D / 4);
+        const uint32_t* vsb = v_sz + row0 * (D / 32);
         st.ksz = *reinterpret_cast<const uint2*>(k_sz + ((size_t)unit * G + gi) * D + qc);
+        if (grp0 + kGroup <= t_end) {  // wave-uniform: the whole group is in range
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s)
+                st.kc[s] = *reinterpret_cast<const uint32_t*>(kcb + koff + s * KTPW * (D / 4));
+#pragma unroll
+            for (int it = 0; it < VITEMS; ++it) {
+                const int item = lane + kWave * it;
+                const int cc = item % W16, pr = item / W16;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    st.vc[it][e] = *reinterpret_cast<const uint32_t*>(vcb + (2 * pr + e) * (D / 4) + 4 * cc);
+                    st.vsz[it][e] = vsb[(2 * pr + e) * (D / 32) + (cc >> 1)];
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             const int t = grp0 + kslot + KTPW * s;
-            st.kc[s] = t < t_end ? *reinterpret_cast<const uint2*>(k_codes + ((size_t)unit * n + t) * (D / 4) + 8 * kcc)
-                                 : make_uint2(0u, 0u);
+            st.kc[s] = t < t_end ? *reinterpret_cast<const uint32_t*>(kcb + koff + s * KTPW * (D / 4)) : 0u;
         }
 #pragma unroll
         for (int it = 0; it < VITEMS; ++it) {
@@ -143,32 +176,24 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
             const int cc = item % W16, pr = item / W16;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const int t = grp0 + 2 * pr + e;
-                if (t < t_end) {
-                    const size_t row = (size_t)unit * n + t;
-                    st.vc[it][e] = *reinterpret_cast<const uint32_t*>(v_codes + row * (D / 4) + 4 * cc);
-                    st.vsz[it][e] = v_sz[row * (D / 32) + (cc >> 1)];
-                } else {
-                    st.vc[it][e] = 0u;
-                    st.vsz[it][e] = 0u;  // s = z = 0: contributes nothing
-                }
+                const bool in = grp0 + 2 * pr + e < t_end;
+                st.vc[it][e] = in ? *reinterpret_cast<const uint32_t*>(vcb + (2 * pr + e) * (D / 4) + 4 * cc) : 0u;
+                st.vsz[it][e] = in ? vsb[(2 * pr + e) * (D / 32) + (cc >> 1)] : 0u;  // s = z = 0 adds nothing
             }
         }
     };
 
     // online-softmax state of this wave (m wave-uniform; l, acc per lane)
-    float m_run[R], lacc[R], acc[VITEMS][R][16], wsum[VITEMS][R], zacc[VITEMS][R];
+    // a lane's value items all use the same code word (item % W16 == lane % W16), so one accumulator set
+    float m_run[R], lacc[R], acc[R][16], wsum[R], zacc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         m_run[r] = -INFINITY;
         lacc[r] = 0.0f;
+        wsum[r] = 0.0f;
+        zacc[r] = 0.0f;
 #pragma unroll
-        for (int it = 0; it < VITEMS; ++it) {
-            wsum[it][r] = 0.0f;
-            zacc[it][r] = 0.0f;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) acc[it][r][c] = 0.0f;
-        }
+        for (int c = 0; c < 16; ++c) acc[r][c] = 0.0f;
     }
 
     auto process = [&](int gi, const Stage& st) {
@@ -193,7 +218,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
                 pl[2 * qj + qhalf] = l0;
                 pl[2 * (qj + 1) + qhalf] = l1;
             }
-            bias[r] = group_sum<kWave>(qlane ? part : 0.0f);
+            bias[r] = dpp_sum<kWave>(qlane ? part : 0.0f);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -202,12 +227,12 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         float gmax[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            uint32_t qp[2][16];
+            uint32_t qp[2][8];
 #pragma unroll
             for (int part = 0; part < 2; ++part) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u32x4 x = *reinterpret_cast<const u32x4*>(&s_qp[wave][r][part][16 * kcc + 4 * i]);
+                for (int i = 0; i < 2; ++i) {
+                    const u32x4 x = *reinterpret_cast<const u32x4*>(&s_qp[wave][r][part][8 * kcc + 4 * i]);
                     qp[part][4 * i] = x[0];
                     qp[part][4 * i + 1] = x[1];
                     qp[part][4 * i + 2] = x[2];
@@ -218,21 +243,15 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 #pragma unroll
             for (int s = 0; s < KSTEPS; ++s) {
                 const int tl = kslot + KTPW * s;
-                uint32_t h0[8], h1[8];
-                unpack16(st.kc[s].x, h0);
-                unpack16(st.kc[s].y, h1);
+                uint32_t h[8];
+                unpack16(st.kc[s], uk, h);
                 float a = 0.0f, al = 0.0f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    a = dot2(qp[0][j], h0[j], a);
-                    al = dot2(qp[1][j], h0[j], al);
+                    a = dot2(qp[0][j], h[j], a);
+                    al = dot2(qp[1][j], h[j], al);
                 }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    a = dot2(qp[0][8 + j], h1[j], a);
-                    al = dot2(qp[1][8 + j], h1[j], al);
-                }
-                float sc = group_sum<KLPT>(a + al) + bias[r];
+                float sc = dpp_sum<KLPT>(a + al) + bias[r];
                 sc = grp0 + tl < t_end ? sc : -INFINITY;
                 if (kcc == 0) s_p[wave][r][tl] = sc;
                 gmax[r] = fmaxf(gmax[r], sc);
@@ -243,9 +262,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         bool rescale = false;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            float mx = gmax[r];
-#pragma unroll
-            for (int o = KLPT; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+            const float mx = dpp_max<kWave>(gmax[r]);
             m_new[r] = fmaxf(m_run[r], mx);
             rescale |= m_new[r] != m_run[r];
         }
@@ -263,13 +280,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
             for (int r = 0; r < R; ++r) {
                 const float alpha = exp2f(m_run[r] - m_new[r]);  // 0 on the first group (m_run = -inf)
                 lacc[r] *= alpha;
+                wsum[r] *= alpha;
+                zacc[r] *= alpha;
 #pragma unroll
-                for (int it = 0; it < VITEMS; ++it) {
-                    wsum[it][r] *= alpha;
-                    zacc[it][r] *= alpha;
-#pragma unroll
-                    for (int c = 0; c < 16; ++c) acc[it][r][c] *= alpha;
-                }
+                for (int c = 0; c < 16; ++c) acc[r][c] *= alpha;
                 m_run[r] = m_new[r];
             }
         }
@@ -284,8 +298,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
             const uint32_t plo = __builtin_amdgcn_perm(st.vc[it][1], st.vc[it][0], 0x05040100u);
             const uint32_t phi = __builtin_amdgcn_perm(st.vc[it][1], st.vc[it][0], 0x07060302u);
             uint32_t hl[8], hh[8];
-            unpack16(plo, hl);  // pair j: (token 0 channel j, token 1 channel j)
-            unpack16(phi, hh);  // pair j: (token 0 channel j+8, token 1 channel j+8)
+            unpack16(plo, uk, hl);  // pair j: (token 0 channel j, token 1 channel j)
+            unpack16(phi, uk, hh);  // pair j: (token 0 channel j+8, token 1 channel j+8)
             const float sA = half_bits_to_f32(st.vsz[it][0] & 0xFFFFu), zA = half_bits_to_f32(st.vsz[it][0] >> 16);
             const float sB = half_bits_to_f32(st.vsz[it][1] & 0xFFFFu), zB = half_bits_to_f32(st.vsz[it][1] >> 16);
 #pragma unroll
@@ -297,13 +311,13 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
                 wv[1] = (_Float16)(pB * sB);
                 uint32_t wu;
                 __builtin_memcpy(&wu, &wv, 4);
-                wsum[it][r] = dot2(wu, 0x3C003C00u, wsum[it][r]);  // exact sum of the fp16 weights
-                zacc[it][r] = fmaf(pA, zA, fmaf(pB, zB, zacc[it][r]));
+                wsum[r] = dot2(wu, 0x3C003C00u, wsum[r]);  // exact sum of the fp16 weights
+                zacc[r] = fmaf(pA, zA, fmaf(pB, zB, zacc[r]));
                 if (cc == 0) lacc[r] += pA + pB;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    acc[it][r][j] = dot2(wu, hl[j], acc[it][r][j]);
-                    acc[it][r][8 + j] = dot2(wu, hh[j], acc[it][r][8 + j]);
+                    acc[r][j] = dot2(wu, hl[j], acc[r][j]);
+                    acc[r][8 + j] = dot2(wu, hh[j], acc[r][8 + j]);
                 }
             }
         }
@@ -338,10 +352,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         }
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-            float x = 0.0f;
-#pragma unroll
-            for (int it = 0; it < VITEMS; ++it)
-                x += acc[it][r][c] - pair_offset(c & 7) * wsum[it][r] + zacc[it][r];
+            float x = acc[r][c] - pair_offset(c & 7) * wsum[r] + zacc[r];
 #pragma unroll
             for (int o = W16; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
             if (lane < W16) s_red[wave][r][16 * lane + c] = x;
