@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const int b = blockIdx.z;
     const int unit = b * Hkv + g;
     const int splits = gridDim.x;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: keeps group bases scalar
     const int lane = threadIdx.x % kWave;
     const int G = (n + kGroup - 1) / kGroup;
     const int t_begin = split * chunk;
@@ -140,27 +140,39 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         uint32_t vc[VITEMS][2];
         uint32_t vsz[VITEMS][2];
     };
-    // lane offsets inside a group (constant); the group bases below are wave-uniform
-    const int koff = kslot * (D / 4) + 4 * kcc;
+    // Lane byte offsets inside a group (constant, unsigned 32-bit) added to
+    // wave-uniform group bases, so loads use scalar base + vector offset.
+    const uint32_t koff = (uint32_t)(kslot * (D / 4) + 4 * kcc);
+    uint32_t vcoff[VITEMS][2], vsoff[VITEMS][2];
+#pragma unroll
+    for (int it = 0; it < VITEMS; ++it) {
+        const int item = lane + kWave * it;
+        const int cc = item % W16, pr = item / W16;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            vcoff[it][e] = (uint32_t)((2 * pr + e) * (D / 4) + 4 * cc);
+            vsoff[it][e] = (uint32_t)(((2 * pr + e) * (D / 32) + (cc >> 1)) * 4);
+        }
+    }
+    auto ld32 = [](const uint8_t* base, uint32_t off) {
+        return *reinterpret_cast<const uint32_t*>(base + off);
+    };
     auto load_stage = [&](int gi, Stage& st) {
         const int grp0 = gi * kGroup;
         const size_t row0 = (size_t)unit * n + grp0;
         const uint8_t* kcb = k_codes + row0 * (D / 4);
         const uint8_t* vcb = v_codes + row0 * (D / 4);
-        const uint32_t* vsb = v_sz + row0 * (D / 32);
+        const uint8_t* vsb = reinterpret_cast<const uint8_t*>(v_sz + row0 * (D / 32));
         st.ksz = *reinterpret_cast<const uint2*>(k_sz + ((size_t)unit * G + gi) * D + qc);
         if (grp0 + kGroup <= t_end) {  // wave-uniform: the whole group is in range
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s)
-                st.kc[s] = *reinterpret_cast<const uint32_t*>(kcb + koff + s * KTPW * (D / 4));
+            for (int s = 0; s < KSTEPS; ++s) st.kc[s] = ld32(kcb, koff + (uint32_t)(s * KTPW * (D / 4)));
 #pragma unroll
             for (int it = 0; it < VITEMS; ++it) {
-                const int item = lane + kWave * it;
-                const int cc = item % W16, pr = item / W16;
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    st.vc[it][e] = *reinterpret_cast<const uint32_t*>(vcb + (2 * pr + e) * (D / 4) + 4 * cc);
-                    st.vsz[it][e] = vsb[(2 * pr + e) * (D / 32) + (cc >> 1)];
+                    st.vc[it][e] = ld32(vcb, vcoff[it][e]);
+                    st.vsz[it][e] = ld32(vsb, vsoff[it][e]);
                 }
             }
             return;
@@ -168,17 +180,17 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             const int t = grp0 + kslot + KTPW * s;
-            st.kc[s] = t < t_end ? *reinterpret_cast<const uint32_t*>(kcb + koff + s * KTPW * (D / 4)) : 0u;
+            st.kc[s] = t < t_end ? ld32(kcb, koff + (uint32_t)(s * KTPW * (D / 4))) : 0u;
         }
 #pragma unroll
         for (int it = 0; it < VITEMS; ++it) {
             const int item = lane + kWave * it;
-            const int cc = item % W16, pr = item / W16;
+            const int pr = item / W16;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const bool in = grp0 + 2 * pr + e < t_end;
-                st.vc[it][e] = in ? *reinterpret_cast<const uint32_t*>(vcb + (2 * pr + e) * (D / 4) + 4 * cc) : 0u;
-                st.vsz[it][e] = in ? vsb[(2 * pr + e) * (D / 32) + (cc >> 1)] : 0u;  // s = z = 0 adds nothing
+                st.vc[it][e] = in ? ld32(vcb, vcoff[it][e]) : 0u;
+                st.vsz[it][e] = in ? ld32(vsb, vsoff[it][e]) : 0u;  // s = z = 0 adds nothing
             }
         }
     };
