@@ -95,12 +95,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const uint8_t* __restrict__ v_codes, const uint32_t* __restrict__ v_sz, int Hkv, int n, int chunk,
     float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
     constexpr int W16 = D / 16;          // 16-channel code words per token
-    constexpr int KLPT = D / 16;         // keys: lanes per token (one code word each)
-    constexpr int KTPW = kWave / KLPT;   // keys: tokens per wave step
-    constexpr int KSTEPS = kGroup / KTPW;
     constexpr int VITEMS = (kGroup / 2) * W16 / kWave;  // values: (token pair, word) items per lane
-    __shared__ uint32_t s_qp[4][R][2][D / 2];  // per wave: q s as hi / lo fp16 pairs (channel j, j+8) per word
-    __shared__ float s_p[4][R][kGroup];        // per wave: scores, then probabilities, of its group
+    // per wave and head: four fp8 pieces of the scaled query, each in MFMA K order (128 bytes)
+    __shared__ __align__(16) uint8_t s_qa[4][R][4][128];
+    __shared__ float s_p[4][R][kGroup];        // per wave: probabilities of its group
     __shared__ float s_red[4][R][D];
     __shared__ float s_ml[4][R][2];
 
@@ -117,32 +115,39 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const int gi_begin = t_begin / kGroup;
     const int gi_end = (t_end + kGroup - 1) / kGroup;
 
-    // query channels 2 lane, 2 lane + 1 (lanes >= D/2 idle here), pre-scaled to log2 units
+    // Query channels of this lane: the pair (c0, c0 + 2) sits at MFMA K positions 2 lane, 2 lane + 1
+    // (lanes >= D/2 idle here).  Pre-scaled to log2 units.
     const bool qlane = lane < D / 2;
-    const int qc = qlane ? 2 * lane : 0;
-    float qs[R][2];
+    const int c0 = qlane ? 32 * (lane / 16) + 16 * ((lane / 8) % 2) + 4 * (lane % 4) + (lane / 4) % 2 : 0;
+    float qk[R][2];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(q + ((size_t)(b * Hkv + g) * R + r) * D + qc);
-        qs[r][0] = qlane ? bf16_bits_to_f32(w & 0xFFFFu) * scale_log2 : 0.0f;
-        qs[r][1] = qlane ? bf16_bits_to_f32(w >> 16) * scale_log2 : 0.0f;
+        const uint16_t* qr = q + ((size_t)(b * Hkv + g) * R + r) * D;
+        qk[r][0] = qlane ? bf16_bits_to_f32(qr[c0]) * scale_log2 : 0.0f;
+        qk[r][1] = qlane ? bf16_bits_to_f32(qr[c0 + 2]) * scale_log2 : 0.0f;
     }
-    // where this lane's two multipliers live in the pair layout: word qc/16, pair (qc%16)%8, half (qc%16)/8
-    const int qword = qc / 16, qj = (qc % 16) % 8, qhalf = (qc % 16) / 8;
-    const int kcc = lane % KLPT;   // keys: the lane's code word
+    // keys as MFMA B operand: lane holds token 16 j + lane % 16, code words 2 (lane / 16), + 1
+    const bool kact = lane / 16 < D / 32;
+    const uint32_t koff = (uint32_t)((lane % 16) * (D / 4) + 8 * (lane / 16));
+    // query pieces as MFMA A operand: row lane % 16 = (head block, piece)
+    const int arow = lane % 16;
+    const uint8_t* a_src = &s_qa[wave][(arow / 4) % R][arow % 4][16 * (lane / 16)];
+    const int myh = (lane / 16) % R;  // head of this lane's score rows
     const UnpackConsts uk = unpack_consts();
-    const int kslot = lane / KLPT;  // keys: token slot
+    if (D < 128) {  // K positions past D stay zero
+        for (int i = lane; i < R * 4 * 128 / 4; i += kWave)
+            reinterpret_cast<uint32_t*>(&s_qa[wave][0][0][0])[i] = 0u;
+    }
 
     // Everything one 32-token group needs from HBM, loaded one group ahead.
     struct Stage {
-        uint32_t kc[KSTEPS];
-        uint2 ksz;
+        uint2 kc[2];
+        uint32_t ksz[2];
         uint32_t vc[VITEMS][2];
         uint32_t vsz[VITEMS][2];
     };
     // Lane byte offsets inside a group (constant, unsigned 32-bit) added to
     // wave-uniform group bases, so loads use scalar base + vector offset.
-    const uint32_t koff = (uint32_t)(kslot * (D / 4) + 4 * kcc);
     uint32_t vcoff[VITEMS][2], vsoff[VITEMS][2];
 #pragma unroll
     for (int it = 0; it < VITEMS; ++it) {
@@ -157,16 +162,22 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     auto ld32 = [](const uint8_t* base, uint32_t off) {
         return *reinterpret_cast<const uint32_t*>(base + off);
     };
+    auto ld64 = [](const uint8_t* base, uint32_t off) {
+        return *reinterpret_cast<const uint2*>(base + off);
+    };
     auto load_stage = [&](int gi, Stage& st) {
         const int grp0 = gi * kGroup;
         const size_t row0 = (size_t)unit * n + grp0;
         const uint8_t* kcb = k_codes + row0 * (D / 4);
         const uint8_t* vcb = v_codes + row0 * (D / 4);
         const uint8_t* vsb = reinterpret_cast<const uint8_t*>(v_sz + row0 * (D / 32));
-        st.ksz = *reinterpret_cast<const uint2*>(k_sz + ((size_t)unit * G + gi) * D + qc);
+        const uint32_t* kszb = k_sz + ((size_t)unit * G + gi) * D;
+        st.ksz[0] = kszb[c0];
+        st.ksz[1] = kszb[c0 + 2];
         if (grp0 + kGroup <= t_end) {  // wave-uniform: the whole group is in range
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) st.kc[s] = ld32(kcb, koff + (uint32_t)(s * KTPW * (D / 4)));
+            for (int j = 0; j < 2; ++j)
+                st.kc[j] = kact ? ld64(kcb, koff + (uint32_t)(j * 16 * (D / 4))) : make_uint2(0u, 0u);
 #pragma unroll
             for (int it = 0; it < VITEMS; ++it) {
 #pragma unroll
@@ -178,9 +189,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
             return;
         }
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-            const int t = grp0 + kslot + KTPW * s;
-            st.kc[s] = t < t_end ? ld32(kcb, koff + (uint32_t)(s * KTPW * (D / 4))) : 0u;
+        for (int j = 0; j < 2; ++j) {
+            const int t = grp0 + 16 * j + lane % 16;
+            st.kc[j] = kact && t < t_end ? ld64(kcb, koff + (uint32_t)(j * 16 * (D / 4))) : make_uint2(0u, 0u);
         }
 #pragma unroll
         for (int it = 0; it < VITEMS; ++it) {
@@ -210,83 +221,89 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 
     auto process = [&](int gi, const Stage& st) {
         const int grp0 = gi * kGroup;
-        // ---- keys: fold the group's fp16 scales into the query (hi / lo parts) ----
-        const float s0 = half_bits_to_f32(st.ksz.x & 0xFFFFu), z0 = half_bits_to_f32(st.ksz.x >> 16);
-        const float s1 = half_bits_to_f32(st.ksz.y & 0xFFFFu), z1 = half_bits_to_f32(st.ksz.y >> 16);
-        float bias[R];
+        // ---- keys: fold the group's fp16 scales into the query, split into fp8 pieces ----
+        const float s0 = half_bits_to_f32(st.ksz[0] & 0xFFFFu), z0 = half_bits_to_f32(st.ksz[0] >> 16);
+        const float s1 = half_bits_to_f32(st.ksz[1] & 0xFFFFu), z1 = half_bits_to_f32(st.ksz[1] >> 16);
+        float bias[R], kmul[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float x0 = qs[r][0] * s0, x1 = qs[r][1] * s1;
-            const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-            const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
-            float part = fmaf(qs[r][0], z0, qs[r][1] * z1);
-            part = fmaf(-((float)h0 + (float)l0), pair_offset(qj), part);
-            part = fmaf(-((float)h1 + (float)l1), pair_offset(qj + 1), part);
+            float x0 = qk[r][0] * s0, x1 = qk[r][1] * s1;
+            // common power of two putting max |x| in [128, 256): every piece stays finite in e4m3
+            const float mx = dpp_max<kWave>(fmaxf(fabsf(x0), fabsf(x1)));
+            const int sig = 8 - __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(mx));
+            x0 = __builtin_amdgcn_ldexpf(x0, sig);
+            x1 = __builtin_amdgcn_ldexpf(x1, sig);
+            uint32_t p01 = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+            f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(p01, false);
+            x0 -= f[0];
+            x1 -= f[1];
+            p01 = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, p01, true);
+            f = __builtin_amdgcn_cvt_pk_f32_fp8(p01, true);
+            x0 -= f[0];
+            x1 -= f[1];
+            uint32_t p23 = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+            f = __builtin_amdgcn_cvt_pk_f32_fp8(p23, false);
+            x0 -= f[0];
+            x1 -= f[1];
+            p23 = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, p23, true);
             if (qlane) {
-                _Float16* ph = reinterpret_cast<_Float16*>(&s_qp[wave][r][0][qword * 8]);
-                _Float16* pl = reinterpret_cast<_Float16*>(&s_qp[wave][r][1][qword * 8]);
-                ph[2 * qj + qhalf] = h0;
-                ph[2 * (qj + 1) + qhalf] = h1;
-                pl[2 * qj + qhalf] = l0;
-                pl[2 * (qj + 1) + qhalf] = l1;
+                *reinterpret_cast<uint16_t*>(&s_qa[wave][r][0][2 * lane]) = (uint16_t)p01;
+                *reinterpret_cast<uint16_t*>(&s_qa[wave][r][1][2 * lane]) = (uint16_t)(p01 >> 16);
+                *reinterpret_cast<uint16_t*>(&s_qa[wave][r][2][2 * lane]) = (uint16_t)p23;
+                *reinterpret_cast<uint16_t*>(&s_qa[wave][r][3][2 * lane]) = (uint16_t)(p23 >> 16);
             }
-            bias[r] = dpp_sum<kWave>(qlane ? part : 0.0f);
+            bias[r] = dpp_sum<kWave>(fmaf(qk[r][0], z0, qk[r][1] * z1));
+            kmul[r] = __builtin_amdgcn_ldexpf(2.0f, -sig);  // fp4 holds code / 2
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // ---- keys: scores of the group's 32 tokens ----
-        float gmax[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            uint32_t qp[2][8];
-#pragma unroll
-            for (int part = 0; part < 2; ++part) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const u32x4 x = *reinterpret_cast<const u32x4*>(&s_qp[wave][r][part][8 * kcc + 4 * i]);
-                    qp[part][4 * i] = x[0];
-                    qp[part][4 * i + 1] = x[1];
-                    qp[part][4 * i + 2] = x[2];
-                    qp[part][4 * i + 3] = x[3];
-                }
-            }
-            gmax[r] = -INFINITY;
-#pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                const int tl = kslot + KTPW * s;
-                uint32_t h[8];
-                unpack16(st.kc[s], uk, h);
-                float a = 0.0f, al = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    a = dot2(qp[0][j], h[j], a);
-                    al = dot2(qp[1][j], h[j], al);
-                }
-                float sc = dpp_sum<KLPT>(a + al) + bias[r];
-                sc = grp0 + tl < t_end ? sc : -INFINITY;
-                if (kcc == 0) s_p[wave][r][tl] = sc;
-                gmax[r] = fmaxf(gmax[r], sc);
-            }
+        // ---- keys: scores of the group's 32 tokens, two 16-token MFMAs (rows = head x piece) ----
+        i32x8 A;
+        {
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(a_src);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(a_src + 64);
+            A = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         }
-        // ---- softmax bookkeeping for this wave (wave-uniform) ----
+        float km = kmul[0], kb = bias[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) {
+            km = myh == r ? kmul[r] : km;
+            kb = myh == r ? bias[r] : kb;
+        }
+        float sc[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t w0 = st.kc[j].x, w1 = st.kc[j].y;
+            const i32x8 Bk = {(int)(w0 & 0x33333333u), (int)((w0 >> 2) & 0x33333333u),
+                              (int)(w1 & 0x33333333u), (int)((w1 >> 2) & 0x33333333u), 0, 0, 0, 0};
+            const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bk, f32x4{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                             0, 4, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+            sc[j] = fmaf((c[0] + c[1]) + (c[2] + c[3]), km, kb);
+        }
+        if (grp0 + kGroup > t_end) {  // wave-uniform: the group's tail is past the range
+#pragma unroll
+            for (int j = 0; j < 2; ++j) sc[j] = grp0 + 16 * j + lane % 16 < t_end ? sc[j] : -INFINITY;
+        }
+        // ---- softmax bookkeeping for this wave (wave-uniform per head) ----
+        const float rowmax = dpp_max<16>(fmaxf(sc[0], sc[1]));
         float m_new[R];
         bool rescale = false;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float mx = dpp_max<kWave>(gmax[r]);
+            const float mx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rowmax), 16 * r));
             m_new[r] = fmaxf(m_run[r], mx);
             rescale |= m_new[r] != m_run[r];
         }
+        float mm = m_new[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) mm = myh == r ? m_new[r] : mm;
         // probabilities of the group's tokens, once per token (0 for masked tokens)
+        if (lane < 16 * R) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-#pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                const int tl = kslot + KTPW * s;
-                if (kcc == 0) s_p[wave][r][tl] = __builtin_amdgcn_exp2f(s_p[wave][r][tl] - m_new[r]);
-            }
+            for (int j = 0; j < 2; ++j) s_p[wave][myh][16 * j + lane % 16] = __builtin_amdgcn_exp2f(sc[j] - mm);
         }
+        // probabilities of the group's tokens, once per token (0 for masked tokens)
         if (rescale) {  // wave-uniform
 #pragma unroll
             for (int r = 0; r < R; ++r) {
