@@ -39,7 +39,7 @@ class PackedCache:
 
     k_codes: torch.Tensor  # uint8 [B, Hkv, n, D/4]
     k_sz: torch.Tensor     # int32 bits of (fp16 s | fp16 z << 16) [B, Hkv, ceil(n/32), D]
-    v_codes: torch.Tensor  # uint8 [B, Hkv, n, D/4]
+    v_codes: torch.Tensor  # uint8 [B, Hkv, ceil(n/32), D, 8]: 32 tokens of a channel per 8 bytes
     v_sz: torch.Tensor     # int32 [B, Hkv, n, D/32]
     B: int
     Hkv: int
@@ -52,7 +52,7 @@ class PackedCache:
         return PackedCache(
             torch.empty((B, Hkv, n_keep, D // 4), dtype=torch.uint8, device=device),
             torch.empty((B, Hkv, G, D), dtype=torch.int32, device=device),
-            torch.empty((B, Hkv, n_keep, D // 4), dtype=torch.uint8, device=device),
+            torch.empty((B, Hkv, G, D, 8), dtype=torch.uint8, device=device),
             torch.empty((B, Hkv, n_keep, D // _lib.GROUP), dtype=torch.int32, device=device),
             B, Hkv, n_keep, D)
 

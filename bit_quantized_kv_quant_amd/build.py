@@ -33,6 +33,8 @@ COMMON = [
 ]
 PER_FILE = {
     "quant_pack.hip": ["-ffp-contract=off"],
+    # MFMA results in ordinary VGPRs: the decode kernel reads every result at once
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -37,7 +37,7 @@ size_t minikv_packed_bytes(int B, int Hkv, int n_keep, int D) {
     if (B < 1 || Hkv < 1 || n_keep < 1 || D < 32 || D % 32) return 0;
     const size_t n = (size_t)n_keep;
     const size_t groups = (n + MINIKV_GROUP - 1) / MINIKV_GROUP;
-    const size_t per = n * D / 4 + groups * D * 4 + n * D / 4 + n * (D / MINIKV_GROUP) * 4;
+    const size_t per = n * D / 4 + groups * D * 4 + groups * MINIKV_GROUP * D / 4 + n * (D / MINIKV_GROUP) * 4;
     return (size_t)B * Hkv * per;
 }
 

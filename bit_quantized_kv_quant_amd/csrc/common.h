@@ -84,6 +84,21 @@ __device__ __forceinline__ float dpp_max(float x) {
     return x;
 }
 
+// Minimum over aligned 16-lane rows (W = 2, 4, 8 or 16), DPP only.
+template <int W>
+__device__ __forceinline__ float dpp_min(float x) {
+    static_assert(W <= 16, "row-local");
+    if constexpr (W >= 2)
+        x = fminf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
+    if constexpr (W >= 4)
+        x = fminf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
+    if constexpr (W >= 8)
+        x = fminf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)));
+    if constexpr (W >= 16)
+        x = fminf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)));
+    return x;
+}
+
 // Butterfly reductions over aligned lane groups of width W (W <= 32), via ds_swizzle-free shuffles.
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {

@@ -6,99 +6,196 @@
 //   out = sum_t softmax_t(q . khat_t * scale) vhat_t,   xhat = code * s + z
 // over the n_keep packed tokens.
 //
-// HBM-bound: the packed bytes of every kept token are read exactly once and
-// dequantised in registers; the R query heads of a KV head share each read.
-//
-// Unpacking: a 32-bit code word holds 16 channels.  One v_and_or puts the two
-// codes at bit position s of the word's 16-bit halves into the mantissas of two
-// fp16 numbers whose exponent is chosen so that each equals exactly
-// 2^(10-s) + code (s = 4, 6 or 8, i.e. offsets 64, 16, 4; the codes at other
-// positions are first shifted there).  Ten instructions give eight fp16 pairs
-// (channel j, channel j+8); v_dot2_f32_f16 then multiplies-and-adds two
-// channels per instruction in fp32, and the known offsets are taken out again
-// with the very same fp16 multipliers, so nothing but the multipliers is
-// rounded.
-// Keys: per 32-token group the wave folds the fp16 scale into the query,
-// x = q * scale * log2 e * s, once per channel, splits it into two fp16 parts
-// (hi = fp16(x), lo = fp16(x - hi): a single fp16 would put scores with large
-// outlier channels outside the output tolerance) and shares them through LDS;
-// a token then costs one unpack and two dot2 per channel pair, plus the fp32
-// zero-point term sum_c q_c z_c computed once per group.
-// Values: the code words of two tokens are interleaved with v_perm so that a
-// dot2 with (p1 s1, p2 s2) accumulates both tokens into one channel; the zero
-// term p z is accumulated per token.  Softmax runs in the log2 domain.
+// HBM-bound: the packed bytes of every kept token are read exactly once; the R
+// query heads of a KV head share each read.  Both contractions run on the
+// matrix cores so that the vector ALUs only unpack and bookkeep:
+//   * a 2-bit code zero-extended to a nibble is the e2m1 (fp4) number code / 2,
+//     so `w & 0x33333333` and `(w >> 2) & 0x33333333` turn a 16-code word into
+//     an MFMA operand;
+//   * the other operand is an fp32 quantity split into e4m3 (fp8) pieces:
+//     x = p0 + p1/16 + p2/256 (+ p3/4096), each piece the fp8 rounding of 16^k
+//     times what is left, so three (four) pieces carry 12 (16) significant
+//     bits of every element and every product with a code is exact; the MFMA
+//     rows hold (head, piece), the row's E8M0 scale restores 16^-k, and the
+//     pieces are summed after the product, in fp32.
+// Keys (16x16x128 f8f6f4, K = channels): per 32-token block the scales fold
+// into the query, x_c = q_c s_c (log2 units), scaled by one power of two so
+// |x| < 256, split into four pieces and staged through LDS in MFMA K order;
+// the zero-point term sum_c q_c z_c is a per-block constant.  One MFMA gives
+// 16 tokens' scores for all R heads.
+// Values (16x16x128 f8f6f4, K = tokens): values are stored packed along
+// tokens (a channel's 32 codes of a block in 8 bytes), the weights w = p s of
+// the step's 128 tokens are split into three pieces per (head, value group),
+// and one MFMA accumulates 16 channels over 128 tokens; sum_t p z is kept per
+// value group on the side.  Softmax runs in the log2 domain, online per
+// 128-token step.
 //
 // Work split: grid (splits, Hkv, B); a workgroup of 4 waves owns a range of
-// `chunk` tokens (a multiple of 128).  Each wave runs its own online softmax
-// over the 32-token groups wave, wave + 4, ..., with every HBM load of the
-// next group issued before the current group is processed (no workgroup
-// barrier until the end); the 4 waves then merge by log-sum-exp.  Partial
-// (m, l, acc) per split go to the workspace; a small second kernel merges the
-// splits and writes bf16.
+// `chunk` tokens (a multiple of 512).  Each wave walks the 128-token steps
+// wave, wave + 4, ...; the next step's key loads go out once the current keys
+// are consumed, its value loads once the current values are (no workgroup
+// barrier until the end); the 4 waves then merge by log-sum-exp.  With one
+// split the workgroup writes the bf16 output itself; otherwise partial
+// (m, l, acc) per split go to the workspace and a small second kernel merges
+// the splits.
 #include "common.h"
 #include "kernels.h"
 
 namespace minikv {
 namespace {
 
-constexpr int kSub = 128;  // tokens per workgroup step: 4 waves x one 32-token group
+constexpr int kStep = 128;        // tokens per wave step: four 32-token blocks
+constexpr int kSub = 4 * kStep;   // tokens per workgroup step
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kScaleOne = 0x7F7F7F7F;  // E8M0 block scale 2^0 for both MFMA operands
 
-// masks / exponent patterns for bit positions 4, 6, 8 of both 16-bit halves
-constexpr uint32_t kM4 = 0x00300030u, kM6 = 0x00C000C0u, kM8 = 0x03000300u;
-constexpr uint32_t kG4 = (21u << 10) | (21u << 26);  // 2^6  = 64
-constexpr uint32_t kG6 = (19u << 10) | (19u << 26);  // 2^4  = 16
-constexpr uint32_t kG8 = (17u << 10) | (17u << 26);  // 2^2  = 4
-// offset carried by pair j (channels j and j+8 of a word)
-__device__ __forceinline__ constexpr float pair_offset(int j) {
-    return (j == 4 || j == 7) ? 4.0f : ((j == 1 || j == 3 || j == 6) ? 16.0f : 64.0f);
+// C = A B with A e4m3 (rows x 128 K), B e2m1 (128 K x 16 columns), fp32
+// accumulate; sa is this lane's A row scale (E8M0 in every byte).
+__device__ __forceinline__ f32x4 mfma_f8_f4(const i32x8& a, const i32x8& b, int sa) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 4, 0, sa, 0,
+                                                            kScaleOne);
 }
 
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t g) { return (x & m) | g; }
-
-// The six mask / exponent constants, held in registers: VOP3 on gfx9 takes no
-// literal, so with literals the compiler splits each v_and_or_b32 in two.
-struct UnpackConsts {
-    uint32_t m4, m6, m8, g4, g6, g8;
-};
-__device__ __forceinline__ UnpackConsts unpack_consts() {
-    uint32_t zero;  // a VGPR 0 the compiler cannot see through, so the constants stay in VGPRs
-    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-    return {kM4 | zero, kM6 | zero, kM8 | zero, kG4 | zero, kG6 | zero, kG8 | zero};
+// B operand from 32 codes (two 16-code words): nibble 8d + i of the operand is
+// code 2i + (d % 2) of word d / 2, as e2m1 = code / 2.
+__device__ __forceinline__ i32x8 codes_e2m1(uint2 w) {
+    return i32x8{(int)(w.x & 0x33333333u), (int)((w.x >> 2) & 0x33333333u),
+                 (int)(w.y & 0x33333333u), (int)((w.y >> 2) & 0x33333333u), 0, 0, 0, 0};
 }
 
-// Eight fp16 pairs of a 16-channel code word: pair j = (off_j + code[j], off_j + code[j + 8]).
-__device__ __forceinline__ void unpack16(uint32_t w, const UnpackConsts& k, uint32_t (&h)[8]) {
-    const uint32_t xl = w << 4, xr = w >> 6;
-    h[0] = and_or(xl, k.m4, k.g4);
-    h[1] = and_or(xl, k.m6, k.g6);
-    h[2] = and_or(w, k.m4, k.g4);
-    h[3] = and_or(w, k.m6, k.g6);
-    h[4] = and_or(w, k.m8, k.g8);
-    h[5] = and_or(xr, k.m4, k.g4);
-    h[6] = and_or(xr, k.m6, k.g6);
-    h[7] = and_or(xr, k.m8, k.g8);
+// A operand: 16 bytes at K 16 blk .. and 16 bytes at K 64 + 16 blk .. of a 128-byte row.
+__device__ __forceinline__ i32x8 a_operand(const uint8_t* row16) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(row16);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(row16 + 64);
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-__device__ __forceinline__ f16x2 as_h2(uint32_t u) {
-    f16x2 r;
-    __builtin_memcpy(&r, &u, 4);
-    return r;
+// e4m3 pieces of two values (|x| < 256): x = sum_k 16^-k fp8_k, fp8_k the e4m3
+// rounding of 16^k times what the earlier pieces leave, so each piece adds four
+// significant bits relative to x itself; piece k of (x0, x1) goes to bytes
+// 2(k%2), 2(k%2) + 1 of w[k/2], and P = 3 leaves piece 3 zero.  The 16^-k comes
+// back as the E8M0 scale 127 - 4k of the piece's MFMA row.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+template <bool kHi>
+__device__ __forceinline__ uint32_t fp8_pk(float a, float b, uint32_t old, float scale) {  // fp8(a / scale), fp8(b / scale)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(s16x2, old), a, b,
+                                                                                scale, kHi));
 }
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
+__device__ __forceinline__ float pow2_bits(uint32_t biased) { return __builtin_bit_cast(float, biased << 23); }
+
+// e4m3 pieces of x0, x1 relative to the power of two u = 2^(e - 127) (|x| < 256 u):
+// x = u sum_k 16^-k fp8_k, fp8_k the e4m3 rounding of 16^k / u times what the
+// earlier pieces leave, so each piece adds four significant bits relative to x
+// itself.  Piece k of (x0, x1) goes to bytes 2(k%2), 2(k%2) + 1 of w[k/2]; P = 3
+// leaves the upper half of w[1] undefined.  The 16^-k comes back as the E8M0
+// scale 127 - 4k of the piece's MFMA row, the u as a multiplier after it.
+template <int P>
+__device__ __forceinline__ void e4m3_pieces(float x0, float x1, uint32_t e, uint32_t (&w)[2]) {
+    const float u0 = pow2_bits(e), u1 = pow2_bits(e - 4), u2 = pow2_bits(e - 8), u3 = pow2_bits(e - 12);
+    w[0] = fp8_pk<false>(x0, x1, __builtin_nondeterministic_value(0u), u0);
+    f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[0], u0, false);
+    x0 -= f[0];
+    x1 -= f[1];
+    w[0] = fp8_pk<true>(x0, x1, w[0], u1);
+    f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[0], u1, true);
+    x0 -= f[0];
+    x1 -= f[1];
+    w[1] = fp8_pk<false>(x0, x1, __builtin_nondeterministic_value(0u), u2);
+    if constexpr (P == 4) {
+        f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[1], u2, false);
+        x0 -= f[0];
+        x1 -= f[1];
+        w[1] = fp8_pk<true>(x0, x1, w[1], u3);
+    }
+}
+// Biased exponent of u for a non-negative maximum m (bits): m < 2^8 u, clamped
+// so that u 16^-3 stays a normal number (tiny maxima only lose their tail).
+__device__ __forceinline__ uint32_t piece_exp(uint32_t m_bits) {
+    const int e = (int)(m_bits >> 23) - 7;
+    return (uint32_t)(e < 27 ? 27 : e);
+}
+
+// Row (16-lane) reductions; each DPP pattern reads inside the row, so the
+// shuffle folds into the combining instruction.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dppu(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t row_umax(uint32_t x) {  // non-negative floats as bits
+    x = max(x, dppu<0xB1>(x));
+    x = max(x, dppu<0x4E>(x));
+    x = max(x, dppu<0x141>(x));
+    return max(x, dppu<0x140>(x));
+}
+__device__ __forceinline__ int row_imax(int x) {
+    x = max(x, (int)dppu<0xB1>((uint32_t)x));
+    x = max(x, (int)dppu<0x4E>((uint32_t)x));
+    x = max(x, (int)dppu<0x141>((uint32_t)x));
+    return max(x, (int)dppu<0x140>((uint32_t)x));
+}
+__device__ __forceinline__ float row_fsum(float x) {
+    x += __builtin_bit_cast(float, dppu<0xB1>(__builtin_bit_cast(uint32_t, x)));
+    x += __builtin_bit_cast(float, dppu<0x4E>(__builtin_bit_cast(uint32_t, x)));
+    x += __builtin_bit_cast(float, dppu<0x141>(__builtin_bit_cast(uint32_t, x)));
+    return x + __builtin_bit_cast(float, dppu<0x140>(__builtin_bit_cast(uint32_t, x)));
+}
+// Order-preserving int key of a float (max of keys = key of the max).
+__device__ __forceinline__ int fkey(float x) {
+    const int b = __builtin_bit_cast(int, x);
+    return b ^ (int)((uint32_t)(b >> 31) >> 1);
+}
+__device__ __forceinline__ float fkey_inv(int k) { return __builtin_bit_cast(float, k ^ (int)((uint32_t)(k >> 31) >> 1)); }
+
+// Four values per lane -> the combination of value r over all 64 lanes, in row r.
+// Two permlane32 swaps pair lanes l, l^32 (lower half keeps v0 / v1, upper v2 / v3),
+// one permlane16 swap pairs rows (keeping one value per row), DPP finishes the row.
+__device__ __forceinline__ uint32_t umax4_rows(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3) {
+    const auto a = __builtin_amdgcn_permlane32_swap(v0, v2, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(v1, v3, false, false);
+    const uint32_t t = max(a[0], a[1]), u = max(b[0], b[1]);
+    const auto c = __builtin_amdgcn_permlane16_swap(t, u, false, false);
+    return row_umax(max(c[0], c[1]));
+}
+__device__ __forceinline__ float fsum4_rows(float v0, float v1, float v2, float v3) {
+    auto bits = [](float x) { return __builtin_bit_cast(uint32_t, x); };
+    auto flt = [](uint32_t x) { return __builtin_bit_cast(float, x); };
+    const auto a = __builtin_amdgcn_permlane32_swap(bits(v0), bits(v2), false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(bits(v1), bits(v3), false, false);
+    const float t = flt(a[0]) + flt(a[1]), u = flt(b[0]) + flt(b[1]);
+    const auto c = __builtin_amdgcn_permlane16_swap(bits(t), bits(u), false, false);
+    return row_fsum(flt(c[0]) + flt(c[1]));
+}
+// Maximum over lanes l, l^16, l^32, l^48 combined with the row: all 64 lanes.
+__device__ __forceinline__ uint32_t umax_all(uint32_t x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    x = max(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return row_umax(max(b[0], b[1]));
+}
+__device__ __forceinline__ uint32_t umax_xor32(uint32_t x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return max(a[0], a[1]);
+}
+
+__device__ __forceinline__ void st16(uint8_t* p, uint32_t v) { *reinterpret_cast<uint16_t*>(p) = (uint16_t)v; }
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int D, int R>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes, const uint32_t* __restrict__ k_sz,
     const uint8_t* __restrict__ v_codes, const uint32_t* __restrict__ v_sz, int Hkv, int n, int chunk,
-    float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
-    constexpr int W16 = D / 16;          // 16-channel code words per token
-    constexpr int VITEMS = (kGroup / 2) * W16 / kWave;  // values: (token pair, word) items per lane
-    // per wave and head: four fp8 pieces of the scaled query, each in MFMA K order (128 bytes)
-    __shared__ __align__(16) uint8_t s_qa[4][R][4][128];
-    __shared__ float s_p[4][R][kGroup];        // per wave: probabilities of its group
+    float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml, __bf16* __restrict__ out) {
+    constexpr int NG = D / 32;  // 32-channel groups: key K blocks and value scale groups
+    constexpr int NT = D / 16;  // 16-channel value tiles
+    constexpr int GPL = NG * R / 4 > 1 ? NG * R / 4 : 1;  // value groups per lane in the weight prep
+    __shared__ __align__(16) uint8_t s_qa[4][4][R][4][128];   // wave, block, head, piece, K position
+    __shared__ __align__(16) uint8_t s_wa[4][R][NG][4][128];  // wave, head, value group, piece, K position
+    __shared__ float s_z[4][R][NG];
     __shared__ float s_red[4][R][D];
     __shared__ float s_ml[4][R][2];
 
@@ -107,16 +204,24 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const int b = blockIdx.z;
     const int unit = b * Hkv + g;
     const int splits = gridDim.x;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: keeps group bases scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: keeps bases scalar
     const int lane = threadIdx.x % kWave;
+    const int col = lane % 16, blk = lane / 16;
+    const int myh = blk % R;  // head of this lane's MFMA result rows
     const int G = (n + kGroup - 1) / kGroup;
     const int t_begin = split * chunk;
     const int t_end = min(n, t_begin + chunk);
-    const int gi_begin = t_begin / kGroup;
-    const int gi_end = (t_end + kGroup - 1) / kGroup;
 
-    // Query channels of this lane: the pair (c0, c0 + 2) sits at MFMA K positions 2 lane, 2 lane + 1
-    // (lanes >= D/2 idle here).  Pre-scaled to log2 units.
+    // never-written LDS positions must read as zero: key K positions >= D, value piece 3
+    {
+        uint32_t* za = reinterpret_cast<uint32_t*>(&s_qa[wave][0][0][0][0]);
+        for (int i = lane; i < 4 * R * 4 * 128 / 4; i += kWave) za[i] = 0u;
+        uint32_t* zw = reinterpret_cast<uint32_t*>(&s_wa[wave][0][0][0][0]);
+        for (int i = lane; i < R * NG * 4 * 128 / 4; i += kWave) zw[i] = 0u;
+    }
+
+    // Query channels c0, c0 + 2 of this lane sit at key K positions 2 lane,
+    // 2 lane + 1 (lanes >= D/2 idle here).  Pre-scaled to log2 units.
     const bool qlane = lane < D / 2;
     const int c0 = qlane ? 32 * (lane / 16) + 16 * ((lane / 8) % 2) + 4 * (lane % 4) + (lane / 4) % 2 : 0;
     float qk[R][2];
@@ -126,266 +231,265 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         qk[r][0] = qlane ? bf16_bits_to_f32(qr[c0]) * scale_log2 : 0.0f;
         qk[r][1] = qlane ? bf16_bits_to_f32(qr[c0 + 2]) * scale_log2 : 0.0f;
     }
-    // keys as MFMA B operand: lane holds token 16 j + lane % 16, code words 2 (lane / 16), + 1
-    const bool kact = lane / 16 < D / 32;
-    const uint32_t koff = (uint32_t)((lane % 16) * (D / 4) + 8 * (lane / 16));
-    // query pieces as MFMA A operand: row lane % 16 = (head block, piece)
-    const int arow = lane % 16;
-    const uint8_t* a_src = &s_qa[wave][(arow / 4) % R][arow % 4][16 * (lane / 16)];
-    const int myh = (lane / 16) % R;  // head of this lane's score rows
-    const UnpackConsts uk = unpack_consts();
-    if (D < 128) {  // K positions past D stay zero
-        for (int i = lane; i < R * 4 * 128 / 4; i += kWave)
-            reinterpret_cast<uint32_t*>(&s_qa[wave][0][0][0])[i] = 0u;
-    }
+    // Key B operand: the lane holds code words 2 blk, 2 blk + 1 (K positions
+    // 32 blk + nibble) of one token; subtile j (0..7) of a step holds tokens
+    // 32 (j/2) + 2 (j%2) + tm0 in its 16 columns, so the lane's two subtiles of
+    // a block carry the tokens u, u + 2 that sit side by side in value K order.
+    const int tm0 = 4 * (col / 2) + col % 2;
+    const bool kact = blk < NG;
+    const uint32_t koff = (uint32_t)(tm0 * (D / 4) + 8 * blk);
+    // Value B operand: channel 16 T + col of block blk of the step, 8 bytes.
+    const uint32_t voff = (uint32_t)((blk * D + col) * 8);
+    // Weight prep: K position of token tm0 within a block (tm0 + 2 follows it),
+    // value groups gbase .. gbase + GPL - 1 for head myh.
+    const int kap = 16 * (col / 8) + 8 * (col % 2) + 2 * ((col / 2) % 4);
+    const int gbase = (blk / R) * GPL;
+    const bool wlane = gbase < NG;
+    // A operand row lane % 16 = (head block, piece); piece k carries scale 16^-k
+    const int ahd = (col / 4) % R, ap = col % 4;
+    const int ascale = (127 - 4 * ap) * 0x01010101;
 
-    // Everything one 32-token group needs from HBM, loaded one group ahead.
+    // Everything one 128-token step needs from HBM, loaded one step ahead.  All
+    // loads are a wave-uniform base plus a 32-bit lane offset.
     struct Stage {
-        uint2 kc[2];
-        uint32_t ksz[2];
-        uint32_t vc[VITEMS][2];
-        uint32_t vsz[VITEMS][2];
+        uint2 kc[8];
+        uint32_t ksz[4][2];
+        uint2 vc[NT];
+        uint32_t vsz[8][GPL];
     };
-    // Lane byte offsets inside a group (constant, unsigned 32-bit) added to
-    // wave-uniform group bases, so loads use scalar base + vector offset.
-    uint32_t vcoff[VITEMS][2], vsoff[VITEMS][2];
-#pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
-        const int item = lane + kWave * it;
-        const int cc = item % W16, pr = item / W16;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            vcoff[it][e] = (uint32_t)((2 * pr + e) * (D / 4) + 4 * cc);
-            vsoff[it][e] = (uint32_t)(((2 * pr + e) * (D / 32) + (cc >> 1)) * 4);
-        }
-    }
-    auto ld32 = [](const uint8_t* base, uint32_t off) {
-        return *reinterpret_cast<const uint32_t*>(base + off);
+    auto ld32 = [](const void* base, uint32_t off) {
+        return *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(base) + off);
     };
-    auto ld64 = [](const uint8_t* base, uint32_t off) {
-        return *reinterpret_cast<const uint2*>(base + off);
+    auto ld64 = [](const void* base, uint32_t off) {
+        return *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + off);
     };
-    auto load_stage = [&](int gi, Stage& st) {
-        const int grp0 = gi * kGroup;
-        const size_t row0 = (size_t)unit * n + grp0;
-        const uint8_t* kcb = k_codes + row0 * (D / 4);
-        const uint8_t* vcb = v_codes + row0 * (D / 4);
-        const uint8_t* vsb = reinterpret_cast<const uint8_t*>(v_sz + row0 * (D / 32));
-        const uint32_t* kszb = k_sz + ((size_t)unit * G + gi) * D;
-        st.ksz[0] = kszb[c0];
-        st.ksz[1] = kszb[c0 + 2];
-        if (grp0 + kGroup <= t_end) {  // wave-uniform: the whole group is in range
+    auto tok_of = [&](int j) { return 32 * (j / 2) + 2 * (j % 2) + tm0; };  // token of subtile j in the step
+    auto kc_off = [&](int j) { return koff + (uint32_t)((32 * (j / 2) + 2 * (j % 2)) * (D / 4)); };
+    const uint32_t kszo = (uint32_t)(c0 * 4);
+    const uint32_t vszo = (uint32_t)((tm0 * NG + gbase) * 4);
+    auto vsz_off = [&](int j, int i) { return vszo + (uint32_t)(((32 * (j / 2) + 2 * (j % 2)) * NG + i) * 4); };
+    auto load_keys = [&](int step, Stage& st) {
+        const int t0 = step * kStep;
+        const int b0 = t0 / kGroup;
+        const uint8_t* kcb = k_codes + ((size_t)unit * n + t0) * (D / 4);
+        const uint32_t* kszb = k_sz + ((size_t)unit * G + b0) * D;
+        if (t0 + kStep <= t_end) {  // wave-uniform: the whole step is in range
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                st.kc[j] = kact ? ld64(kcb, koff + (uint32_t)(j * 16 * (D / 4))) : make_uint2(0u, 0u);
+            for (int j = 0; j < 8; ++j) st.kc[j] = kact ? ld64(kcb, kc_off(j)) : make_uint2(0u, 0u);
 #pragma unroll
-            for (int it = 0; it < VITEMS; ++it) {
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    st.vc[it][e] = ld32(vcb, vcoff[it][e]);
-                    st.vsz[it][e] = ld32(vsb, vsoff[it][e]);
-                }
+            for (int bk = 0; bk < 4; ++bk) {
+                st.ksz[bk][0] = ld32(kszb, kszo + (uint32_t)(bk * D * 4));
+                st.ksz[bk][1] = ld32(kszb, kszo + (uint32_t)((bk * D + 2) * 4));
             }
             return;
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int t = grp0 + 16 * j + lane % 16;
-            st.kc[j] = kact && t < t_end ? ld64(kcb, koff + (uint32_t)(j * 16 * (D / 4))) : make_uint2(0u, 0u);
+        for (int j = 0; j < 8; ++j) {
+            const bool in = kact && t0 + tok_of(j) < t_end;
+            st.kc[j] = in ? ld64(kcb, kc_off(j)) : make_uint2(0u, 0u);
         }
 #pragma unroll
-        for (int it = 0; it < VITEMS; ++it) {
-            const int item = lane + kWave * it;
-            const int pr = item / W16;
+        for (int bk = 0; bk < 4; ++bk) {
+            const bool in = t0 + kGroup * bk < t_end;
+            st.ksz[bk][0] = in ? ld32(kszb, kszo + (uint32_t)(bk * D * 4)) : 0u;
+            st.ksz[bk][1] = in ? ld32(kszb, kszo + (uint32_t)((bk * D + 2) * 4)) : 0u;
+        }
+    };
+    auto load_values = [&](int step, Stage& st) {
+        const int t0 = step * kStep;
+        const int b0 = t0 / kGroup;
+        const uint8_t* vcb = v_codes + ((size_t)unit * G + b0) * D * 8;
+        const uint32_t* vsb = v_sz + ((size_t)unit * n + t0) * NG;
+        if (t0 + kStep <= t_end) {
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const bool in = grp0 + 2 * pr + e < t_end;
-                st.vc[it][e] = in ? ld32(vcb, vcoff[it][e]) : 0u;
-                st.vsz[it][e] = in ? ld32(vsb, vsoff[it][e]) : 0u;  // s = z = 0 adds nothing
-            }
+            for (int T = 0; T < NT; ++T) st.vc[T] = ld64(vcb, voff + (uint32_t)(128 * T));
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int i = 0; i < GPL; ++i) st.vsz[j][i] = wlane ? ld32(vsb, vsz_off(j, i)) : 0u;
+            return;
+        }
+        const bool vin = t0 + kGroup * blk < t_end;
+#pragma unroll
+        for (int T = 0; T < NT; ++T) st.vc[T] = vin ? ld64(vcb, voff + (uint32_t)(128 * T)) : make_uint2(0u, 0u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool in = wlane && t0 + tok_of(j) < t_end;
+#pragma unroll
+            for (int i = 0; i < GPL; ++i) st.vsz[j][i] = in ? ld32(vsb, vsz_off(j, i)) : 0u;  // s = z = 0
         }
     };
 
-    // online-softmax state of this wave (m wave-uniform; l, acc per lane)
-    // a lane's value items all use the same code word (item % W16 == lane % W16), so one accumulator set
-    float m_run[R], lacc[R], acc[R][16], wsum[R], zacc[R];
+    // online-softmax state of this lane's head (uniform within its 16-lane row)
+    float m_run = -INFINITY, lacc = 0.0f;
+    float acc[NT], zacc[GPL];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        m_run[r] = -INFINITY;
-        lacc[r] = 0.0f;
-        wsum[r] = 0.0f;
-        zacc[r] = 0.0f;
+    for (int T = 0; T < NT; ++T) acc[T] = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) acc[r][c] = 0.0f;
-    }
+    for (int i = 0; i < GPL; ++i) zacc[i] = 0.0f;
 
-    auto process = [&](int gi, const Stage& st) {
-        const int grp0 = gi * kGroup;
-        // ---- keys: fold the group's fp16 scales into the query, split into fp8 pieces ----
-        const float s0 = half_bits_to_f32(st.ksz[0] & 0xFFFFu), z0 = half_bits_to_f32(st.ksz[0] >> 16);
-        const float s1 = half_bits_to_f32(st.ksz[1] & 0xFFFFu), z1 = half_bits_to_f32(st.ksz[1] >> 16);
-        float bias[R], kmul[R];
+    // One step; the next step's loads (step + 4) go out as soon as this step's
+    // registers of the same kind are consumed.
+    auto process = [&](int step, Stage& st, bool more) {
+        const int t0 = step * kStep;
+        // ---- keys: fold each block's fp16 scales into the query ----
+        float x[4][R][2], zp[4][R];
+        uint32_t mxb[4][R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float x0 = qk[r][0] * s0, x1 = qk[r][1] * s1;
-            // common power of two putting max |x| in [128, 256): every piece stays finite in e4m3
-            const float mx = dpp_max<kWave>(fmaxf(fabsf(x0), fabsf(x1)));
-            const int sig = 8 - __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(mx));
-            x0 = __builtin_amdgcn_ldexpf(x0, sig);
-            x1 = __builtin_amdgcn_ldexpf(x1, sig);
-            uint32_t p01 = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-            f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(p01, false);
-            x0 -= f[0];
-            x1 -= f[1];
-            p01 = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, p01, true);
-            f = __builtin_amdgcn_cvt_pk_f32_fp8(p01, true);
-            x0 -= f[0];
-            x1 -= f[1];
-            uint32_t p23 = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-            f = __builtin_amdgcn_cvt_pk_f32_fp8(p23, false);
-            x0 -= f[0];
-            x1 -= f[1];
-            p23 = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, p23, true);
-            if (qlane) {
-                *reinterpret_cast<uint16_t*>(&s_qa[wave][r][0][2 * lane]) = (uint16_t)p01;
-                *reinterpret_cast<uint16_t*>(&s_qa[wave][r][1][2 * lane]) = (uint16_t)(p01 >> 16);
-                *reinterpret_cast<uint16_t*>(&s_qa[wave][r][2][2 * lane]) = (uint16_t)p23;
-                *reinterpret_cast<uint16_t*>(&s_qa[wave][r][3][2 * lane]) = (uint16_t)(p23 >> 16);
-            }
-            bias[r] = dpp_sum<kWave>(fmaf(qk[r][0], z0, qk[r][1] * z1));
-            kmul[r] = __builtin_amdgcn_ldexpf(2.0f, -sig);  // fp4 holds code / 2
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // ---- keys: scores of the group's 32 tokens, two 16-token MFMAs (rows = head x piece) ----
-        i32x8 A;
-        {
-            const u32x4 lo = *reinterpret_cast<const u32x4*>(a_src);
-            const u32x4 hi = *reinterpret_cast<const u32x4*>(a_src + 64);
-            A = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        }
-        float km = kmul[0], kb = bias[0];
-#pragma unroll
-        for (int r = 1; r < R; ++r) {
-            km = myh == r ? kmul[r] : km;
-            kb = myh == r ? bias[r] : kb;
-        }
-        float sc[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t w0 = st.kc[j].x, w1 = st.kc[j].y;
-            const i32x8 Bk = {(int)(w0 & 0x33333333u), (int)((w0 >> 2) & 0x33333333u),
-                              (int)(w1 & 0x33333333u), (int)((w1 >> 2) & 0x33333333u), 0, 0, 0, 0};
-            const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bk, f32x4{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                             0, 4, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
-            sc[j] = fmaf((c[0] + c[1]) + (c[2] + c[3]), km, kb);
-        }
-        if (grp0 + kGroup > t_end) {  // wave-uniform: the group's tail is past the range
-#pragma unroll
-            for (int j = 0; j < 2; ++j) sc[j] = grp0 + 16 * j + lane % 16 < t_end ? sc[j] : -INFINITY;
-        }
-        // ---- softmax bookkeeping for this wave (wave-uniform per head) ----
-        const float rowmax = dpp_max<16>(fmaxf(sc[0], sc[1]));
-        float m_new[R];
-        bool rescale = false;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float mx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rowmax), 16 * r));
-            m_new[r] = fmaxf(m_run[r], mx);
-            rescale |= m_new[r] != m_run[r];
-        }
-        float mm = m_new[0];
-#pragma unroll
-        for (int r = 1; r < R; ++r) mm = myh == r ? m_new[r] : mm;
-        // probabilities of the group's tokens, once per token (0 for masked tokens)
-        if (lane < 16 * R) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) s_p[wave][myh][16 * j + lane % 16] = __builtin_amdgcn_exp2f(sc[j] - mm);
-        }
-        // probabilities of the group's tokens, once per token (0 for masked tokens)
-        if (rescale) {  // wave-uniform
+        for (int bk = 0; bk < 4; ++bk) {
+            const float s0 = half_bits_to_f32(st.ksz[bk][0] & 0xFFFFu), z0 = half_bits_to_f32(st.ksz[bk][0] >> 16);
+            const float s1 = half_bits_to_f32(st.ksz[bk][1] & 0xFFFFu), z1 = half_bits_to_f32(st.ksz[bk][1] >> 16);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const float alpha = exp2f(m_run[r] - m_new[r]);  // 0 on the first group (m_run = -inf)
-                lacc[r] *= alpha;
-                wsum[r] *= alpha;
-                zacc[r] *= alpha;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) acc[r][c] *= alpha;
-                m_run[r] = m_new[r];
+                x[bk][r][0] = qk[r][0] * s0;
+                x[bk][r][1] = qk[r][1] * s1;
+                mxb[bk][r] = __builtin_bit_cast(uint32_t, fmaxf(fabsf(x[bk][r][0]), fabsf(x[bk][r][1])));
+                zp[bk][r] = fmaf(qk[r][0], z0, qk[r][1] * z1);
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // ---- values: token pairs ----
+        // per (block, head): max |x| sets the pieces' power of two, sum q z is the block's score offset
+        float bias[4][R], kmul[4][R];
 #pragma unroll
-        for (int it = 0; it < VITEMS; ++it) {
-            const int item = lane + kWave * it;
-            const int cc = item % W16, pr = item / W16;
-            const uint32_t plo = __builtin_amdgcn_perm(st.vc[it][1], st.vc[it][0], 0x05040100u);
-            const uint32_t phi = __builtin_amdgcn_perm(st.vc[it][1], st.vc[it][0], 0x07060302u);
-            uint32_t hl[8], hh[8];
-            unpack16(plo, uk, hl);  // pair j: (token 0 channel j, token 1 channel j)
-            unpack16(phi, uk, hh);  // pair j: (token 0 channel j+8, token 1 channel j+8)
-            const float sA = half_bits_to_f32(st.vsz[it][0] & 0xFFFFu), zA = half_bits_to_f32(st.vsz[it][0] >> 16);
-            const float sB = half_bits_to_f32(st.vsz[it][1] & 0xFFFFu), zB = half_bits_to_f32(st.vsz[it][1] >> 16);
+        for (int r = 0; r < R; ++r) {
+            const uint32_t mrow = umax4_rows(mxb[0][r], mxb[1][r], mxb[2][r], mxb[3][r]);
+            const float zrow = fsum4_rows(zp[0][r], zp[1][r], zp[2][r], zp[3][r]);
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float pA = s_p[wave][r][2 * pr];
-                const float pB = s_p[wave][r][2 * pr + 1];
-                f16x2 wv;
-                wv[0] = (_Float16)(pA * sA);
-                wv[1] = (_Float16)(pB * sB);
-                uint32_t wu;
-                __builtin_memcpy(&wu, &wv, 4);
-                wsum[r] = dot2(wu, 0x3C003C00u, wsum[r]);  // exact sum of the fp16 weights
-                zacc[r] = fmaf(pA, zA, fmaf(pB, zB, zacc[r]));
-                if (cc == 0) lacc[r] += pA + pB;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    acc[r][j] = dot2(wu, hl[j], acc[r][j]);
-                    acc[r][8 + j] = dot2(wu, hh[j], acc[r][8 + j]);
+            for (int bk = 0; bk < 4; ++bk) {
+                const uint32_t e = piece_exp((uint32_t)__builtin_amdgcn_readlane((int)mrow, 16 * bk));
+                bias[bk][r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zrow), 16 * bk));
+                kmul[bk][r] = pow2_bits(e + 1);  // e2m1 holds code / 2
+                uint32_t w[2];
+                e4m3_pieces<4>(x[bk][r][0], x[bk][r][1], e, w);
+                if (qlane) {
+                    st16(&s_qa[wave][bk][r][0][2 * lane], w[0]);
+                    st16(&s_qa[wave][bk][r][1][2 * lane], w[0] >> 16);
+                    st16(&s_qa[wave][bk][r][2][2 * lane], w[1]);
+                    st16(&s_qa[wave][bk][r][3][2 * lane], w[1] >> 16);
                 }
             }
         }
+        wave_sync_lds();
+        // ---- keys: 8 MFMAs of 16 tokens, result rows = (head, piece) ----
+        float sc[8];
+#pragma unroll
+        for (int bk = 0; bk < 4; ++bk) {
+            const i32x8 A = a_operand(&s_qa[wave][bk][ahd][ap][16 * blk]);
+            float km = kmul[bk][0], kb = bias[bk][0];
+#pragma unroll
+            for (int r = 1; r < R; ++r) {
+                km = myh == r ? kmul[bk][r] : km;
+                kb = myh == r ? bias[bk][r] : kb;
+            }
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = 2 * bk + jj;
+                const f32x4 c = mfma_f8_f4(A, codes_e2m1(st.kc[j]), ascale);
+                sc[j] = fmaf((c[0] + c[1]) + (c[2] + c[3]), km, kb);
+            }
+        }
+        if (more) load_keys(step + 4, st);
+        if (t0 + kStep > t_end) {  // wave-uniform: the step's tail is past the range
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sc[j] = t0 + tok_of(j) < t_end ? sc[j] : -INFINITY;
+        }
+        // ---- online softmax over the step (a 16-lane row holds all 128 tokens of its head) ----
+        float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        const float m_new = fmaxf(m_run, fkey_inv(row_imax(fkey(mx))));
+        if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {  // wave-uniform
+            const float alpha = exp2f(m_run - m_new);  // 0 on the first step (m_run = -inf)
+            lacc *= alpha;
+#pragma unroll
+            for (int T = 0; T < NT; ++T) acc[T] *= alpha;
+#pragma unroll
+            for (int i = 0; i < GPL; ++i) zacc[i] *= alpha;
+            m_run = m_new;
+        }
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(sc[j] - m_run);  // 0 for masked tokens
+            lacc += p[j];
+        }
+        // ---- values: weights w = p s per (token, value group), three e4m3 pieces ----
+        float wv[8][GPL];
+        float wmax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+#pragma unroll
+            for (int i = 0; i < GPL; ++i) {
+                wv[j][i] = p[j] * half_bits_to_f32(st.vsz[j][i] & 0xFFFFu);
+                zacc[i] = fmaf(p[j], half_bits_to_f32(st.vsz[j][i] >> 16), zacc[i]);
+                wmax = fmaxf(wmax, wv[j][i]);
+            }
+        }
+        // max over the lanes of this head: all 64 (R = 1), rows b and b + 2 (R = 2), the row (R = 4)
+        uint32_t wmb = __builtin_bit_cast(uint32_t, wmax);
+        if constexpr (R == 1) wmb = umax_all(wmb);
+        else if constexpr (R == 2) wmb = row_umax(umax_xor32(wmb));
+        else wmb = row_umax(wmb);
+        const uint32_t ew = piece_exp(wmb);
+#pragma unroll
+        for (int bk = 0; bk < 4; ++bk) {
+#pragma unroll
+            for (int i = 0; i < GPL; ++i) {
+                uint32_t w[2];
+                e4m3_pieces<3>(wv[2 * bk][i], wv[2 * bk + 1][i], ew, w);
+                if (wlane) {
+                    uint8_t* dst = &s_wa[wave][myh][gbase + i][0][32 * bk + kap];
+                    st16(dst, w[0]);
+                    st16(dst + 128, w[0] >> 16);
+                    st16(dst + 256, w[1]);
+                }
+            }
+        }
+        const float wmul = pow2_bits(ew + 1);
+        wave_sync_lds();
+        // ---- values: NT MFMAs of 16 channels x 128 tokens, result rows = (head, piece) ----
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+            const i32x8 A = a_operand(&s_wa[wave][ahd][gg][ap][16 * blk]);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int T = 2 * gg + tt;
+                const f32x4 c = mfma_f8_f4(A, codes_e2m1(st.vc[T]), ascale);
+                acc[T] = fmaf((c[0] + c[1]) + c[2], wmul, acc[T]);
+            }
+        }
+        if (more) load_values(step + 4, st);
     };
 
-    // each wave walks groups wave, wave + 4, ... of this split, one group prefetched
-    // (a second prefetched group costs more in occupancy than it gains)
+    // each wave walks steps wave, wave + 4, ... of this split
     {
-        Stage A, Bst;
-        int gi = gi_begin + wave;
-        if (gi < gi_end) load_stage(gi, A);
-        while (gi < gi_end) {
-            if (gi + 4 < gi_end) load_stage(gi + 4, Bst);
-            process(gi, A);
-            gi += 4;
-            if (gi >= gi_end) break;
-            if (gi + 4 < gi_end) load_stage(gi + 4, A);
-            process(gi, Bst);
-            gi += 4;
+        const int step_begin = t_begin / kStep;
+        const int step_end = (t_end + kStep - 1) / kStep;
+        Stage st;
+        int s = step_begin + wave;
+        if (s < step_end) {
+            load_keys(s, st);
+            load_values(s, st);
         }
+        for (; s < step_end; s += 4) process(s, st, s + 4 < step_end);
     }
 
-    // ---- this wave's partial: remove the unpack offsets, reduce lanes holding the same word ----
+    // ---- this wave's partial: l and the zero-point sums per row, then out = acc + sum p z ----
+    const float lsum = row_fsum(lacc);
+    float zs[GPL];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        float l = lacc[r];
+    for (int i = 0; i < GPL; ++i) zs[i] = row_fsum(zacc[i]);
+    if (col == 0) {
+        if (wlane) {
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) l += __shfl_xor(l, o, kWave);
-        if (lane == 0) {
-            s_ml[wave][r][0] = m_run[r];
-            s_ml[wave][r][1] = l;
+            for (int i = 0; i < GPL; ++i) s_z[wave][myh][gbase + i] = zs[i];
         }
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            float x = acc[r][c] - pair_offset(c & 7) * wsum[r] + zacc[r];
-#pragma unroll
-            for (int o = W16; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
-            if (lane < W16) s_red[wave][r][16 * lane + c] = x;
+        if (blk < R) {
+            s_ml[wave][blk][0] = m_run;
+            s_ml[wave][blk][1] = lsum;
         }
+    }
+    wave_sync_lds();
+    if (blk < R) {
+#pragma unroll
+        for (int T = 0; T < NT; ++T) s_red[wave][blk][16 * T + col] = acc[T] + s_z[wave][blk][T / 2];
     }
     __syncthreads();
     // ---- merge the 4 waves (log-sum-exp) into this split's partial ----
@@ -398,6 +502,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
             const float f = exp2f(s_ml[w][r][0] - M);  // 0 for a wave that saw no tokens
             x = fmaf(s_red[w][r][d], f, x);
             L = fmaf(s_ml[w][r][1], f, L);
+        }
+        if (splits == 1) {  // the workgroup saw every token: normalise here
+            out[((size_t)(b * Hkv + g) * R + r) * D + d] = (__bf16)(x / L);
+            continue;
         }
         const size_t o = (((size_t)(b * Hkv + g) * R + r) * splits + split);
         ws_acc[o * D + d] = x;
@@ -435,9 +543,9 @@ hipError_t launch_dr(const void* q, const uint8_t* k_codes, const uint32_t* k_sz
     float* ws_ml = ws_acc + (size_t)B * Hq * plan.splits * D;
     hipLaunchKernelGGL((decode_partial_kernel<D, R>), dim3(plan.splits, Hkv, B), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), k_codes, k_sz, v_codes, v_sz, Hkv, n, plan.chunk,
-                       scale_log2, ws_acc, ws_ml);
+                       scale_log2, ws_acc, ws_ml, static_cast<__bf16*>(out));
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || plan.splits == 1) return e;  // one split: the partial kernel wrote out
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(B * Hq), dim3(D), 0, stream, ws_acc, ws_ml,
                        plan.splits, static_cast<__bf16*>(out));
     return hipGetLastError();

@@ -18,7 +18,7 @@ hipError_t launch_select_topk(const float* scores, int B, int Hkv, int T_ctx, in
 // Decode: split plan shared by the workspace-size query and the launcher.
 struct DecodePlan {
     int splits;  // token ranges per (sequence, KV head)
-    int chunk;   // tokens per split (multiple of 32)
+    int chunk;   // tokens per split (multiple of 512)
 };
 DecodePlan decode_plan(int B, int Hkv, int n_keep);
 size_t decode_ws_bytes(int B, int Hq, int D, const DecodePlan& plan);

@@ -11,8 +11,8 @@
 // evaluation bit for bit.
 //
 // HBM-bound gather: each kept row is read once (coalesced 4-byte lane loads of
-// two channels), each packed byte written once (dword stores assembled with
-// lane shuffles).
+// two channels), each packed byte written once (key codes: dword stores
+// assembled with lane shuffles; value codes: one 16-byte store per lane).
 #include "common.h"
 #include "kernels.h"
 
@@ -103,43 +103,52 @@ __global__ __launch_bounds__(64) void quant_pack_k_kernel(
     }
 }
 
-// Values: each wave handles TW = 128/D tokens per step; lane owns two channels,
-// 16 lanes form one 32-channel group.
-template <typename T, int D, int kTokPerWave>
-__global__ __launch_bounds__(256) void quant_pack_v_kernel(
+// Values: one wave per (block of 32 kept tokens, KV head, sequence).  Lane l
+// owns channels 2l, 2l+1 (D/2 active lanes); a 16-lane row is one 32-channel
+// group, so each token's min / max is a row reduction.  The codes are gathered
+// along tokens: the lane ends with the 32 codes of each of its two channels
+// (8 bytes each, the block's token 4m+j in bits 2j..2j+1 of byte m) and stores
+// both in one 16-byte write; tokens past n_keep stay code 0.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void quant_pack_v_kernel(
     const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, int n_keep, int Hkv,
     uint8_t* __restrict__ v_codes, uint32_t* __restrict__ v_sz) {
-    constexpr int LT = D / 2;         // lanes per token
-    constexpr int TW = kWave / LT;    // tokens per wave step
+    const int gi = blockIdx.x;
     const int unit = blockIdx.z * Hkv + blockIdx.y;
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
-    const int slot = lane / LT;
-    const int lt = lane % LT;
-    const int c = 2 * lt;
+    const int lane = threadIdx.x;
+    const bool active = lane < D / 2;
+    const int c = 2 * (active ? lane : 0);
+    const int G = (n_keep + kGroup - 1) / kGroup;
+    const int t0 = gi * kGroup;
+    const int cnt = min(kGroup, n_keep - t0);
     const T* base = v + (size_t)unit * T_ctx * D;
-    const int tb = (blockIdx.x * 4 + wave) * kTokPerWave;
-#pragma unroll 2
-    for (int s = 0; s < kTokPerWave; s += TW) {
-        const int t = tb + s + slot;
-        const bool valid = t < n_keep;
-        Pair x = {0.0f, 0.0f};
-        if (valid) {
-            const int pos = idx ? idx[(size_t)unit * n_keep + t] : t;
-            x = load_pair<T>(base + (size_t)pos * D, c);
-        }
-        float mn = group_min<16>(fminf(x.a, x.b));
-        float mx = group_max<16>(fmaxf(x.a, x.b));
-        const GroupParams p = group_params(mn, mx);
-        uint32_t nib = code_of(x.a, p) | (code_of(x.b, p) << 2);
-        uint32_t word = group_or<8>(nib << (4 * (lane & 7)));
-        if (valid) {
-            if ((lt & 15) == 0)
-                v_sz[((size_t)unit * n_keep + t) * (D / 32) + (lt >> 4)] = p.word;
-            if ((lt & 7) == 0)
-                *reinterpret_cast<uint32_t*>(v_codes + ((size_t)unit * n_keep + t) * (D / 4) + 4 * (lt >> 3)) = word;
+    const int32_t* ids = idx ? idx + (size_t)unit * n_keep + t0 : nullptr;
+
+    Pair x[kGroup];
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) {
+        x[t] = {0.0f, 0.0f};
+        if (t < cnt && active) {
+            const int pos = ids ? ids[t] : t0 + t;
+            x[t] = load_pair<T>(base + (size_t)pos * D, c);
         }
     }
+    uint32_t wa[2] = {0u, 0u}, wb[2] = {0u, 0u};
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) {
+        if (t < cnt) {  // uniform across the wave
+            const float mn = dpp_min<16>(fminf(x[t].a, x[t].b));
+            const float mx = dpp_max<16>(fmaxf(x[t].a, x[t].b));
+            const GroupParams p = group_params(mn, mx);
+            wa[t / 16] |= code_of(x[t].a, p) << (2 * (t % 16));
+            wb[t / 16] |= code_of(x[t].b, p) << (2 * (t % 16));
+            if (active && (lane & 15) == 0)
+                v_sz[((size_t)unit * n_keep + t0 + t) * (D / 32) + (lane >> 4)] = p.word;
+        }
+    }
+    if (active)
+        *reinterpret_cast<uint4*>(v_codes + (((size_t)unit * G + gi) * D + c) * 8) =
+            make_uint4(wa[0], wa[1], wb[0], wb[1]);
 }
 
 template <typename T, int D>
@@ -152,10 +161,7 @@ hipError_t launch_typed(const void* k, const void* v, const int32_t* idx, int B,
                        static_cast<const T*>(k), idx, T_ctx, n_keep, Hkv, k_codes, k_sz);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    constexpr int kTokPerWave = 8;
-    const int per_block = 4 * kTokPerWave;
-    dim3 gv((n_keep + per_block - 1) / per_block, Hkv, B);
-    hipLaunchKernelGGL((quant_pack_v_kernel<T, D, kTokPerWave>), gv, dim3(256), 0, stream,
+    hipLaunchKernelGGL((quant_pack_v_kernel<T, D>), gk, dim3(64), 0, stream,
                        static_cast<const T*>(v), idx, T_ctx, n_keep, Hkv, v_codes, v_sz);
     return hipGetLastError();
 }

@@ -58,13 +58,17 @@ enum { MINIKV_GROUP = 32 };  /* quantisation group: 32 kept tokens (K) or 32 cha
  * Packed 2-bit cache of n_keep tokens per (sequence, KV head): the "compact
  * layout" of the method-details section.  All four arrays are caller-owned
  * device buffers:
- *   k_codes  uint8 [B][Hkv][n_keep][D/4]         4 codes per byte: channel 4m+j in bits 2j..2j+1
- *   k_sz     uint32[B][Hkv][ceil(n_keep/32)][D]  per channel, per group of 32 kept tokens
- *   v_codes  uint8 [B][Hkv][n_keep][D/4]
+ *   k_codes  uint8 [B][Hkv][n_keep][D/4]         packed along channels: byte m of a token
+ *                                                holds channels 4m..4m+3, channel 4m+j in bits 2j..2j+1
+ *   k_sz     uint32[B][Hkv][G][D]                per channel, per block of 32 kept tokens
+ *   v_codes  uint8 [B][Hkv][G][D][8]             packed along tokens: the 8 bytes of (block, channel)
+ *                                                hold its 32 codes, token 4m+j of the block in bits
+ *                                                2j..2j+1 of byte m; tokens past n_keep are code 0
  *   v_sz     uint32[B][Hkv][n_keep][D/32]        per token, per group of 32 channels
- * A k_sz / v_sz word holds fp16 scale s in bits 0..15 and fp16 zero z in bits
- * 16..31; a code c stands for c*s + z.  Kept tokens are stored in ascending
- * position order; the last key group of a row may hold fewer than 32 tokens.
+ * with G = ceil(n_keep/32).  A k_sz / v_sz word holds fp16 scale s in bits
+ * 0..15 and fp16 zero z in bits 16..31; a code c stands for c*s + z.  Kept
+ * tokens are stored in ascending position order; the last key group of a row
+ * may hold fewer than 32 tokens.
  */
 typedef struct {
     uint8_t *k_codes;
@@ -154,8 +158,8 @@ int minikv_decode_attn(const void *q, const minikv_packed_t *cache, int Hq, floa
 
 /* ---- host helpers (no GPU work) ---- */
 
-/* Bytes of the packed cache: per (sequence, KV head) n*D/4 + ceil(n/32)*D*4 +
- * n*D/4 + n*(D/32)*4.  Returns 0 for invalid sizes. */
+/* Bytes of the packed cache: per (sequence, KV head), G = ceil(n/32):
+ * n*D/4 + G*D*4 + G*32*D/4 + n*(D/32)*4.  Returns 0 for invalid sizes. */
 size_t minikv_packed_bytes(int B, int Hkv, int n_keep, int D);
 
 /* Workspace bytes minikv_decode_attn needs for this shape (0 for invalid sizes). */

@@ -45,6 +45,8 @@ from .minikv_ref import (  # noqa: F401
     code_near_ties,
     pack_codes_ref,
     unpack_codes_ref,
+    pack_value_codes_ref,
+    unpack_value_codes_ref,
     sz_words_ref,
     dequant_ref,
     decode_ref,

@@ -12,9 +12,13 @@ Layouts (all row-major):
   q, o        [B, Hq, T, D]      k, v      [B, Hkv, T, D]
   lse         [B, Hq, T]         scores    [B, Hkv, T]
   idx         [B, Hkv, n_keep]   int32, ascending token positions
-  k_codes     [B, Hkv, n_keep, D/4] uint8    k_scale/k_zero [B, Hkv, ceil(n_keep/32), D] fp16
-  v_codes     [B, Hkv, n_keep, D/4] uint8    v_scale/v_zero [B, Hkv, n_keep, D/32]      fp16
-A code byte m of a row holds channels 4m..4m+3; channel 4m+j sits in bits 2j..2j+1.
+  k_codes     [B, Hkv, n_keep, D/4] uint8         k_scale/k_zero [B, Hkv, ceil(n_keep/32), D] fp16
+  v_codes     [B, Hkv, ceil(n_keep/32), D, 8] uint8  v_scale/v_zero [B, Hkv, n_keep, D/32]  fp16
+Keys are packed along channels: byte m of a token's row holds channels
+4m..4m+3, channel 4m+j in bits 2j..2j+1.  Values are packed along tokens, in
+blocks of 32 kept tokens: the 8 bytes of (block, channel) hold the channel's
+32 codes, byte m holding tokens 4m..4m+3 of the block, token 4m+j in bits
+2j..2j+1; tokens past n_keep in the last block have code 0.
 """
 
 import math
@@ -266,6 +270,25 @@ def unpack_codes_ref(packed):
     return np.stack(parts, axis=-1).reshape(p.shape[:-1] + (p.shape[-1] * 4,)).astype(np.uint8)
 
 
+def pack_value_codes_ref(codes):
+    """Value codes [B, Hkv, n, D] -> token-packed blocks [B, Hkv, ceil(n/32), D, 8] (zero padded)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    B, Hkv, n, D = c.shape
+    G = -(-n // GROUP)
+    pad = np.zeros((B, Hkv, G * GROUP, D), np.uint8)
+    pad[:, :, :n, :] = c
+    blocks = pad.reshape(B, Hkv, G, GROUP, D)
+    return pack_codes_ref(np.swapaxes(blocks, 3, 4))  # pack the 32 tokens of each (block, channel)
+
+
+def unpack_value_codes_ref(packed, n):
+    """Inverse of pack_value_codes_ref for the first n tokens: -> codes [B, Hkv, n, D]."""
+    p = np.asarray(packed, dtype=np.uint8)
+    B, Hkv, G, D, _ = p.shape
+    c = np.swapaxes(unpack_codes_ref(p), 3, 4)  # [B, Hkv, G, 32, D]
+    return c.reshape(B, Hkv, G * GROUP, D)[:, :, :n, :]
+
+
 def sz_words_ref(scale, zero):
     """Interleave fp16 scale / zero into 32-bit words: scale in bits 0..15, zero in 16..31."""
     s = np.asarray(scale, dtype=np.float16).view(np.uint16).astype(np.uint32)
@@ -319,7 +342,7 @@ def quant_pack_ref(k, v, idx=None, return_u=False):
         "k_codes": pack_codes_ref(k_codes),
         "k_scale": k_scale,
         "k_zero": k_zero,
-        "v_codes": pack_codes_ref(c.reshape(B, Hkv, n, D)),
+        "v_codes": pack_value_codes_ref(c.reshape(B, Hkv, n, D)),
         "v_scale": s16,
         "v_zero": z16,
     }
@@ -344,8 +367,8 @@ def dequant_ref(packed, D=None):
     Returns (k_hat [B, Hkv, n, D], v_hat [B, Hkv, n, D]).
     """
     kc = unpack_codes_ref(packed["k_codes"]).astype(np.float64)
-    vc = unpack_codes_ref(packed["v_codes"]).astype(np.float64)
     B, Hkv, n, Dk = kc.shape
+    vc = unpack_value_codes_ref(packed["v_codes"], n).astype(np.float64)
     ks = np.asarray(packed["k_scale"], np.float64)
     kz = np.asarray(packed["k_zero"], np.float64)
     tok_group = np.arange(n) // GROUP
@@ -390,11 +413,12 @@ def decode_ref(q, packed, sm_scale=None):
 def packed_bytes_ref(B, Hkv, n_keep, D):
     """Bytes of the packed cache: codes, per-group K scale/zero, per-token V scale/zero.
 
-    Per (sequence, KV head): K codes n*D/4 + K scale/zero ceil(n/32)*D*4 +
-    V codes n*D/4 + V scale/zero n*(D/32)*4.
+    Per (sequence, KV head), with G = ceil(n/32): K codes n*D/4 + K scale/zero
+    G*D*4 + V codes G*32*D/4 (whole 32-token blocks) + V scale/zero n*(D/32)*4.
     """
     n = int(n_keep)
-    per = n * D // 4 + (-(-n // GROUP)) * D * 4 + n * D // 4 + n * (D // GROUP) * 4
+    G = -(-n // GROUP)
+    per = n * D // 4 + G * D * 4 + G * GROUP * D // 4 + n * (D // GROUP) * 4
     return B * Hkv * per
 
 

@@ -215,6 +215,28 @@ def test_pack_roundtrip():
     assert np.array_equal(oracle.unpack_codes_ref(p), c)
 
 
+def test_value_code_layout_by_hand():
+    # one code 3 at kept token 37 (block 1, token 5 of the block), channel 5:
+    # byte (37 - 32) // 4 = 1 of (block 1, channel 5), bits 2 * ((37 - 32) % 4) = 2..3
+    c = np.zeros((1, 1, 40, 8), np.uint8)
+    c[0, 0, 37, 5] = 3
+    p = oracle.pack_value_codes_ref(c)
+    assert p.shape == (1, 1, 2, 8, 8)
+    want = np.zeros_like(p)
+    want[0, 0, 1, 5, 1] = 3 << 2
+    assert np.array_equal(p, want)
+    # every token of a 32-token block in its own bit pair, tail tokens zero
+    rng = np.random.default_rng(4)
+    c = rng.integers(0, 4, size=(2, 3, 45, 64)).astype(np.uint8)
+    p = oracle.pack_value_codes_ref(c)
+    for (b, h, t, ch) in [(0, 0, 0, 0), (1, 2, 44, 63), (0, 1, 31, 7), (1, 0, 32, 40)]:
+        byte = int(p[b, h, t // 32, ch, (t % 32) // 4])
+        assert (byte >> (2 * (t % 4))) & 3 == c[b, h, t, ch]
+    assert not p[:, :, 1, :, 4:].any()          # tokens 45..63 of block 1 are padding
+    assert not (p[:, :, 1, :, 3] >> 2).any()    # tokens 45..47 in byte 3
+    assert np.array_equal(oracle.unpack_value_codes_ref(p, 45), c)
+
+
 def test_sz_words_layout():
     w = oracle.sz_words_ref(np.float16(1.0), np.float16(-2.0))
     assert int(w) == (0xC000 << 16) | 0x3C00
@@ -225,11 +247,12 @@ def test_bit_accounting_closed_form():
     assert oracle.packed_bytes_ref(1, 1, 64, 64) == 3072
     assert oracle.compression_ratio_ref(256, 64, 64) == 0.953125
     assert oracle.compression_ratio_ref(256, 256, 64) == 0.8125     # 2-bit alone: 81.25 %
-    # LLaMA2-7B-shaped: 614 kept of 4096, D = 128 -> 59,360 B per head
-    assert oracle.packed_bytes_ref(1, 1, 614, 128) == 59360
-    assert abs(oracle.compression_ratio_ref(4096, 614, 128) - (1 - 59360 / 2097152)) < 1e-15
-    # prefill 16k: 2457 kept -> 235,984 B per head
-    assert oracle.packed_bytes_ref(1, 1, 2457, 128) == 235984
+    # LLaMA2-7B-shaped: 614 kept of 4096, D = 128, 20 blocks:
+    # 614*32 + 20*512 + 20*1024 + 614*16 = 60,192 B per head
+    assert oracle.packed_bytes_ref(1, 1, 614, 128) == 60192
+    assert abs(oracle.compression_ratio_ref(4096, 614, 128) - (1 - 60192 / 2097152)) < 1e-15
+    # prefill 16k: 2457 kept, 77 blocks: 2457*32 + 77*512 + 77*1024 + 2457*16 = 236,208 B
+    assert oracle.packed_bytes_ref(1, 1, 2457, 128) == 236208
     # the arrays the oracle produces have exactly that many bytes
     d = synth.tiny_inputs()
     idx = np.broadcast_to(np.arange(64, dtype=np.int32) * 4, (1, 2, 64))
@@ -460,7 +483,7 @@ def test_decode_bruteforce_loops():
     kb, vb = p["k_codes"][0, 0], p["v_codes"][0, 0]
     khat = [[((int(kb[t, c // 4]) >> (2 * (c % 4))) & 3) * float(p["k_scale"][0, 0, t // 32, c])
              + float(p["k_zero"][0, 0, t // 32, c]) for c in range(D)] for t in range(n)]
-    vhat = [[((int(vb[t, c // 4]) >> (2 * (c % 4))) & 3) * float(p["v_scale"][0, 0, t, c // 32])
+    vhat = [[((int(vb[t // 32, c, (t % 32) // 4]) >> (2 * (t % 4))) & 3) * float(p["v_scale"][0, 0, t, c // 32])
              + float(p["v_zero"][0, 0, t, c // 32]) for c in range(D)] for t in range(n)]
     logits = [sum(q[0, 0, c] * khat[t][c] for c in range(D)) / math.sqrt(D) for t in range(n)]
     m = max(logits)
