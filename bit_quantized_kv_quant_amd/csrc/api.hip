@@ -43,7 +43,7 @@ size_t minikv_packed_bytes(int B, int Hkv, int n_keep, int D) {
 
 size_t minikv_decode_ws_bytes(int B, int Hq, int Hkv, int n_keep, int D) {
     if (B < 1 || Hq < 1 || Hkv < 1 || n_keep < 1 || Hq % Hkv || !supported_d(D)) return 0;
-    return minikv::decode_ws_bytes(B, Hq, D, minikv::decode_plan(B, Hkv, n_keep));
+    return minikv::decode_ws_bytes(B, Hq, D, minikv::decode_plan(B, Hq, Hkv, n_keep, D));
 }
 
 int minikv_keep_count(int T, int pct_milli) {
@@ -157,7 +157,7 @@ int minikv_decode_attn(const void* q, const minikv_packed_t* cache, int Hq, floa
     if (misaligned(q) || misaligned(out) || misaligned(cache->k_codes) || misaligned(cache->k_sz) ||
         misaligned(cache->v_codes) || misaligned(cache->v_sz) || (ws && misaligned(ws)))
         return MINIKV_ERR_ALIGN;
-    const minikv::DecodePlan plan = minikv::decode_plan(B, Hkv, n);
+    const minikv::DecodePlan plan = minikv::decode_plan(B, Hq, Hkv, n, D);
     if (!ws || ws_bytes < minikv::decode_ws_bytes(B, Hq, D, plan)) return MINIKV_ERR_WORKSPACE;
     return status_of(minikv::launch_decode(q, cache->k_codes, cache->k_sz, cache->v_codes, cache->v_sz, B, Hq,
                                            Hkv, n, D, resolve_scale(sm_scale, D), out, ws, plan,

@@ -30,14 +30,18 @@
 // value group on the side.  Softmax runs in the log2 domain, online per
 // 128-token step.
 //
-// Work split: grid (splits, Hkv, B); a workgroup of 4 waves owns a range of
-// `chunk` tokens (a multiple of 512).  Each wave walks the 128-token steps
-// wave, wave + 4, ...; the next step's key loads go out once the current keys
-// are consumed, its value loads once the current values are (no workgroup
-// barrier until the end); the 4 waves then merge by log-sum-exp.  With one
-// split the workgroup writes the bf16 output itself; otherwise partial
-// (m, l, acc) per split go to the workspace and a small second kernel merges
-// the splits.
+// Work split: an item is a (sequence, KV head, token range of `chunk`
+// tokens, a multiple of 128); enough ranges per KV head to give >= 4096 items.
+// The grid holds as many 4-wave workgroups as stay resident, and every wave
+// walks its own items (no workgroup barrier): all 128-token steps of an item in
+// order, the next step's key loads issued once the current keys are consumed
+// and its value loads once the current values are, across item boundaries too.
+// With one range per KV head the wave writes the bf16 output itself; otherwise
+// partial (m, l, acc) per range go to the workspace and a small second kernel
+// merges them.
+#include <algorithm>
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -45,7 +49,6 @@ namespace minikv {
 namespace {
 
 constexpr int kStep = 128;        // tokens per wave step: four 32-token blocks
-constexpr int kSub = 4 * kStep;   // tokens per workgroup step
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kScaleOne = 0x7F7F7F7F;  // E8M0 block scale 2^0 for both MFMA operands
 
@@ -185,32 +188,32 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Work item = (sequence, KV head, range of `chunk` tokens), numbered
+// item = unit * splits + split with unit = b * Hkv + g.  Each wave is
+// independent: it walks items blockIdx.x * 4 + wave, + 4 gridDim.x, ..., all
+// 128-token steps of an item in order, and issues the first loads of its next
+// item while it finishes the current one.
 template <int D, int R>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes, const uint32_t* __restrict__ k_sz,
-    const uint8_t* __restrict__ v_codes, const uint32_t* __restrict__ v_sz, int Hkv, int n, int chunk,
-    float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml, __bf16* __restrict__ out) {
+    const uint8_t* __restrict__ v_codes, const uint32_t* __restrict__ v_sz, int n, int chunk, int splits,
+    int n_items, float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    __bf16* __restrict__ out) {
     constexpr int NG = D / 32;  // 32-channel groups: key K blocks and value scale groups
     constexpr int NT = D / 16;  // 16-channel value tiles
     constexpr int GPL = NG * R / 4 > 1 ? NG * R / 4 : 1;  // value groups per lane in the weight prep
     __shared__ __align__(16) uint8_t s_qa[4][4][R][4][128];   // wave, block, head, piece, K position
     __shared__ __align__(16) uint8_t s_wa[4][R][NG][4][128];  // wave, head, value group, piece, K position
     __shared__ float s_z[4][R][NG];
-    __shared__ float s_red[4][R][D];
-    __shared__ float s_ml[4][R][2];
 
-    const int split = blockIdx.x;
-    const int g = blockIdx.y;
-    const int b = blockIdx.z;
-    const int unit = b * Hkv + g;
-    const int splits = gridDim.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: keeps bases scalar
     const int lane = threadIdx.x % kWave;
     const int col = lane % 16, blk = lane / 16;
     const int myh = blk % R;  // head of this lane's MFMA result rows
     const int G = (n + kGroup - 1) / kGroup;
-    const int t_begin = split * chunk;
-    const int t_end = min(n, t_begin + chunk);
+    const int nwaves = gridDim.x * 4;
+    int item = blockIdx.x * 4 + wave;
+    if (item >= n_items) return;  // wave-uniform; the kernel has no workgroup barrier
 
     // never-written LDS positions must read as zero: key K positions >= D, value piece 3
     {
@@ -221,22 +224,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     }
 
     // Query channels c0, c0 + 2 of this lane sit at key K positions 2 lane,
-    // 2 lane + 1 (lanes >= D/2 idle here).  Pre-scaled to log2 units.
+    // 2 lane + 1 (lanes >= D/2 idle here).
     const bool qlane = lane < D / 2;
     const int c0 = qlane ? 32 * (lane / 16) + 16 * ((lane / 8) % 2) + 4 * (lane % 4) + (lane / 4) % 2 : 0;
-    float qk[R][2];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint16_t* qr = q + ((size_t)(b * Hkv + g) * R + r) * D;
-        qk[r][0] = qlane ? bf16_bits_to_f32(qr[c0]) * scale_log2 : 0.0f;
-        qk[r][1] = qlane ? bf16_bits_to_f32(qr[c0 + 2]) * scale_log2 : 0.0f;
-    }
     // Key B operand: the lane holds code words 2 blk, 2 blk + 1 (K positions
     // 32 blk + nibble) of one token; subtile j (0..7) of a step holds tokens
     // 32 (j/2) + 2 (j%2) + tm0 in its 16 columns, so the lane's two subtiles of
     // a block carry the tokens u, u + 2 that sit side by side in value K order.
     const int tm0 = 4 * (col / 2) + col % 2;
-    const bool kact = blk < NG;
     const uint32_t koff = (uint32_t)(tm0 * (D / 4) + 8 * blk);
     // Value B operand: channel 16 T + col of block blk of the step, 8 bytes.
     const uint32_t voff = (uint32_t)((blk * D + col) * 8);
@@ -249,89 +244,80 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const int ahd = (col / 4) % R, ap = col % 4;
     const int ascale = (127 - 4 * ap) * 0x01010101;
 
-    // Everything one 128-token step needs from HBM, loaded one step ahead.  All
-    // loads are a wave-uniform base plus a 32-bit lane offset.
+    // Everything one 128-token step needs from HBM.  Every load goes through a
+    // buffer resource whose base is the step's first byte and whose size ends
+    // at the last valid byte of the item's token range: lanes past the range
+    // read zeros (codes 0, s = z = 0) with no branch, so the loads of the next
+    // step land straight in the registers the current step has consumed.
     struct Stage {
         uint2 kc[8];
         uint32_t ksz[4][2];
         uint2 vc[NT];
         uint32_t vsz[8][GPL];
     };
-    auto ld32 = [](const void* base, uint32_t off) {
-        return *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(base) + off);
-    };
-    auto ld64 = [](const void* base, uint32_t off) {
-        return *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + off);
+    auto rsrc = [](const void* base, int bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
     };
     auto tok_of = [&](int j) { return 32 * (j / 2) + 2 * (j % 2) + tm0; };  // token of subtile j in the step
     auto kc_off = [&](int j) { return koff + (uint32_t)((32 * (j / 2) + 2 * (j % 2)) * (D / 4)); };
     const uint32_t kszo = (uint32_t)(c0 * 4);
-    const uint32_t vszo = (uint32_t)((tm0 * NG + gbase) * 4);
+    const uint32_t vszo = (uint32_t)((tm0 * NG + (wlane ? gbase : 0)) * 4);
     auto vsz_off = [&](int j, int i) { return vszo + (uint32_t)(((32 * (j / 2) + 2 * (j % 2)) * NG + i) * 4); };
-    auto load_keys = [&](int step, Stage& st) {
-        const int t0 = step * kStep;
-        const int b0 = t0 / kGroup;
-        const uint8_t* kcb = k_codes + ((size_t)unit * n + t0) * (D / 4);
-        const uint32_t* kszb = k_sz + ((size_t)unit * G + b0) * D;
-        if (t0 + kStep <= t_end) {  // wave-uniform: the whole step is in range
+    // position of a step: KV unit, step index, end of the item's token range
+    struct Pos {
+        int unit, step, t_end;
+    };
+    auto load_keys = [&](const Pos& ps, Stage& st) {
+        const int t0 = ps.step * kStep;
+        const int nt = ps.t_end - t0;  // valid tokens from t0
+        const auto rk = rsrc(k_codes + ((size_t)ps.unit * n + t0) * (D / 4), nt * (D / 4));
+        const auto rs = rsrc(k_sz + ((size_t)ps.unit * G + t0 / kGroup) * D, (nt + kGroup - 1) / kGroup * D * 4);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) st.kc[j] = kact ? ld64(kcb, kc_off(j)) : make_uint2(0u, 0u);
-#pragma unroll
-            for (int bk = 0; bk < 4; ++bk) {
-                st.ksz[bk][0] = ld32(kszb, kszo + (uint32_t)(bk * D * 4));
-                st.ksz[bk][1] = ld32(kszb, kszo + (uint32_t)((bk * D + 2) * 4));
-            }
-            return;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bool in = kact && t0 + tok_of(j) < t_end;
-            st.kc[j] = in ? ld64(kcb, kc_off(j)) : make_uint2(0u, 0u);
-        }
+        for (int j = 0; j < 8; ++j)
+            st.kc[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, (int)kc_off(j), 0, 0));
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk) {
-            const bool in = t0 + kGroup * bk < t_end;
-            st.ksz[bk][0] = in ? ld32(kszb, kszo + (uint32_t)(bk * D * 4)) : 0u;
-            st.ksz[bk][1] = in ? ld32(kszb, kszo + (uint32_t)((bk * D + 2) * 4)) : 0u;
+            st.ksz[bk][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(kszo + bk * D * 4), 0, 0);
+            st.ksz[bk][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(kszo + (bk * D + 2) * 4), 0, 0);
         }
     };
-    auto load_values = [&](int step, Stage& st) {
-        const int t0 = step * kStep;
-        const int b0 = t0 / kGroup;
-        const uint8_t* vcb = v_codes + ((size_t)unit * G + b0) * D * 8;
-        const uint32_t* vsb = v_sz + ((size_t)unit * n + t0) * NG;
-        if (t0 + kStep <= t_end) {
+    auto load_values = [&](const Pos& ps, Stage& st) {
+        const int t0 = ps.step * kStep;
+        const int nt = ps.t_end - t0;
+        const auto rv = rsrc(v_codes + ((size_t)ps.unit * G + t0 / kGroup) * D * 8, (nt + kGroup - 1) / kGroup * D * 8);
+        const auto rz = rsrc(v_sz + ((size_t)ps.unit * n + t0) * NG, nt * NG * 4);
 #pragma unroll
-            for (int T = 0; T < NT; ++T) st.vc[T] = ld64(vcb, voff + (uint32_t)(128 * T));
+        for (int T = 0; T < NT; ++T)
+            st.vc[T] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(voff + 128 * T), 0, 0));
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-                for (int i = 0; i < GPL; ++i) st.vsz[j][i] = wlane ? ld32(vsb, vsz_off(j, i)) : 0u;
-            return;
+            for (int i = 0; i < GPL; ++i) st.vsz[j][i] = __builtin_amdgcn_raw_buffer_load_b32(rz, (int)vsz_off(j, i), 0, 0);
+    };
+    // the query of a KV unit: bf16 bits of channels c0, c0 + 2 for each of its R heads
+    auto load_q = [&](int unit, uint32_t (&qb)[R][2]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint16_t* qr = q + ((size_t)unit * R + r) * D;
+            qb[r][0] = qr[c0];
+            qb[r][1] = qr[c0 + 2];
         }
-        const bool vin = t0 + kGroup * blk < t_end;
-#pragma unroll
-        for (int T = 0; T < NT; ++T) st.vc[T] = vin ? ld64(vcb, voff + (uint32_t)(128 * T)) : make_uint2(0u, 0u);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bool in = wlane && t0 + tok_of(j) < t_end;
-#pragma unroll
-            for (int i = 0; i < GPL; ++i) st.vsz[j][i] = in ? ld32(vsb, vsz_off(j, i)) : 0u;  // s = z = 0
-        }
+    };
+    auto pos_of = [&](int it) {  // first step of an item
+        const int t0 = (it % splits) * chunk;
+        return Pos{it / splits, t0 / kStep, min(n, t0 + chunk)};
     };
 
     // online-softmax state of this lane's head (uniform within its 16-lane row)
-    float m_run = -INFINITY, lacc = 0.0f;
+    float qk[R][2];
+    float m_run, lacc;
     float acc[NT], zacc[GPL];
-#pragma unroll
-    for (int T = 0; T < NT; ++T) acc[T] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < GPL; ++i) zacc[i] = 0.0f;
 
-    // One step; the next step's loads (step + 4) go out as soon as this step's
+    // One step; the loads of the next position go out as soon as this step's
     // registers of the same kind are consumed.
-    auto process = [&](int step, Stage& st, bool more) {
-        const int t0 = step * kStep;
+    auto process = [&](const Pos& ps, Stage& st, const Pos& nx) {
+        const int t0 = ps.step * kStep;
+        const int t_end = ps.t_end;
         // ---- keys: fold each block's fp16 scales into the query ----
         float x[4][R][2], zp[4][R];
         uint32_t mxb[4][R];
@@ -387,7 +373,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
                 sc[j] = fmaf((c[0] + c[1]) + (c[2] + c[3]), km, kb);
             }
         }
-        if (more) load_keys(step + 4, st);
+        load_keys(nx, st);
         if (t0 + kStep > t_end) {  // wave-uniform: the step's tail is past the range
 #pragma unroll
             for (int j = 0; j < 8; ++j) sc[j] = t0 + tok_of(j) < t_end ? sc[j] : -INFINITY;
@@ -455,64 +441,66 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
                 acc[T] = fmaf((c[0] + c[1]) + c[2], wmul, acc[T]);
             }
         }
-        if (more) load_values(step + 4, st);
+        load_values(nx, st);
     };
 
-    // each wave walks steps wave, wave + 4, ... of this split
-    {
-        const int step_begin = t_begin / kStep;
-        const int step_end = (t_end + kStep - 1) / kStep;
-        Stage st;
-        int s = step_begin + wave;
-        if (s < step_end) {
-            load_keys(s, st);
-            load_values(s, st);
-        }
-        for (; s < step_end; s += 4) process(s, st, s + 4 < step_end);
-    }
-
-    // ---- this wave's partial: l and the zero-point sums per row, then out = acc + sum p z ----
-    const float lsum = row_fsum(lacc);
-    float zs[GPL];
+    Stage st;
+    Pos ps = pos_of(item);
+    uint32_t qb[R][2];
+    load_q(ps.unit, qb);
+    load_keys(ps, st);
+    load_values(ps, st);
+    while (true) {
+        const int split = item % splits;
 #pragma unroll
-    for (int i = 0; i < GPL; ++i) zs[i] = row_fsum(zacc[i]);
-    if (col == 0) {
-        if (wlane) {
-#pragma unroll
-            for (int i = 0; i < GPL; ++i) s_z[wave][myh][gbase + i] = zs[i];
+        for (int r = 0; r < R; ++r) {
+            qk[r][0] = qlane ? bf16_bits_to_f32(qb[r][0]) * scale_log2 : 0.0f;  // log2 units
+            qk[r][1] = qlane ? bf16_bits_to_f32(qb[r][1]) * scale_log2 : 0.0f;
         }
+        m_run = -INFINITY;
+        lacc = 0.0f;
+#pragma unroll
+        for (int T = 0; T < NT; ++T) acc[T] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < GPL; ++i) zacc[i] = 0.0f;
+        const int next_item = item + nwaves;
+        const Pos first_next = pos_of(next_item);
+        const int step_end = (ps.t_end + kStep - 1) / kStep;
+        for (; ps.step < step_end; ++ps.step) {
+            // next position: the next step, the next item's first step, or (past the
+            // last item) this step again, a harmless reload that keeps loads unconditional
+            const bool last = ps.step + 1 == step_end;
+            const Pos nx = !last ? Pos{ps.unit, ps.step + 1, ps.t_end} : (next_item < n_items ? first_next : ps);
+            load_q(nx.unit, qb);
+            process(ps, st, nx);
+        }
+        // ---- this item's result: row sums of l and of sum p z, out = acc + sum p z ----
+        const float lsum = row_fsum(lacc);
+#pragma unroll
+        for (int i = 0; i < GPL; ++i) {
+            const float zs = row_fsum(zacc[i]);
+            if (col == 0 && wlane) s_z[wave][myh][gbase + i] = zs;
+        }
+        wave_sync_lds();
         if (blk < R) {
-            s_ml[wave][blk][0] = m_run;
-            s_ml[wave][blk][1] = lsum;
-        }
-    }
-    wave_sync_lds();
-    if (blk < R) {
+            const size_t row = (size_t)ps.unit * R + blk;  // query head b * Hq + g * R + blk
 #pragma unroll
-        for (int T = 0; T < NT; ++T) s_red[wave][blk][16 * T + col] = acc[T] + s_z[wave][blk][T / 2];
-    }
-    __syncthreads();
-    // ---- merge the 4 waves (log-sum-exp) into this split's partial ----
-    for (int i = threadIdx.x; i < R * D; i += blockDim.x) {
-        const int r = i / D, d = i % D;
-        const float M = fmaxf(fmaxf(s_ml[0][r][0], s_ml[1][r][0]), fmaxf(s_ml[2][r][0], s_ml[3][r][0]));
-        float x = 0.0f, L = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float f = exp2f(s_ml[w][r][0] - M);  // 0 for a wave that saw no tokens
-            x = fmaf(s_red[w][r][d], f, x);
-            L = fmaf(s_ml[w][r][1], f, L);
+            for (int T = 0; T < NT; ++T) {
+                const float x = acc[T] + s_z[wave][blk][T / 2];
+                if (splits == 1)
+                    out[row * D + 16 * T + col] = (__bf16)(x / lsum);
+                else
+                    ws_acc[(row * splits + split) * D + 16 * T + col] = x;
+            }
+            if (splits > 1 && col == 0) {
+                ws_ml[(row * splits + split) * 2 + 0] = m_run;
+                ws_ml[(row * splits + split) * 2 + 1] = lsum;
+            }
         }
-        if (splits == 1) {  // the workgroup saw every token: normalise here
-            out[((size_t)(b * Hkv + g) * R + r) * D + d] = (__bf16)(x / L);
-            continue;
-        }
-        const size_t o = (((size_t)(b * Hkv + g) * R + r) * splits + split);
-        ws_acc[o * D + d] = x;
-        if (d == 0) {
-            ws_ml[o * 2 + 0] = M;
-            ws_ml[o * 2 + 1] = L;
-        }
+        wave_sync_lds();  // s_z is rewritten by the next item
+        if (next_item >= n_items) break;
+        item = next_item;
+        ps = first_next;
     }
 }
 
@@ -535,15 +523,38 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     out[(size_t)bh * D + d] = (__bf16)(o / L);
 }
 
+// Resident workgroups of a decode instantiation on the current device: the
+// persistent grid is sized to it.  Host-side queries only, cached.
+template <int D, int R>
+int resident_workgroups() {
+    static const int per_cu = [] {
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partial_kernel<D, R>, 256, 0) != hipSuccess || nb < 1)
+            nb = 1;
+        return nb;
+    }();
+    static std::atomic<int> cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int c = cus[dev].load(std::memory_order_relaxed);
+    if (c <= 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) c = 256;
+        cus[dev].store(c, std::memory_order_relaxed);
+    }
+    return per_cu * c;
+}
+
 template <int D, int R>
 hipError_t launch_dr(const void* q, const uint8_t* k_codes, const uint32_t* k_sz, const uint8_t* v_codes,
                      const uint32_t* v_sz, int B, int Hq, int Hkv, int n, float scale_log2, void* out,
                      void* ws, const DecodePlan& plan, hipStream_t stream) {
     float* ws_acc = static_cast<float*>(ws);
     float* ws_ml = ws_acc + (size_t)B * Hq * plan.splits * D;
-    hipLaunchKernelGGL((decode_partial_kernel<D, R>), dim3(plan.splits, Hkv, B), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), k_codes, k_sz, v_codes, v_sz, Hkv, n, plan.chunk,
-                       scale_log2, ws_acc, ws_ml, static_cast<__bf16*>(out));
+    const long items = (long)B * Hkv * plan.splits;
+    const long grid = std::min<long>((items + 3) / 4, resident_workgroups<D, R>());
+    hipLaunchKernelGGL((decode_partial_kernel<D, R>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), k_codes, k_sz, v_codes, v_sz, n, plan.chunk, plan.splits,
+                       (int)items, scale_log2, ws_acc, ws_ml, static_cast<__bf16*>(out));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;  // one split: the partial kernel wrote out
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(B * Hq), dim3(D), 0, stream, ws_acc, ws_ml,
@@ -565,15 +576,16 @@ hipError_t launch_d(const void* q, const uint8_t* k_codes, const uint32_t* k_sz,
 
 }  // namespace
 
-DecodePlan decode_plan(int B, int Hkv, int n_keep) {
+DecodePlan decode_plan(int B, int Hq, int Hkv, int n_keep, int D) {
+    (void)Hq;
+    (void)D;
     const long units = (long)B * Hkv;
-    const int max_splits = (n_keep + kSub - 1) / kSub;
-    long want = (2048 + units - 1) / units;  // aim for >= 8 workgroups per CU
-    int splits = (int)(want < 1 ? 1 : (want > max_splits ? max_splits : want));
-    int chunk = (n_keep + splits - 1) / splits;
-    chunk = (chunk + kSub - 1) / kSub * kSub;
-    splits = (n_keep + chunk - 1) / chunk;
-    return {splits, chunk};
+    const int steps = (n_keep + kStep - 1) / kStep;
+    const long want = (4096 + units - 1) / units;  // aim for >= 4096 work items
+    int splits = (int)(want < 1 ? 1 : (want > steps ? steps : want));
+    const int per = (steps + splits - 1) / splits;
+    splits = (steps + per - 1) / per;
+    return {splits, per * kStep};
 }
 
 size_t decode_ws_bytes(int B, int Hq, int D, const DecodePlan& plan) {

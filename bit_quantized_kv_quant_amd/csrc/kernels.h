@@ -18,9 +18,9 @@ hipError_t launch_select_topk(const float* scores, int B, int Hkv, int T_ctx, in
 // Decode: split plan shared by the workspace-size query and the launcher.
 struct DecodePlan {
     int splits;  // token ranges per (sequence, KV head)
-    int chunk;   // tokens per split (multiple of 512)
+    int chunk;   // tokens per split (multiple of 128)
 };
-DecodePlan decode_plan(int B, int Hkv, int n_keep);
+DecodePlan decode_plan(int B, int Hq, int Hkv, int n_keep, int D);
 size_t decode_ws_bytes(int B, int Hq, int D, const DecodePlan& plan);
 
 hipError_t launch_decode(const void* q, const uint8_t* k_codes, const uint32_t* k_sz,
