@@ -16,6 +16,14 @@ alone while rotating over >= 1 GB of distinct packed caches, so its HBM figure
 is not served from the 256 MB Infinity Cache.  The CPU oracle is timed on a
 bounded sample of the same work (cpu_baseline).
 
+Two multi-layer decode sweeps follow (extra objects in the JSON line): the
+LLaMA2-13B-shaped pyramid cache (40 layers x 40 heads, context 8192, per-layer
+budget 30 % -> 5 %) at a batch that fills about 227 GB of HBM, and the
+Mistral-7B-shaped GQA cache (32 layers, 32 / 8 heads, 6600 kept tokens of a
+44000-token prompt, batch 4).  A decode step there is one query per sequence
+through every layer; kept-token K/V are drawn directly from the workload's
+distributions and packed by the library.
+
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
 
@@ -42,7 +50,52 @@ def parse():
     ap.add_argument("--decode-rotation-gb", type=float, default=1.2)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after the timed region, run one device copy of this size (counter calibration)")
+    ap.add_argument("--pyramid-batch", type=int, default=1024,
+                    help="batch of the 40-layer pyramid decode sweep (1024 fills about 227 GB; 0 skips it)")
+    ap.add_argument("--no-gqa-sweep", action="store_true", help="skip the 32-layer GQA decode sweep")
     return ap.parse_args()
+
+
+def decode_layers(torch, mk, synth, wl, B, budgets, reps=3, chunk=64):
+    """Pack one cache per layer (kept-token K/V drawn directly), then time decode
+    steps through all layers: one query per sequence per step."""
+    dev = torch.device("cuda:0")
+    caches = []
+    for l, n in enumerate(budgets):
+        c = mk.PackedCache.alloc(B, wl.Hkv, n, wl.D, dev)
+        for b0 in range(0, B, chunk):
+            b1 = min(B, b0 + chunk)
+            k, v = synth.make_kept_kv(wl, n, dev, seed=wl.seed * 100000 + l * 1000 + b0, B=b1 - b0)
+            sub = mk.PackedCache(c.k_codes[b0:b1], c.k_sz[b0:b1], c.v_codes[b0:b1], c.v_sz[b0:b1],
+                                 b1 - b0, wl.Hkv, n, wl.D)
+            mk.quant_pack(k, v, out=sub)
+            del k, v
+        caches.append(c)
+    q = synth.make_decode_q(wl, dev, B=B)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(16, max(mk.decode_ws_bytes(B, wl.Hq, wl.Hkv, c.n_keep, wl.D) for c in caches)),
+                     dtype=torch.uint8, device=dev)
+    for c in caches:  # warm-up pass
+        mk.decode_attn(q, c, out=out, ws=ws)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        for c in caches:
+            mk.decode_attn(q, c, out=out, ws=ws)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    cache_bytes = sum(c.nbytes() for c in caches)
+    qo_bytes = 2 * B * wl.Hq * wl.D * 2 * len(caches)
+    gbs = (cache_bytes + qo_bytes) / (ms * 1e-3) / 1e9
+    del caches
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "batch": B, "layers": len(budgets), "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+            "kept_tokens_first_last": [int(budgets[0]), int(budgets[-1])], "packed_GB": cache_bytes / 1e9,
+            "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3), "achieved_GBs": gbs,
+            "hbm_frac": gbs / PEAK_HBM_GBS}
 
 
 class StageTimer:
@@ -263,6 +316,19 @@ def main():
                    "rotation_bytes": n_rot * cache_bytes},
         "output_tokens_per_s": B / (ms_per_step * 1e-3),
     }
+    # ---- multi-layer decode sweeps (the chain's buffers are released first) ----
+    del q, k, v, o, lse, scores, idx, cache, out, ws, qdec
+    torch.cuda.empty_cache()
+    if args.pyramid_batch > 0:
+        pw = synth.WORKLOADS["llama13b_pyramid"]
+        budgets = [mk.pyramid_keep(pw.T, pw.layers, l, *pw.pyramid) for l in range(pw.layers)]
+        res["decode_pyramid"] = decode_layers(torch, mk, synth, pw, args.pyramid_batch, budgets)
+        print(f"# pyramid decode: {json.dumps(res['decode_pyramid'])}", file=sys.stderr, flush=True)
+    if not args.no_gqa_sweep:
+        gw = synth.WORKLOADS["mistral_44k"]
+        budgets = [mk.keep_count(gw.T, gw.budget_pct)] * gw.layers
+        res["decode_gqa"] = decode_layers(torch, mk, synth, gw, gw.B, budgets, reps=20)
+        print(f"# gqa decode: {json.dumps(res['decode_gqa'])}", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)

@@ -504,23 +504,51 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     }
 }
 
-// Merge the splits of one (sequence, query head): log-sum-exp weights, bf16 out.
+// Merge the token ranges of one (sequence, query head): the range maxima and
+// weights 2^(m_s - M) are computed cooperatively and kept in LDS, then every
+// thread (one channel) sums its partials with several loads in flight.
+constexpr int kMaxSplits = 256;
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ ws_acc,
                                                            const float* __restrict__ ws_ml, int splits,
                                                            __bf16* __restrict__ out) {
+    constexpr int NW = D / kWave;
+    __shared__ float s_w[kMaxSplits];
+    __shared__ float s_part[2][NW];
     const int bh = blockIdx.x;
-    const int d = threadIdx.x;
+    const int t = threadIdx.x;
     const float* ml = ws_ml + (size_t)bh * splits * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.0f, o = 0.0f;
-    for (int s = 0; s < splits; ++s) {
+    float m = -INFINITY;
+    for (int s = t; s < splits; s += D) m = fmaxf(m, ml[2 * s]);
+    m = dpp_max<kWave>(m);
+    if (t % kWave == 0) s_part[0][t / kWave] = m;
+    __syncthreads();
+    float M = s_part[0][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_part[0][w]);
+    float l = 0.0f;
+    for (int s = t; s < splits; s += D) {
         const float w = exp2f(ml[2 * s] - M);
-        L = fmaf(ml[2 * s + 1], w, L);
-        o = fmaf(ws_acc[((size_t)bh * splits + s) * D + d], w, o);
+        s_w[s] = w;
+        l = fmaf(ml[2 * s + 1], w, l);
     }
-    out[(size_t)bh * D + d] = (__bf16)(o / L);
+    l = dpp_sum<kWave>(l);
+    if (t % kWave == 0) s_part[1][t / kWave] = l;
+    __syncthreads();
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) L += s_part[1][w];
+    const float* a = ws_acc + (size_t)bh * splits * D + t;
+    float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
+    int s = 0;
+    for (; s + 4 <= splits; s += 4) {
+        o0 = fmaf(a[(size_t)s * D], s_w[s], o0);
+        o1 = fmaf(a[(size_t)(s + 1) * D], s_w[s + 1], o1);
+        o2 = fmaf(a[(size_t)(s + 2) * D], s_w[s + 2], o2);
+        o3 = fmaf(a[(size_t)(s + 3) * D], s_w[s + 3], o3);
+    }
+    for (; s < splits; ++s) o0 = fmaf(a[(size_t)s * D], s_w[s], o0);
+    out[(size_t)bh * D + t] = (__bf16)(((o0 + o1) + (o2 + o3)) / L);
 }
 
 // Resident workgroups of a decode instantiation on the current device: the
@@ -583,6 +611,7 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int n_keep, int D) {
     const int steps = (n_keep + kStep - 1) / kStep;
     const long want = (4096 + units - 1) / units;  // aim for >= 4096 work items
     int splits = (int)(want < 1 ? 1 : (want > steps ? steps : want));
+    if (splits > kMaxSplits) splits = kMaxSplits;
     const int per = (steps + splits - 1) / splits;
     splits = (steps + per - 1) / per;
     return {splits, per * kStep};
