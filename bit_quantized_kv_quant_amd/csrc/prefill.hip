@@ -107,22 +107,27 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     const int ntiles = (kv_end + kBN - 1) / kBN;
 
     // K tiles are register-staged (global -> VGPR -> LDS, XOR-swizzled 16-byte
-    // chunks).  Rows past the end are clamped to the last row: those keys are
-    // always masked.  (A global_load_lds path would skip the VGPR hop, but the
-    // compiler then waits for every outstanding load before any LDS read.)
+    // chunks).  Loads go through a buffer resource based at the tile's first
+    // row and sized to the rows that exist: rows past T read as zeros, and such
+    // keys sit only in diagonal tiles, where they are masked.  (A
+    // global_load_lds path would skip the VGPR hop, but the compiler then waits
+    // for every outstanding load before any LDS read.)
     u32x4 pk[LOADS];
     // Row and chunk of the first 16-byte chunk this thread stages; its later
-    // chunks are kRowStep rows further down.  Signed row arithmetic throughout.
+    // chunks are kRowStep rows further down.
     const int row0 = (int)(threadIdx.x / CH);
     const int col0 = 8 * (int)(threadIdx.x % CH);
     constexpr int kRowStep = NT / CH;
-    auto tile_row = [&](int n0, int i) -> int {  // clamped source row of chunk i
-        return min(n0 + row0 + kRowStep * i, T_ctx - 1);
+    const int goff0 = (row0 * D + col0) * 2;  // byte offset of chunk 0 inside a tile
+    auto tile_rsrc = [&](const uint16_t* base, int n0) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + (kvbase + (size_t)n0) * D), 0,
+                                                 (T_ctx - n0) * D * 2, 0x00020000);
     };
     auto load_k = [&](int n0) {
+        const auto rk = tile_rsrc(k, n0);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i)
-            pk[i] = *reinterpret_cast<const u32x4*>(k + (kvbase + (size_t)tile_row(n0, i)) * D + col0);
+            pk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, goff0 + i * kRowStep * D * 2, 0, 0));
     };
     auto store_k = [&](int buf) {
 #pragma unroll
@@ -135,11 +140,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     u32x4 pv[kWithO ? LOADS : 1];
     auto load_v = [&](int n0) {
         if constexpr (kWithO) {
+            const auto rv = tile_rsrc(v, n0);
 #pragma unroll
             for (int i = 0; i < LOADS; ++i)
-                pv[i] = *reinterpret_cast<const u32x4*>(v + (kvbase + (size_t)tile_row(n0, i)) * D + col0);
+                pv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, goff0 + i * kRowStep * D * 2, 0, 0));
         }
     };
+
     auto store_v = [&](int buf) {
         if constexpr (kWithO) {
 #pragma unroll
