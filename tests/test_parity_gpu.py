@@ -316,3 +316,80 @@ def test_repeat_runs_bit_identical(dev):
                     out.clone()])
     for a, b in zip(*res):
         assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# full-size configurations, checked on sampled outputs
+# ---------------------------------------------------------------------------
+
+def _slice_cache(cache, bsel):
+    """The packed cache of the sequences bsel (device copies)."""
+    ix = torch.as_tensor(bsel, device=cache.k_codes.device)
+    return mk.PackedCache(cache.k_codes[ix].contiguous(), cache.k_sz[ix].contiguous(),
+                          cache.v_codes[ix].contiguous(), cache.v_sz[ix].contiguous(),
+                          len(bsel), cache.Hkv, cache.n_keep, cache.D)
+
+
+@pytest.mark.parametrize("B", [64, 256])
+@pytest.mark.parametrize("layer", [0, 39])
+def test_decode_pyramid_layer_sampled(dev, B, layer):
+    """LLaMA2-13B-shaped pyramid layer (40 heads, context 8192, budget 30 % -> 5 %): the
+    whole batch decoded (several work items per wave; at B = 64 each KV head is split
+    into token ranges), sampled sequences against the oracle."""
+    wl = synth.WORKLOADS["llama13b_pyramid"]
+    n = oracle.pyramid_keep(wl.T, wl.layers, layer, *wl.pyramid)
+    say("pyramid decode layer", layer, "n", n, "B", B)
+    cache = mk.PackedCache.alloc(B, wl.Hkv, n, wl.D, dev)
+    for b0 in range(0, B, 64):
+        b1 = min(B, b0 + 64)
+        k, v = synth.make_kept_kv(wl, n, dev, seed=wl.seed * 100000 + layer * 1000 + b0, B=b1 - b0)
+        sub = mk.PackedCache(cache.k_codes[b0:b1], cache.k_sz[b0:b1], cache.v_codes[b0:b1], cache.v_sz[b0:b1],
+                             b1 - b0, wl.Hkv, n, wl.D)
+        mk.quant_pack(k, v, out=sub)
+        del k, v
+    q = synth.make_decode_q(wl, dev, B=B)
+    out = mk.decode_attn(q, cache)
+    torch.cuda.synchronize()
+    bsel = sorted({0, 1, B // 2, B - 1})
+    ref = oracle.decode_ref(to_np(q)[bsel], packed_to_np(_slice_cache(cache, bsel)))
+    assert_attn_close(to_np(out)[bsel], ref, "pyramid decode")
+
+
+def test_gqa_44k_chain_sampled(dev):
+    """Mistral-7B-shaped long context (GQA 32 / 8, prompt 44000, batch 4, 15 % budget):
+    the whole chain at full size; o / lse on sampled rows and window scores for the
+    first KV heads of sequence 0, selection exact on the GPU's scores, packing
+    bit-exact, decode of every head against the oracle."""
+    wl = synth.WORKLOADS["mistral_44k"]
+    say("gqa 44k: prefill")
+    q, k, v, _ = synth.make_qkv(wl, dev)
+    o, lse, sc = mk.prefill_attn_scores(q, k, v, wl.window)
+    torch.cuda.synchronize()
+    hq = slice(0, 8)   # query heads 0..7 = KV heads 0, 1
+    hk = slice(0, 2)
+    qb = to_np(q[0:1, hq])
+    kb = to_np(k[0:1, hk])
+    vb = to_np(v[0:1, hk])
+    rows = np.array([0, 1, 127, 128, 4095, 22000, 43967, 43968, 43999])
+    o_ref, lse_ref = oracle.prefill_ref(qb, kb, vb, rows=rows)
+    assert_attn_close(to_np(o[0:1, hq])[:, :, rows], o_ref, "gqa prefill o")
+    assert np.abs(to_np(lse[0:1, hq])[:, :, rows] - lse_ref).max() < 1e-4
+    say("gqa 44k: window scores")
+    sc_ref = oracle.window_scores_ref(qb, kb, wl.window)
+    sc_np = to_np(sc)
+    rel = np.abs(sc_np[0:1, hk] - sc_ref) / np.maximum(sc_ref, 1e-6)
+    assert rel.max() < 1e-4
+    say("gqa 44k: select / pack / decode")
+    n_keep = oracle.keep_count(wl.T, wl.budget_pct)
+    nh, nr = oracle.split_heavy_recent(n_keep)
+    idx = mk.select_topk(sc, nh, nr)
+    cache = mk.quant_pack(k, v, idx)
+    qdec = synth.make_decode_q(wl, dev)
+    out = mk.decode_attn(qdec, cache)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    assert np.array_equal(idx_np, oracle.select_ref(sc_np, nh, nr))
+    del o, q
+    got = packed_to_np(cache)
+    assert_packed_equal(got, oracle.quant_pack_ref(to_np(k), to_np(v), idx_np))
+    assert_attn_close(to_np(out), oracle.decode_ref(to_np(qdec), got), "gqa decode")
