@@ -7,8 +7,9 @@
 //   s = fp16(fl32(max - min) / 3), z = fp16(min),
 //   code = s == 0 ? 0 : clamp(rint(fl32(x - z) / s), 0, 3)
 // The file is compiled with -ffp-contract=off so no multiply-add is fused and
-// the divides stay correctly rounded; the codes then match a plain IEEE
-// evaluation bit for bit.
+// the divide by 3 stays correctly rounded; the codes come from exact threshold
+// tests (code_of) and match a plain IEEE evaluation of the rule bit for bit.
+// Inputs are finite (-fno-honor-nans: min / max need no NaN handling).
 //
 // HBM-bound gather: each kept row is read once (coalesced 4-byte lane loads of
 // two channels), each packed byte written once (key codes: dword stores
@@ -36,7 +37,8 @@ template <> __device__ __forceinline__ Pair load_pair<uint16_t>(const uint16_t* 
 
 struct GroupParams {
     float s, z;
-    uint32_t word;  // fp16 s in bits 0..15, fp16 z in bits 16..31
+    uint32_t word;     // fp16 s in bits 0..15, fp16 z in bits 16..31
+    float e1, e2, e3;  // decision thresholds of code_of (infinite when s == 0)
 };
 
 __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
@@ -44,15 +46,26 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
     float s32 = rng / 3.0f;
     uint32_t sb = f32_to_half_bits_rn(s32);
     uint32_t zb = f32_to_half_bits_rn(mn);
-    return {half_bits_to_f32(sb), half_bits_to_f32(zb), sb | (zb << 16)};
+    const float s = half_bits_to_f32(sb);
+    const bool zero = s == 0.0f;
+    return {s, half_bits_to_f32(zb), sb | (zb << 16),
+            zero ? INFINITY : s * 0x1p-25f, zero ? INFINITY : -s * 0x1p-24f, zero ? INFINITY : s * 0x1p-23f};
 }
 
+// code = s == 0 ? 0 : clamp(rint(u), 0, 3) with u = fl32(d / s), d = fl32(x - z), decided
+// without dividing.  Round-half-even is monotone, so
+//   rint(u) >= 1  <=>  u > 0.5  <=>  d / s > 0.5 + 2^-25   (the rounding midpoint above 0.5 ties to 0.5)
+//   rint(u) >= 2  <=>  u >= 1.5 <=>  d / s >= 1.5 - 2^-24  (the midpoint below 1.5 ties to 1.5)
+//   rint(u) >= 3  <=>  u > 2.5  <=>  d / s > 2.5 + 2^-23
+// and, with s > 0, d / s > c + t  <=>  d - c s > t s.  c s is exact (s is an fp16 value, c in
+// {0.5, 1.5, 2.5}); fma(-c, s, d) rounds d - c s once, and wherever d is within [c s / 2, 2 c s] that
+// difference is exact (Sterbenz), so the comparison with the exact t s is exact; outside that range
+// |d - c s| >= c s / 2 dwarfs both the rounding and t s, so the sign decides alone.  With s == 0 all
+// thresholds are infinite and the code is 0.
 __device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
-    if (p.s == 0.0f) return 0u;
-    float u = (x - p.z) / p.s;
-    float r = __builtin_rintf(u);
-    r = fminf(fmaxf(r, 0.0f), 3.0f);
-    return (uint32_t)r;
+    const float d = x - p.z;
+    return (uint32_t)(fmaf(-0.5f, p.s, d) > p.e1) + (uint32_t)(fmaf(-1.5f, p.s, d) >= p.e2) +
+           (uint32_t)(fmaf(-2.5f, p.s, d) > p.e3);
 }
 
 // Keys: one wave per (group of 32 kept tokens, KV head, sequence).
