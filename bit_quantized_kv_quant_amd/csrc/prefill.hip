@@ -10,16 +10,16 @@
 // probabilities without storing any T x T matrix.
 //
 // gfx950 design: a workgroup of 8 waves owns 256 query rows (32 per wave) and
-// streams 64-key tiles of K and V through two LDS stages (XOR-swizzled 16-byte
-// chunks, register-prefetched one tile ahead for V and two for K; one barrier
-// per tile).  Workgroups are ordered XCD-aware so the K/V prefix a head's query
+// streams 64-key tiles of K and V through two LDS stages (register-prefetched
+// one tile ahead for V and two for K; one barrier per tile).  Workgroups are ordered XCD-aware so the K/V prefix a head's query
 // blocks share stays in one L2.  Each wave software-pipelines its tiles: the
 // QK^T MFMAs of tile t+1 are issued while the softmax of tile t runs.  Each wave computes S^T = K Q^T with
 // bf16 MFMA 32x32x16, so an accumulator column is one query: a lane owns the
 // softmax state (running max, partial sum) of its query, and the row max needs
 // one permlane32 swap.  P^T is already in the B-operand layout of the second
-// product O^T = V^T P^T; the V^T operand comes straight from the row-major V
-// tile with ds_read_b64_tr_b16 (LDS transpose read).  The key order inside a
+// product O^T = V^T P^T.  V is transposed on its way into LDS (each thread
+// packs the fp16 values of two adjacent keys into one dword), so every V^T
+// operand is a single 16-byte LDS read.  The key order inside a
 // 32-key block is permuted (phys) so that accumulator register v of a lane is
 // key 16*half + v, which makes both operand layouts line up without shuffles.
 // Causal: tiles above the diagonal are never loaded; only tiles that cross it
@@ -44,16 +44,26 @@ constexpr float kLn2 = 0.6931471805599453f;
 // logical accumulator row r of a 32-key block -> physical key within the block
 __device__ __forceinline__ int phys_key(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
 
-// XOR swizzles of the 16-byte chunk index inside a 256-byte (D = 128) row:
-// K rows are read 32 rows x one chunk at a time, V rows 4 rows x 4 chunks.
+// inverse of phys_key: LDS row (lane order) of key r of a 32-key block
+__device__ __forceinline__ int key_lane(int r) { return (r & 3) | (((r >> 4) & 1) << 2) | (((r >> 2) & 3) << 3); }
+
+// Staged K tile: the keys of each 32-key block are stored in the order the
+// lanes read them (row key_lane(r) holds key r), with rows padded by 16 bytes,
+// so a K-operand read (32 consecutive rows, one 16-byte chunk) and a staging
+// write (one row, all chunks) both touch distinct banks per 16 lanes, and every
+// operand address is one lane constant plus an immediate.
 template <int D>
-__device__ __forceinline__ int swz_k(int r) {
-    return ((r & 7) | (((r >> 4) & 1) << 3)) & (D / 8 - 1);
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int r) {
-    return (4 * (r & 3)) & (D / 8 - 1);
-}
+constexpr int kKStride = D + 8;  // elements per staged K row
+
+// Staged V^T tile.  Element (key, d) with key = 32 bk + 16 half + 8 s + i and
+// d = 8 c + e, c = 8 c_hi + c_lo, sits in line
+//   ((bk * 2 + s) * (D / 64) + c_hi) * 8 + e
+// at byte 16 (c_lo + 8 half) + 2 i.  Lines are padded from 256 to 288 bytes, so
+// the 64 lanes of a transposed-store dword write (fixed e, varying c_lo, half
+// and key pair) and every 16 lanes of a PV operand read (16 consecutive rows d,
+// one chunk) each touch distinct LDS banks; both addresses are one lane
+// constant plus an immediate.
+constexpr int kVtLine = 288;
 
 template <int D, bool kWithO, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
@@ -65,10 +75,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     constexpr int KS = D / 16;              // MFMA k-steps over the head dim
     constexpr int DB = D / 32;              // 32-wide output blocks over the head dim
     constexpr int LOADS = kBN * CH / NT;    // V chunks per thread per tile
-    constexpr int TILE = kBN * D;           // elements of one staged tile
+    constexpr int KST = kKStride<D>;
+    constexpr int TILE = kBN * KST;         // elements of one staged K tile
+    constexpr int CH2 = D / 64;             // 64-wide halves of the head dim
+    constexpr int VT_BYTES = 32 * CH2 * kVtLine;  // one staged V^T tile (padded lines)
+    static_assert(!kWithO || WAVES == 8, "the V^T staging map assumes 8 waves");
     // two LDS stages: tile t is read from one while tile t+1 is written to the other
     __shared__ __attribute__((aligned(16))) uint16_t sK[2 * TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[kWithO ? 2 * TILE : 8];
+    __shared__ __attribute__((aligned(16))) char sV[kWithO ? 2 * VT_BYTES : 16];
 
     // XCD-aware order: workgroup L is dispatched to XCD L % 8.  Work item W =
     // (L % 8) * per + L / 8 gives each XCD a contiguous run of (sequence, head)
@@ -133,32 +147,44 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int r = row0 + kRowStep * i, c = col0 / 8;
-            *reinterpret_cast<u32x4*>(sK + buf * TILE + r * D + 8 * (c ^ swz_k<D>(r))) = pk[i];
+            *reinterpret_cast<u32x4*>(sK + buf * TILE + (32 * (r >> 5) + key_lane(r & 31)) * KST + 8 * c) = pk[i];
         }
     };
-    // V tiles are register-staged so they can be converted to fp16 on the way in.
-    u32x4 pv[kWithO ? LOADS : 1];
+    // V tiles are register-staged, converted to fp16 and stored transposed
+    // (V^T, see kVtLine): thread (bk, s, c_hi from the wave; c_lo, dw, half from
+    // the lane) loads the 16-byte chunk c = 8 c_hi + c_lo of keys 2j and 2j+1,
+    // j = 16 bk + 8 half + 4 s + dw, and writes the eight fp16 pairs
+    // (V[2j][8c+e], V[2j+1][8c+e]) as dwords of V^T rows 8c+e.
+    const int vw = wave;
+    const bool v_active = vw < 4 * CH2;  // D = 64 needs half of the waves
+    const int v_chi = vw % CH2, v_s = (vw / CH2) & 1, v_bk = (vw / CH2 / 2) & 1;
+    const int v_clo = lane & 7, v_dw = (lane >> 3) & 3, v_half = lane >> 5;
+    const int v_j = 16 * v_bk + 8 * v_half + 4 * v_s + v_dw;
+    const int goffv = (2 * v_j * D + 8 * (8 * v_chi + v_clo)) * 2;
+    const int woffv = kVtLine * 8 * ((v_bk * 2 + v_s) * CH2 + v_chi) + 16 * (v_clo + 8 * v_half) + 4 * v_dw;
+    u32x4 pv[kWithO ? 2 : 1];
     auto load_v = [&](int n0) {
         if constexpr (kWithO) {
             const auto rv = tile_rsrc(v, n0);
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i)
-                pv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, goff0 + i * kRowStep * D * 2, 0, 0));
+            if (v_active) {
+                pv[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, goffv, 0, 0));
+                pv[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, goffv + 2 * D, 0, 0));
+            }
         }
     };
 
     auto store_v = [&](int buf) {
         if constexpr (kWithO) {
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                const int r = row0 + kRowStep * i, c = col0 / 8;
-                f16x8 hv;
+            if (v_active) {
+                char* dst = sV + buf * VT_BYTES + woffv;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    hv[2 * w] = (_Float16)__uint_as_float(pv[i][w] << 16);
-                    hv[2 * w + 1] = (_Float16)__uint_as_float(pv[i][w] & 0xFFFF0000u);
+                    const f16x2 lo = {(_Float16)__uint_as_float(pv[0][w] << 16), (_Float16)__uint_as_float(pv[1][w] << 16)};
+                    const f16x2 hi = {(_Float16)__uint_as_float(pv[0][w] & 0xFFFF0000u),
+                                      (_Float16)__uint_as_float(pv[1][w] & 0xFFFF0000u)};
+                    *reinterpret_cast<f16x2*>(dst + kVtLine * (2 * w)) = lo;
+                    *reinterpret_cast<f16x2*>(dst + kVtLine * (2 * w + 1)) = hi;
                 }
-                *reinterpret_cast<f16x8*>(sV + buf * TILE + r * D + 8 * (c ^ swz_v<D>(r))) = hv;
             }
         }
     };
@@ -173,37 +199,33 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
 #pragma unroll
     for (int d = 0; d < (kWithO ? DB : 1); ++d) oacc[d] = f32x16{};
 
-    // Per-lane LDS offsets (elements).  K operand of k-step kk, key block bk:
-    // koff[kk] + 32 bk D.  V^T operand of head-dim block d, key block bk, half
-    // s, rows +0 / +4: voff[d] + (32 bk + 8 s + 4 hi) D.  The swizzle terms are
-    // lane constants, so only these few offsets live in registers.
-    const int krow = phys_key(lane & 31);
-    int koff[KS];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) koff[kk] = krow * D + 8 * ((2 * kk + half) ^ swz_k<D>(krow));
-    const int grp = lane >> 4;        // 16-lane group of the transpose read
-    const int tj = (lane & 15) >> 2;  // row inside the 4-row transpose block
-    const int tc = lane & 3;          // 4-element column chunk
-    int voff[DB];
-#pragma unroll
-    for (int d = 0; d < DB; ++d)
-        voff[d] = (16 * (grp >> 1) + tj) * D + 8 * (4 * (d ^ (tj & (DB - 1))) + 2 * (grp & 1) + (tc >> 1)) +
-                  4 * (tc & 1);
+    // Per-lane LDS offset (elements) of the K operand: k-step kk of key block
+    // bk is at koff + 16 kk + 32 bk KST.
+    const int koff = (lane & 31) * KST + 8 * half;
+    // V^T operand of head-dim block d, key block bk, key half s: the 16-byte
+    // chunk (row 32 d + lane % 32, keys 32 bk + 16 half + 8 s + 0..7), at byte
+    // voff + vt_imm(d, bk, s).
+    const int voff = kVtLine * (lane & 7) + 16 * ((lane >> 3) & 3) + 128 * half;
 
-    // S^T = K Q^T of the tile in stage `buf`, one 32-key block at a time; a
-    // block's K operands are all requested before its MFMA chain.
+    // S^T = K Q^T of the tile in stage `buf`, one 32-key block at a time; the
+    // K operands are requested four k-steps at a time, each group before the
+    // MFMAs that use it (fewer live registers while the softmax runs).
     auto qk = [&](int buf, f32x16 (&sacc)[2]) {
-        const uint16_t* tk = sK + buf * TILE;
+        const uint16_t* tk = sK + buf * TILE + koff;
+        constexpr int G = KS < 4 ? KS : 4;
 #pragma unroll
         for (int bk = 0; bk < 2; ++bk) {
-            bf16x8 a[KS];
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk)
-                a[kk] = *reinterpret_cast<const bf16x8*>(tk + koff[kk] + 32 * bk * D);
             sacc[bk] = f32x16{};
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk)
-                sacc[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], qreg[kk], sacc[bk], 0, 0, 0);
+            for (int k0 = 0; k0 < KS; k0 += G) {
+                bf16x8 a[G];
+#pragma unroll
+                for (int kk = 0; kk < G; ++kk)
+                    a[kk] = *reinterpret_cast<const bf16x8*>(tk + 16 * (k0 + kk) + 32 * bk * KST);
+#pragma unroll
+                for (int kk = 0; kk < G; ++kk)
+                    sacc[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], qreg[k0 + kk], sacc[bk], 0, 0, 0);
+            }
         }
     };
     // Online softmax of one tile: returns the fp16 probabilities (PV operand)
@@ -243,21 +265,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     // O^T += V^T P^T, one 32-wide block of the head dim at a time; the next
     // block's V^T operands are requested before this block's MFMAs.
     auto pv_mma = [&](int buf, const f16x8 (&pb)[2][2]) {
-        const _Float16* tv = reinterpret_cast<const _Float16*>(sV + buf * TILE);
+        const char* tv = sV + buf * VT_BYTES + voff;
         auto read_v = [&](int d, f16x8 (&av)[2][2]) {
 #pragma unroll
-            for (int bk = 0; bk < 2; ++bk) {
+            for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const _Float16* p0 = tv + voff[d] + (32 * bk + 8 * s) * D;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4*)(p0));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4*)(p0 + 4 * D));
-                    const i16x4 both[2] = {lo, hi};
-                    __builtin_memcpy(&av[bk][s], both, 16);
-                }
-            }
+                for (int s = 0; s < 2; ++s)
+                    av[bk][s] = *reinterpret_cast<const f16x8*>(
+                        tv + kVtLine * 8 * ((bk * 2 + s) * CH2 + (d >> 1)) + 64 * (d & 1));
         };
         f16x8 va[2][2][2];
         read_v(0, va[0]);
