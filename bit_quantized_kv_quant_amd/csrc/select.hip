@@ -9,8 +9,9 @@
 // One 1024-thread workgroup per (sequence, KV head) row.  Each thread holds a
 // contiguous run of candidate scores in registers as order-preserving uint32
 // keys.  An MSB-first radix select (4 passes of 8 bits, per-wave LDS
-// histograms) finds the threshold key and how many threshold-equal keys to
-// take; two block scans then compact the kept positions in ascending order.
+// histograms, the threshold digit found by one wave's prefix sum) finds the
+// threshold key and how many threshold-equal keys to take; two block scans
+// then compact the kept positions in ascending order.
 // Every decision is an integer comparison of fp32 bit patterns, so the result
 // equals a sort of the same fp32 scores.
 #include "common.h"
@@ -108,16 +109,32 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(const float* __re
                 s_hist[tid] = c;
             }
             __syncthreads();
-            if (tid == 0) {
-                uint32_t cum = 0;
-                for (int d = 255; d >= 0; --d) {
-                    const uint32_t c = s_hist[d];
-                    if (cum + c >= krem) {
-                        s_prefix = prefix | ((uint32_t)d << shift);
-                        s_krem = krem - cum;
-                        break;
+            if (tid < kWave) {
+                // Threshold digit: the bucket d (counting down from 255) whose
+                // count takes the running total from below krem to >= krem.
+                // Lane l owns buckets 255 - 4l - j, j = 0..3; a wave prefix
+                // sum over lanes gives each bucket the count above it.
+                uint32_t c[4], incl[4], run = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    c[j] = s_hist[255 - 4 * tid - j];
+                    run += c[j];
+                    incl[j] = run;
+                }
+                uint32_t scan = run;
+#pragma unroll
+                for (int o = 1; o < kWave; o <<= 1) {
+                    const uint32_t y = (uint32_t)__shfl_up((int)scan, o, kWave);
+                    if (tid >= o) scan += y;
+                }
+                const uint32_t above_lane = scan - run;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t above = above_lane + incl[j] - c[j];
+                    if (above < krem && krem <= above + c[j]) {  // exactly one bucket
+                        s_prefix = prefix | ((uint32_t)(255 - 4 * tid - j) << shift);
+                        s_krem = krem - above;
                     }
-                    cum += c;
                 }
             }
             __syncthreads();

@@ -7,11 +7,13 @@
 // i.e. the softmax probability mass key j receives from the W observation rows,
 // recomputed from the logits and pass 1's per-row lse, never stored as a matrix.
 //
-// gfx950 design: a wave owns 32 keys and holds them as the B operand of
-// S = Q_window K^T (bf16 MFMA 32x32x16), so an accumulator column is one key:
+// gfx950 design: a wave walks a run of blocks of 32 keys, each held as the B operand
+// of S = Q_window K^T (bf16 MFMA 32x32x16), so an accumulator column is one key:
 // the sum over window rows is a per-lane sum plus one permlane32 swap.  K is
-// read from HBM once; the window queries (W x D per head) and their lse come
-// from L2.  Summation order is fixed, so the scores are deterministic.
+// read from HBM once, the next block's K loaded while the current one is
+// reduced; for one query head and a window of up to 32 rows the Q operand and
+// the row lse stay in registers, otherwise they come from L2 per key block.
+// Summation order is fixed, so the scores are deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,12 +22,65 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// K^T operand of key block kt0: lane holds k[kt0 + lane % 32][16 kk + 8 half + 0..7]
+// (rows past T read as zeros through the buffer resource).
 template <int D>
-__global__ __launch_bounds__(256) void window_scores_kernel(const uint16_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ k,
-                                                            const float* __restrict__ lse, int T_ctx, int Hq,
-                                                            int Hkv, int W, float scale_log2,
-                                                            float* __restrict__ scores) {
+__device__ __forceinline__ void load_kblock(__amdgpu_buffer_rsrc_t rk, int kt0, int lane, bf16x8 (&kreg)[D / 16]) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        kreg[kk] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, ((kt0 + (lane & 31)) * D + 16 * kk + 8 * (lane >> 5)) * 2, 0, 0));
+}
+
+// Scores of key block kt0 against the window rows of one query head, given the
+// Q operand of row block rb (qa) and the lane's 16 row log-sum-exps (log2
+// domain, +inf for rows past the window).
+template <int D>
+__device__ __forceinline__ float block_mass(const bf16x8 (&qa)[D / 16], const bf16x8 (&kreg)[D / 16], const float (&l2)[16],
+                                            float scale_log2, int row0, int kt0, int lane) {
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kreg[kk], sacc, 0, 0, 0);
+    const int half = lane >> 5;
+    const int j = kt0 + (lane & 31);
+    float acc = 0.0f;
+    if (kt0 + 31 <= row0) {  // every window row of the block sees every key of the block
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc += exp2f(fmaf(sacc[e], scale_log2, -l2[e]));
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int i = row0 + 8 * (e >> 2) + 4 * half + (e & 3);
+            if (j <= i) acc += exp2f(fmaf(sacc[e], scale_log2, -l2[e]));
+        }
+    }
+    return acc;
+}
+
+template <int D>
+__device__ __forceinline__ void load_qblock(const uint16_t* __restrict__ q, const float* __restrict__ lse, size_t qbase,
+                                            int w0, int W, int rb, int lane, bf16x8 (&qa)[D / 16], float (&l2)[16]) {
+    const int half = lane >> 5;
+    const int r = 32 * rb + (lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        qa[kk] = r < W ? *reinterpret_cast<const bf16x8*>(q + (qbase + w0 + r) * D + 16 * kk + 8 * half) : bf16x8{};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int m = 32 * rb + 8 * (e >> 2) + 4 * half + (e & 3);
+        l2[e] = m < W ? lse[qbase + w0 + m] * kLog2e : INFINITY;
+    }
+}
+
+// grid (ceil(T / (128 nbw)), Hkv, B), 4 waves; wave w owns the nbw key blocks
+// from (blockIdx.x * 4 + w) * nbw (nbw even).  kRes: one query head per KV
+// head and a window of at most 32 rows (Q operand and row lse in registers).
+template <int D, bool kRes>
+__global__ __launch_bounds__(256, 3) void window_scores_kernel(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ k,
+                                                               const float* __restrict__ lse, int T_ctx, int Hq,
+                                                               int Hkv, int W, int nbw, float scale_log2,
+                                                               float* __restrict__ scores) {
     constexpr int KS = D / 16;
     const int g = blockIdx.y;
     const int b = blockIdx.z;
@@ -33,59 +88,77 @@ __global__ __launch_bounds__(256) void window_scores_kernel(const uint16_t* __re
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int half = lane >> 5;
-    const int kt0 = (blockIdx.x * 4 + wave) * 32;
-    if (kt0 >= T_ctx) return;
-    const int j = kt0 + (lane & 31);
+    const int kb0 = (blockIdx.x * 4 + wave) * nbw;
+    if (kb0 * 32 >= T_ctx) return;
+    const int nb = min(nbw, (T_ctx - kb0 * 32 + 31) / 32);  // key blocks of this wave
     const size_t kvbase = ((size_t)b * Hkv + g) * T_ctx;
     const int w0 = T_ctx - W;  // first window row
-
-    // K^T operand: lane holds k[j][16 kk + 8 half + 0..7]
-    bf16x8 kreg[KS];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-        kreg[kk] = (j < T_ctx) ? *reinterpret_cast<const bf16x8*>(k + (kvbase + j) * D + 16 * kk + 8 * half)
-                               : bf16x8{};
-
-    float acc = 0.0f;
     const int nrb = (W + 31) / 32;
-    for (int r = 0; r < R; ++r) {
-        const int h = g * R + r;
-        const size_t qbase = ((size_t)b * Hq + h) * T_ctx;
-        for (int rb = 0; rb < nrb; ++rb) {
-            // rows of this block whose last key is below kt0 contribute nothing
-            const int row0 = w0 + 32 * rb;
-            if (row0 + 31 < kt0) continue;
-            const int qrow = row0 + (lane & 31);
-            const bool qvalid = 32 * rb + (lane & 31) < W;
-            f32x16 sacc = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const bf16x8 a = qvalid ? *reinterpret_cast<const bf16x8*>(q + (qbase + qrow) * D + 16 * kk + 8 * half)
-                                        : bf16x8{};
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[kk], sacc, 0, 0, 0);
-            }
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = 8 * (e >> 2) + 4 * half + (e & 3);  // accumulator row = window row in block
-                const int i = row0 + m;
-                if (32 * rb + m < W && j <= i) {
-                    const float l2 = lse[qbase + i] * kLog2e;
-                    acc += exp2f(fmaf(sacc[e], scale_log2, -l2));
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k + kvbase * D), 0, T_ctx * D * 2, 0x00020000);
+    auto emit = [&](int i, float a) {  // the block's per-key sums over the two lane halves
+        a += swap_halves(a);
+        const int j = (kb0 + i) * 32 + (lane & 31);
+        if (half == 0 && j < T_ctx) scores[kvbase + j] = a;
+    };
+
+    bf16x8 ka[KS], kb[KS];
+    load_kblock<D>(rk, kb0 * 32, lane, ka);
+    if constexpr (kRes) {
+        // One query head, one row block: the Q operand and the row lse stay in
+        // registers; K blocks stream through two register sets.
+        bf16x8 qa[KS];
+        float l2[16];
+        load_qblock<D>(q, lse, ((size_t)b * Hq + g) * T_ctx, w0, W, 0, lane, qa, l2);
+        for (int i = 0; i < nb; i += 2) {
+            if (i + 1 < nb) load_kblock<D>(rk, (kb0 + i + 1) * 32, lane, kb);
+            emit(i, block_mass<D>(qa, ka, l2, scale_log2, w0, (kb0 + i) * 32, lane));
+            if (i + 2 < nb) load_kblock<D>(rk, (kb0 + i + 2) * 32, lane, ka);
+            if (i + 1 < nb) emit(i + 1, block_mass<D>(qa, kb, l2, scale_log2, w0, (kb0 + i + 1) * 32, lane));
+        }
+    } else {
+        // Grouped heads or a window of several row blocks: per key block, the
+        // Q operands of every (head, row block) come from L2.
+        auto mass = [&](int i, const bf16x8 (&kr)[KS]) {
+            const int kt0 = (kb0 + i) * 32;
+            float a = 0.0f;
+            for (int r = 0; r < R; ++r) {
+                const size_t qbase = ((size_t)b * Hq + g * R + r) * T_ctx;
+                for (int rb = 0; rb < nrb; ++rb) {
+                    const int row0 = w0 + 32 * rb;
+                    if (row0 + 31 < kt0) continue;  // rows entirely before this key block
+                    bf16x8 qa[KS];
+                    float l2[16];
+                    load_qblock<D>(q, lse, qbase, w0, W, rb, lane, qa, l2);
+                    a += block_mass<D>(qa, kr, l2, scale_log2, row0, kt0, lane);
                 }
             }
+            return a;
+        };
+        for (int i = 0; i < nb; i += 2) {
+            if (i + 1 < nb) load_kblock<D>(rk, (kb0 + i + 1) * 32, lane, kb);
+            emit(i, mass(i, ka));
+            if (i + 2 < nb) load_kblock<D>(rk, (kb0 + i + 2) * 32, lane, ka);
+            if (i + 1 < nb) emit(i + 1, mass(i + 1, kb));
         }
     }
-    acc += swap_halves(acc);
-    if (half == 0 && j < T_ctx) scores[kvbase + j] = acc;
 }
 
 template <int D>
 hipError_t launch_ws(const void* q, const void* k, const float* lse, int B, int T_ctx, int Hq, int Hkv, int W,
                      float sm_scale, float* scores, hipStream_t stream) {
-    const int nkb = (T_ctx + 127) / 128;
-    hipLaunchKernelGGL((window_scores_kernel<D>), dim3(nkb, Hkv, B), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse, T_ctx, Hq, Hkv, W,
-                       sm_scale * kLog2e, scores);
+    // Key blocks per wave: about one round of resident waves (256 CUs x 12),
+    // even for the two-set K pipeline.
+    const long long blocks = (long long)B * Hkv * ((T_ctx + 31) / 32);
+    int nbw = (int)((blocks + 3071) / 3072);
+    nbw = max(2, nbw + (nbw & 1));
+    const int nwg = (T_ctx + 128 * nbw - 1) / (128 * nbw);
+    const dim3 grid(nwg, Hkv, B);
+    if (Hq == Hkv && W <= 32)
+        hipLaunchKernelGGL((window_scores_kernel<D, true>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(q),
+                           static_cast<const uint16_t*>(k), lse, T_ctx, Hq, Hkv, W, nbw, sm_scale * kLog2e, scores);
+    else
+        hipLaunchKernelGGL((window_scores_kernel<D, false>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(q),
+                           static_cast<const uint16_t*>(k), lse, T_ctx, Hq, Hkv, W, nbw, sm_scale * kLog2e, scores);
     return hipGetLastError();
 }
 
