@@ -13,7 +13,8 @@
 //
 // HBM-bound gather: each kept row is read once (coalesced 4-byte lane loads of
 // two channels), each packed byte written once (key codes: dword stores
-// assembled with lane shuffles; value codes: one 16-byte store per lane).
+// assembled with DPP ORs; value codes: one 16-byte store per lane).  Keys and
+// values of a token group are packed by the two waves of one workgroup.
 #include "common.h"
 #include "kernels.h"
 
@@ -41,9 +42,19 @@ struct GroupParams {
     float e1, e2, e3;  // decision thresholds of code_of (infinite when s == 0)
 };
 
+// fl32(r / 3) for r >= 0 without the divide sequence: q0 = fl(r c) with
+// c = fl32(1/3), then one fma correction step.  Checked exhaustively against the
+// IEEE quotient for every finite r >= 0 (bit-identical); r = +inf is taken apart.
+__device__ __forceinline__ float div3(float r) {
+    const float c = 1.0f / 3.0f;
+    const float q0 = r * c;
+    const float q1 = fmaf(fmaf(-3.0f, q0, r), c, q0);
+    return r <= 0x1.fffffep127f ? q1 : INFINITY;
+}
+
 __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
     float rng = mx - mn;
-    float s32 = rng / 3.0f;
+    float s32 = div3(rng);
     uint32_t sb = f32_to_half_bits_rn(s32);
     uint32_t zb = f32_to_half_bits_rn(mn);
     const float s = half_bits_to_f32(sb);
@@ -68,15 +79,23 @@ __device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
            (uint32_t)(fmaf(-2.5f, p.s, d) > p.e3);
 }
 
+// OR over aligned groups of 8 lanes: quad swaps, then the mirrored half row.
+__device__ __forceinline__ uint32_t or8(uint32_t x) {
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, true);  // row_half_mirror
+    return x;
+}
+
 // Keys: one wave per (group of 32 kept tokens, KV head, sequence).
 // Lane l owns channels 2l, 2l+1 (D/2 active lanes).
 template <typename T, int D>
-__global__ __launch_bounds__(64) void quant_pack_k_kernel(
+__device__ __forceinline__ void pack_keys(
     const T* __restrict__ k, const int32_t* __restrict__ idx, int T_ctx, int n_keep, int Hkv,
     uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz) {
     const int gi = blockIdx.x;
     const int unit = blockIdx.z * Hkv + blockIdx.y;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x % kWave;
     const bool active = lane < D / 2;
     const int c = 2 * (active ? lane : 0);
     const int G = (n_keep + kGroup - 1) / kGroup;
@@ -109,7 +128,7 @@ __global__ __launch_bounds__(64) void quant_pack_k_kernel(
     for (int t = 0; t < kGroup; ++t) {
         if (t < cnt) {  // uniform across the wave
             uint32_t nib = active ? (code_of(x[t].a, p0) | (code_of(x[t].b, p1) << 2)) : 0u;
-            uint32_t word = group_or<8>(nib << (4 * (lane & 7)));
+            uint32_t word = or8(nib << (4 * (lane & 7)));
             if (active && (lane & 7) == 0)
                 *reinterpret_cast<uint32_t*>(crow + (size_t)t * (D / 4) + 4 * (lane >> 3)) = word;
         }
@@ -123,12 +142,12 @@ __global__ __launch_bounds__(64) void quant_pack_k_kernel(
 // (8 bytes each, the block's token 4m+j in bits 2j..2j+1 of byte m) and stores
 // both in one 16-byte write; tokens past n_keep stay code 0.
 template <typename T, int D>
-__global__ __launch_bounds__(64) void quant_pack_v_kernel(
+__device__ __forceinline__ void pack_values(
     const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, int n_keep, int Hkv,
     uint8_t* __restrict__ v_codes, uint32_t* __restrict__ v_sz) {
     const int gi = blockIdx.x;
     const int unit = blockIdx.z * Hkv + blockIdx.y;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x % kWave;
     const bool active = lane < D / 2;
     const int c = 2 * (active ? lane : 0);
     const int G = (n_keep + kGroup - 1) / kGroup;
@@ -164,18 +183,133 @@ __global__ __launch_bounds__(64) void quant_pack_v_kernel(
             make_uint4(wa[0], wa[1], wb[0], wb[1]);
 }
 
+// Full groups (32 kept tokens): the same rule without per-token branches.  Rows
+// are gathered through a buffer resource sized to the head's T rows (a position
+// outside [0, T) reads as zeros instead of faulting); key-code words and value
+// parameters are collected in registers and written four and two stores per
+// lane at the end.
+template <typename T> __device__ __forceinline__ Pair load_pair_buf(__amdgpu_buffer_rsrc_t r, int off);
+template <> __device__ __forceinline__ Pair load_pair_buf<float>(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    return {__uint_as_float(w.x), __uint_as_float(w.y)};
+}
+template <> __device__ __forceinline__ Pair load_pair_buf<uint16_t>(__amdgpu_buffer_rsrc_t r, int off) {
+    const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    return {bf16_bits_to_f32(w & 0xFFFFu), bf16_bits_to_f32(w >> 16)};
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void gather_full(const T* __restrict__ x, const int32_t* __restrict__ idx, int T_ctx,
+                                            int n_keep, int unit, int t0, int c, Pair (&out)[kGroup]) {
+    const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(x + (size_t)unit * T_ctx * D), 0,
+                                                     T_ctx * D * (int)sizeof(T), 0x00020000);
+    if (idx) {  // one branch per wave: the positions are read once, as scalars
+        const int32_t* ids = idx + (size_t)unit * n_keep + t0;
+        int pos[kGroup];
+#pragma unroll
+        for (int t = 0; t < kGroup; ++t) pos[t] = ids[t];
+#pragma unroll
+        for (int t = 0; t < kGroup; ++t) out[t] = load_pair_buf<T>(r, (pos[t] * D + c) * (int)sizeof(T));
+    } else {
+#pragma unroll
+        for (int t = 0; t < kGroup; ++t) out[t] = load_pair_buf<T>(r, ((t0 + t) * D + c) * (int)sizeof(T));
+    }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void pack_keys_full(
+    const T* __restrict__ k, const int32_t* __restrict__ idx, int T_ctx, int n_keep, int Hkv,
+    uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz) {
+    const int gi = blockIdx.x;
+    const int unit = blockIdx.z * Hkv + blockIdx.y;
+    const int lane = threadIdx.x % kWave;
+    const bool active = lane < D / 2;
+    const int c = 2 * (active ? lane : 0);
+    const int G = (n_keep + kGroup - 1) / kGroup;
+    const int t0 = gi * kGroup;
+    Pair x[kGroup];
+    gather_full<T, D>(k, idx, T_ctx, n_keep, unit, t0, c, x);
+    float mn0 = x[0].a, mx0 = x[0].a, mn1 = x[0].b, mx1 = x[0].b;
+#pragma unroll
+    for (int t = 1; t < kGroup; ++t) {
+        mn0 = fminf(mn0, x[t].a); mx0 = fmaxf(mx0, x[t].a);
+        mn1 = fminf(mn1, x[t].b); mx1 = fmaxf(mx1, x[t].b);
+    }
+    const GroupParams p0 = group_params(mn0, mx0);
+    const GroupParams p1 = group_params(mn1, mx1);
+    if (active) *reinterpret_cast<uint2*>(k_sz + ((size_t)unit * G + gi) * D + c) = make_uint2(p0.word, p1.word);
+    // Token t's word for channel block lane / 8 is kept by the lane with lane % 8 == t % 8.
+    uint32_t kw[kGroup / 8] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) {
+        const uint32_t nib = code_of(x[t].a, p0) | (code_of(x[t].b, p1) << 2);
+        const uint32_t word = or8(nib << (4 * (lane & 7)));
+        kw[t / 8] = (lane & 7) == (t & 7) ? word : kw[t / 8];
+    }
+    uint8_t* crow = k_codes + ((size_t)unit * n_keep + t0) * (D / 4);
+    if (active) {
+#pragma unroll
+        for (int m = 0; m < kGroup / 8; ++m)
+            *reinterpret_cast<uint32_t*>(crow + (size_t)(8 * m + (lane & 7)) * (D / 4) + 4 * (lane >> 3)) = kw[m];
+    }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void pack_values_full(
+    const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, int n_keep, int Hkv,
+    uint8_t* __restrict__ v_codes, uint32_t* __restrict__ v_sz) {
+    const int gi = blockIdx.x;
+    const int unit = blockIdx.z * Hkv + blockIdx.y;
+    const int lane = threadIdx.x % kWave;
+    const bool active = lane < D / 2;
+    const int c = 2 * (active ? lane : 0);
+    const int G = (n_keep + kGroup - 1) / kGroup;
+    const int t0 = gi * kGroup;
+    Pair x[kGroup];
+    gather_full<T, D>(v, idx, T_ctx, n_keep, unit, t0, c, x);
+    // Token t's parameter word of row lane / 16 is kept by the lane with lane % 16 == t % 16.
+    uint32_t wa[2] = {0u, 0u}, wb[2] = {0u, 0u}, vw[2] = {0u, 0u};
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) {
+        const float mn = dpp_min<16>(fminf(x[t].a, x[t].b));
+        const float mx = dpp_max<16>(fmaxf(x[t].a, x[t].b));
+        const GroupParams p = group_params(mn, mx);
+        wa[t / 16] |= code_of(x[t].a, p) << (2 * (t % 16));
+        wb[t / 16] |= code_of(x[t].b, p) << (2 * (t % 16));
+        vw[t / 16] = (lane & 15) == (t & 15) ? p.word : vw[t / 16];
+    }
+    if (active) {
+        *reinterpret_cast<uint4*>(v_codes + (((size_t)unit * G + gi) * D + c) * 8) = make_uint4(wa[0], wa[1], wb[0], wb[1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            v_sz[((size_t)unit * n_keep + t0 + 16 * h + (lane & 15)) * (D / 32) + (lane >> 4)] = vw[h];
+    }
+}
+
+// One workgroup per (group of 32 kept tokens, KV head, sequence): wave 0 packs
+// the keys, wave 1 the values.
+template <typename T, int D>
+__global__ __launch_bounds__(128) void quant_pack_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, int n_keep,
+    int Hkv, uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz, uint8_t* __restrict__ v_codes,
+    uint32_t* __restrict__ v_sz) {
+    const bool full = (blockIdx.x + 1) * kGroup <= n_keep;
+    if (threadIdx.x < kWave) {
+        if (full) pack_keys_full<T, D>(k, idx, T_ctx, n_keep, Hkv, k_codes, k_sz);
+        else pack_keys<T, D>(k, idx, T_ctx, n_keep, Hkv, k_codes, k_sz);
+    } else {
+        if (full) pack_values_full<T, D>(v, idx, T_ctx, n_keep, Hkv, v_codes, v_sz);
+        else pack_values<T, D>(v, idx, T_ctx, n_keep, Hkv, v_codes, v_sz);
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const void* k, const void* v, const int32_t* idx, int B, int Hkv, int T_ctx,
                         int n_keep, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes, uint32_t* v_sz,
                         hipStream_t stream) {
     const int G = (n_keep + kGroup - 1) / kGroup;
-    dim3 gk(G, Hkv, B);
-    hipLaunchKernelGGL((quant_pack_k_kernel<T, D>), gk, dim3(64), 0, stream,
-                       static_cast<const T*>(k), idx, T_ctx, n_keep, Hkv, k_codes, k_sz);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((quant_pack_v_kernel<T, D>), gk, dim3(64), 0, stream,
-                       static_cast<const T*>(v), idx, T_ctx, n_keep, Hkv, v_codes, v_sz);
+    hipLaunchKernelGGL((quant_pack_kernel<T, D>), dim3(G, Hkv, B), dim3(128), 0, stream, static_cast<const T*>(k),
+                       static_cast<const T*>(v), idx, T_ctx, n_keep, Hkv, k_codes, k_sz, v_codes, v_sz);
     return hipGetLastError();
 }
 
