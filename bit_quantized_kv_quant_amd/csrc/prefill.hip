@@ -65,10 +65,13 @@ constexpr int kKStride = D + 8;  // elements per staged K row
 // constant plus an immediate.
 constexpr int kVtLine = 288;
 
+// One block of 32 * WAVES query rows (query block qb of (sequence, head) hs),
+// staged through the workgroup's LDS.
 template <int D, bool kWithO, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int B_,
-    int T_ctx, int Hq, int Hkv, int nqb, float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse) {
+__device__ __forceinline__ void fa_block(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int T_ctx,
+    int Hq, int Hkv, float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse, int hs, int qb,
+    uint16_t* __restrict__ sK, char* __restrict__ sV) {
     constexpr int NT = 64 * WAVES;          // threads
     constexpr int BM = 32 * WAVES;          // query rows per workgroup
     constexpr int CH = D / 8;               // 16-byte chunks per row
@@ -80,20 +83,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     constexpr int CH2 = D / 64;             // 64-wide halves of the head dim
     constexpr int VT_BYTES = 32 * CH2 * kVtLine;  // one staged V^T tile (padded lines)
     static_assert(!kWithO || WAVES == 8, "the V^T staging map assumes 8 waves");
-    // two LDS stages: tile t is read from one while tile t+1 is written to the other
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2 * TILE];
-    __shared__ __attribute__((aligned(16))) char sV[kWithO ? 2 * VT_BYTES : 16];
-
-    // XCD-aware order: workgroup L is dispatched to XCD L % 8.  Work item W =
-    // (L % 8) * per + L / 8 gives each XCD a contiguous run of (sequence, head)
-    // pairs, all query blocks of a head back to back (longest first), so the
-    // K/V prefix a head's blocks re-read stays in that XCD's L2.
-    const int nwork = nqb * Hq * B_;
-    const int per = (nwork + kXcds - 1) / kXcds;
-    const int W = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-    if (W >= nwork) return;
-    const int hs = W / nqb;
-    const int qb = nqb - 1 - W % nqb;
     const int b = hs / Hq;
     const int h = hs % Hq;
     const int g = h / (Hq / Hkv);
@@ -137,19 +126,21 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + (kvbase + (size_t)n0) * D), 0,
                                                  (T_ctx - n0) * D * 2, 0x00020000);
     };
-    auto load_k = [&](int n0) {
+    auto load_k_into = [&](int n0, u32x4 (&dst)[LOADS]) {
         const auto rk = tile_rsrc(k, n0);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i)
-            pk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, goff0 + i * kRowStep * D * 2, 0, 0));
+            dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, goff0 + i * kRowStep * D * 2, 0, 0));
     };
-    auto store_k = [&](int buf) {
+    auto store_k_from = [&](int buf, const u32x4 (&src)[LOADS]) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int r = row0 + kRowStep * i, c = col0 / 8;
-            *reinterpret_cast<u32x4*>(sK + buf * TILE + (32 * (r >> 5) + key_lane(r & 31)) * KST + 8 * c) = pk[i];
+            *reinterpret_cast<u32x4*>(sK + buf * TILE + (32 * (r >> 5) + key_lane(r & 31)) * KST + 8 * c) = src[i];
         }
     };
+    auto load_k = [&](int n0) { load_k_into(n0, pk); };
+    auto store_k = [&](int buf) { store_k_from(buf, pk); };
     // V tiles are register-staged, converted to fp16 and stored transposed
     // (V^T, see kVtLine): thread (bk, s, c_hi from the wave; c_lo, dw, half from
     // the lane) loads the 16-byte chunk c = 8 c_hi + c_lo of keys 2j and 2j+1,
@@ -293,13 +284,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     // (they read the other K stage), then tile t's PV MFMAs follow.  K is staged
     // two tiles ahead, V one tile ahead.
     const int t_last = __builtin_amdgcn_readfirstlane(min(qw0 / kBN, ntiles - 1));  // wave-uniform
-    load_k(0);
-    load_v(0);
-    store_k(0);
-    store_v(0);
-    if (ntiles > 1) {
-        load_k(kBN);
-        store_k(1);
+    {  // first two K tiles and the first V tile: all loads in flight at once
+        u32x4 pk1[LOADS];
+        load_k(0);
+        load_v(0);
+        if (ntiles > 1) load_k_into(kBN, pk1);
+        store_k(0);
+        store_v(0);
+        if (ntiles > 1) store_k_from(1, pk1);
     }
     __syncthreads();
     f32x16 sacc[2];
@@ -359,13 +351,66 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     }
 }
 
+// Persistent workgroups, one per CU, dispatched round-robin over the XCDs
+// (workgroup L on XCD L % 8).  Each XCD owns a contiguous run of (sequence,
+// head) pairs, so the K/V prefix a head's query blocks re-read stays in that
+// XCD's L2.  Within an XCD the query blocks of each head are taken in pairs
+// (qb, nqb - 1 - qb), which cost the same, and the pairs are dealt round-robin
+// to the XCD's workgroups: equal work per workgroup, and no re-dispatch gaps
+// between blocks (a block's output stores drain while the next one loads).
+template <int D, bool kWithO, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int B_,
+    int T_ctx, int Hq, int Hkv, int nqb, float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse) {
+    constexpr int TILE = kBN * kKStride<D>;
+    constexpr int VT_BYTES = 32 * (D / 64) * kVtLine;
+    // two LDS stages: tile t is read from one while tile t+1 is written to the other
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2 * TILE];
+    __shared__ __attribute__((aligned(16))) char sV[kWithO ? 2 * VT_BYTES : 16];
+
+    const int heads = B_ * Hq;
+    const int per = (heads + kXcds - 1) / kXcds;
+    const int xcd = blockIdx.x % kXcds;
+    const int slot = blockIdx.x / kXcds;
+    const int nslots = gridDim.x / kXcds;
+    const int h0 = xcd * per;
+    const int nh = max(0, min(heads, h0 + per) - h0);
+    const int pairs = (nqb + 1) / 2;  // per head
+    // one call site: (pair p, second) walks the long then the short block of each pair
+    int p = slot;
+    bool second = false;
+    while (p < nh * pairs) {
+        const int hs = h0 + p / pairs;
+        const int j = p % pairs;
+        fa_block<D, kWithO, WAVES>(q, k, v, T_ctx, Hq, Hkv, scale_log2, o, lse, hs, second ? j : nqb - 1 - j, sK, sV);
+        if (!second && j != nqb - 1 - j) {
+            second = true;
+        } else {
+            second = false;
+            p += nslots;
+        }
+    }
+}
+
+int cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, c = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+            n = c;
+        else
+            n = 256;
+    }
+    return n;
+}
+
 template <int D, bool kWithO>
 hipError_t launch_fa(const void* q, const void* k, const void* v, int B, int T_ctx, int Hq, int Hkv,
                      float sm_scale, void* o, float* lse, hipStream_t stream) {
     constexpr int WAVES = kFaWaves;
     const int nqb = (T_ctx + 32 * WAVES - 1) / (32 * WAVES);
-    const int nwork = nqb * Hq * B;
-    const int grid = (nwork + kXcds - 1) / kXcds * kXcds;
+    const int grid = max(kXcds, cu_count() / kXcds * kXcds);
     hipLaunchKernelGGL((fa_fwd_kernel<D, kWithO, WAVES>), dim3(grid), dim3(64 * WAVES), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), B, T_ctx, Hq, Hkv, nqb, sm_scale * kLog2e,
