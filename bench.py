@@ -22,7 +22,10 @@ budget 30 % -> 5 %) at a batch that fills about 227 GB of HBM, and the
 Mistral-7B-shaped GQA cache (32 layers, 32 / 8 heads, 6600 kept tokens of a
 44000-token prompt, batch 4).  A decode step there is one query per sequence
 through every layer; kept-token K/V are drawn directly from the workload's
-distributions and packed by the library.
+distributions and packed by the library.  Then two single-layer prefill lines
+(1 x 32 heads x 16384 tokens, and one layer of the Mistral-7B-shaped GQA
+prompt, 4 x 32 / 8 heads x 44000 tokens): passes 1 and 2, selection and
+packing, each timed alone.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -53,6 +56,8 @@ def parse():
     ap.add_argument("--pyramid-batch", type=int, default=1024,
                     help="batch of the 40-layer pyramid decode sweep (1024 fills about 227 GB; 0 skips it)")
     ap.add_argument("--no-gqa-sweep", action="store_true", help="skip the 32-layer GQA decode sweep")
+    ap.add_argument("--no-prefill-sweep", action="store_true",
+                    help="skip the single-layer prefill lines (1 x 32 x 16384 and the 44k-token GQA layer)")
     return ap.parse_args()
 
 
@@ -96,6 +101,51 @@ def decode_layers(torch, mk, synth, wl, B, budgets, reps=3, chunk=64):
             "kept_tokens_first_last": [int(budgets[0]), int(budgets[-1])], "packed_GB": cache_bytes / 1e9,
             "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3), "achieved_GBs": gbs,
             "hbm_frac": gbs / PEAK_HBM_GBS}
+
+
+def prefill_layer(torch, mk, synth, wl, reps):
+    """One layer of a prefill workload through the chain's first four steps,
+    each timed alone (HIP events, `reps` calls after one warm-up call)."""
+    dev = torch.device("cuda:0")
+    q, k, v, _ = synth.make_qkv(wl, dev)
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    n_keep = mk.keep_count(T, wl.budget_pct)
+    n_heavy, n_recent = mk.split_heavy_recent(n_keep)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    scores = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Hkv, n_keep), dtype=torch.int32, device=dev)
+    cache = mk.PackedCache.alloc(B, Hkv, n_keep, D, dev)
+    calls = {
+        "prefill_attn": lambda: mk.prefill_attn(q, k, v, o=o, lse=lse),
+        "window_scores": lambda: mk.window_scores(q, k, lse, wl.window, scores=scores),
+        "select_topk": lambda: mk.select_topk(scores, n_heavy, n_recent, idx=idx),
+        "quant_pack": lambda: mk.quant_pack(k, v, idx, out=cache),
+    }
+    ms = {}
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / reps
+    flops = 2.0 * D * T * (T + 1) * Hq * B
+    tf = flops / (ms["prefill_attn"] * 1e-3) / 1e12
+    k_bytes = k.numel() * k.element_size()
+    pack_bytes = 2 * B * Hkv * n_keep * D * k.element_size() + cache.nbytes()
+    res = {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "context": T, "head_dim": D,
+           "window": wl.window, "n_keep": n_keep, "stages_ms": ms,
+           "prefill_TFLOPs": tf, "prefill_mfma_frac": tf / PEAK_BF16_TFLOPS,
+           "window_scores_GBs": k_bytes / (ms["window_scores"] * 1e-3) / 1e9,
+           "quant_pack_GBs": pack_bytes / (ms["quant_pack"] * 1e-3) / 1e9}
+    del q, k, v, o, lse, scores, idx, cache
+    torch.cuda.empty_cache()
+    return res
 
 
 class StageTimer:
@@ -329,6 +379,11 @@ def main():
         budgets = [mk.keep_count(gw.T, gw.budget_pct)] * gw.layers
         res["decode_gqa"] = decode_layers(torch, mk, synth, gw, gw.B, budgets, reps=20)
         print(f"# gqa decode: {json.dumps(res['decode_gqa'])}", file=sys.stderr, flush=True)
+    if not args.no_prefill_sweep:
+        res["prefill_16k"] = prefill_layer(torch, mk, synth, synth.WORKLOADS["prefill_16k"], reps=10)
+        print(f"# prefill 16k: {json.dumps(res['prefill_16k'])}", file=sys.stderr, flush=True)
+        res["prefill_gqa_44k"] = prefill_layer(torch, mk, synth, synth.WORKLOADS["mistral_44k"], reps=3)
+        print(f"# prefill gqa 44k (one layer): {json.dumps(res['prefill_gqa_44k'])}", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)
