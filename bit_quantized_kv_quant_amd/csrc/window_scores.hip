@@ -12,7 +12,8 @@
 // the sum over window rows is a per-lane sum plus one permlane32 swap.  K is
 // read from HBM once, the next block's K loaded while the current one is
 // reduced; for one query head and a window of up to 32 rows the Q operand and
-// the row lse stay in registers, otherwise they come from L2 per key block.
+// the row lse stay in registers, for up to four (query head, row block) sets
+// they are staged once per workgroup in LDS, otherwise they come from L2.
 // Summation order is fixed, so the scores are deterministic.
 #include "common.h"
 #include "kernels.h"
@@ -72,10 +73,14 @@ __device__ __forceinline__ void load_qblock(const uint16_t* __restrict__ q, cons
     }
 }
 
+constexpr int kMaxStaged = 4;  // (query head, row block) operand sets a workgroup can keep in LDS
+
 // grid (ceil(T / (128 nbw)), Hkv, B), 4 waves; wave w owns the nbw key blocks
-// from (blockIdx.x * 4 + w) * nbw (nbw even).  kRes: one query head per KV
-// head and a window of at most 32 rows (Q operand and row lse in registers).
-template <int D, bool kRes>
+// from (blockIdx.x * 4 + w) * nbw (nbw even).  kMode 0: one query head per KV
+// head and a window of at most 32 rows (Q operand and row lse in registers);
+// 1: at most kMaxStaged (query head, row block) pairs, staged once per
+// workgroup in LDS in the operand layout; 2: anything else (operands from L2).
+template <int D, int kMode>
 __global__ __launch_bounds__(256, 3) void window_scores_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const float* __restrict__ lse, int T_ctx, int Hq,
@@ -89,11 +94,30 @@ __global__ __launch_bounds__(256, 3) void window_scores_kernel(const uint16_t* _
     const int lane = threadIdx.x % kWave;
     const int half = lane >> 5;
     const int kb0 = (blockIdx.x * 4 + wave) * nbw;
-    if (kb0 * 32 >= T_ctx) return;
-    const int nb = min(nbw, (T_ctx - kb0 * 32 + 31) / 32);  // key blocks of this wave
     const size_t kvbase = ((size_t)b * Hkv + g) * T_ctx;
     const int w0 = T_ctx - W;  // first window row
     const int nrb = (W + 31) / 32;
+
+    // [set][kk][lane] Q operands and [set][row] lse * log2(e) of the staged sets
+    __shared__ bf16x8 s_q[kMode == 1 ? kMaxStaged * KS * kWave : 1];
+    __shared__ float s_l2[kMode == 1 ? kMaxStaged * 32 : 1];
+    if constexpr (kMode == 1) {
+        const int nset = R * nrb;
+        for (int c = threadIdx.x; c < nset * 32 * (D / 8); c += 256) {  // coalesced 16-byte chunks
+            const int set = c / (32 * (D / 8)), m = (c / (D / 8)) % 32, ch = c % (D / 8);
+            const int r = set / nrb, row = 32 * (set % nrb) + m;
+            const size_t qbase = ((size_t)b * Hq + g * R + r) * T_ctx;
+            s_q[(set * KS + (ch >> 1)) * kWave + ((ch & 1) << 5 | m)] =
+                row < W ? *reinterpret_cast<const bf16x8*>(q + (qbase + w0 + row) * D + 8 * ch) : bf16x8{};
+        }
+        for (int c = threadIdx.x; c < nset * 32; c += 256) {
+            const int set = c / 32, r = set / nrb, row = 32 * (set % nrb) + c % 32;
+            s_l2[c] = row < W ? lse[((size_t)b * Hq + g * R + r) * T_ctx + w0 + row] * kLog2e : INFINITY;
+        }
+        __syncthreads();
+    }
+    if (kb0 * 32 >= T_ctx) return;
+    const int nb = min(nbw, (T_ctx - kb0 * 32 + 31) / 32);  // key blocks of this wave
     const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k + kvbase * D), 0, T_ctx * D * 2, 0x00020000);
     auto emit = [&](int i, float a) {  // the block's per-key sums over the two lane halves
         a += swap_halves(a);
@@ -103,7 +127,7 @@ __global__ __launch_bounds__(256, 3) void window_scores_kernel(const uint16_t* _
 
     bf16x8 ka[KS], kb[KS];
     load_kblock<D>(rk, kb0 * 32, lane, ka);
-    if constexpr (kRes) {
+    if constexpr (kMode == 0) {
         // One query head, one row block: the Q operand and the row lse stay in
         // registers; K blocks stream through two register sets.
         bf16x8 qa[KS];
@@ -116,19 +140,30 @@ __global__ __launch_bounds__(256, 3) void window_scores_kernel(const uint16_t* _
             if (i + 1 < nb) emit(i + 1, block_mass<D>(qa, kb, l2, scale_log2, w0, (kb0 + i + 1) * 32, lane));
         }
     } else {
-        // Grouped heads or a window of several row blocks: per key block, the
-        // Q operands of every (head, row block) come from L2.
+        // Per key block, every (query head, row block) set: operands from LDS
+        // (mode 1) or from L2 (mode 2).
         auto mass = [&](int i, const bf16x8 (&kr)[KS]) {
             const int kt0 = (kb0 + i) * 32;
             float a = 0.0f;
             for (int r = 0; r < R; ++r) {
-                const size_t qbase = ((size_t)b * Hq + g * R + r) * T_ctx;
                 for (int rb = 0; rb < nrb; ++rb) {
                     const int row0 = w0 + 32 * rb;
                     if (row0 + 31 < kt0) continue;  // rows entirely before this key block
                     bf16x8 qa[KS];
                     float l2[16];
-                    load_qblock<D>(q, lse, qbase, w0, W, rb, lane, qa, l2);
+                    if constexpr (kMode == 1) {
+                        const int set = r * nrb + rb;
+#pragma unroll
+                        for (int kk = 0; kk < KS; ++kk) qa[kk] = s_q[(set * KS + kk) * kWave + lane];
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const f32x4 t = *reinterpret_cast<const f32x4*>(s_l2 + set * 32 + 8 * g4 + 4 * half);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) l2[4 * g4 + e] = t[e];
+                        }
+                    } else {
+                        load_qblock<D>(q, lse, ((size_t)b * Hq + g * R + r) * T_ctx, w0, W, rb, lane, qa, l2);
+                    }
                     a += block_mass<D>(qa, kr, l2, scale_log2, row0, kt0, lane);
                 }
             }
@@ -153,12 +188,16 @@ hipError_t launch_ws(const void* q, const void* k, const float* lse, int B, int 
     nbw = max(2, nbw + (nbw & 1));
     const int nwg = (T_ctx + 128 * nbw - 1) / (128 * nbw);
     const dim3 grid(nwg, Hkv, B);
+    const auto qq = static_cast<const uint16_t*>(q);
+    const auto kk = static_cast<const uint16_t*>(k);
+    const float sl = sm_scale * kLog2e;
+    const int sets = (Hq / Hkv) * ((W + 31) / 32);
     if (Hq == Hkv && W <= 32)
-        hipLaunchKernelGGL((window_scores_kernel<D, true>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(q),
-                           static_cast<const uint16_t*>(k), lse, T_ctx, Hq, Hkv, W, nbw, sm_scale * kLog2e, scores);
+        hipLaunchKernelGGL((window_scores_kernel<D, 0>), grid, dim3(256), 0, stream, qq, kk, lse, T_ctx, Hq, Hkv, W, nbw, sl, scores);
+    else if (sets <= kMaxStaged)
+        hipLaunchKernelGGL((window_scores_kernel<D, 1>), grid, dim3(256), 0, stream, qq, kk, lse, T_ctx, Hq, Hkv, W, nbw, sl, scores);
     else
-        hipLaunchKernelGGL((window_scores_kernel<D, false>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(q),
-                           static_cast<const uint16_t*>(k), lse, T_ctx, Hq, Hkv, W, nbw, sm_scale * kLog2e, scores);
+        hipLaunchKernelGGL((window_scores_kernel<D, 2>), grid, dim3(256), 0, stream, qq, kk, lse, T_ctx, Hq, Hkv, W, nbw, sl, scores);
     return hipGetLastError();
 }
 
