@@ -50,6 +50,11 @@ from .minikv_ref import (  # noqa: F401
     sz_words_ref,
     dequant_ref,
     decode_ref,
+    stream_split_ref,
+    concat_packed_ref,
+    stream_init_ref,
+    stream_append_ref,
+    stream_decode_ref,
     packed_bytes_ref,
     compression_ratio_ref,
 )

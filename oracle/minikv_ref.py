@@ -407,6 +407,93 @@ def decode_ref(q, packed, sm_scale=None):
 
 
 # ---------------------------------------------------------------------------
+# Streaming decode: generated tokens join the cache.  Keys are quantised per
+# channel over groups of 32 tokens (gptget.net summary, 方法论 / 方法详解), so a
+# key group can only be formed once 32 tokens exist.  Reading (the pages are
+# silent on generation): the packed region holds whole 32-token groups only;
+# the remaining kept tokens and the generated ones wait, unquantised (their
+# 16-bit values), in a residual window of at most 31 tokens, and every 32nd
+# residual token packs the window as the next group.  Decode attends to the
+# packed tokens and the residual ones.
+# ---------------------------------------------------------------------------
+
+def stream_split_ref(n_keep):
+    """(packed, residual) token counts of an n_keep-token selection: whole groups are packed."""
+    n_pk = GROUP * (int(n_keep) // GROUP)
+    return n_pk, int(n_keep) - n_pk
+
+
+def _empty_packed(B, Hkv, D):
+    return {
+        "k_codes": np.zeros((B, Hkv, 0, D // 4), np.uint8),
+        "k_scale": np.zeros((B, Hkv, 0, D), np.float16),
+        "k_zero": np.zeros((B, Hkv, 0, D), np.float16),
+        "v_codes": np.zeros((B, Hkv, 0, D, 8), np.uint8),
+        "v_scale": np.zeros((B, Hkv, 0, D // GROUP), np.float16),
+        "v_zero": np.zeros((B, Hkv, 0, D // GROUP), np.float16),
+    }
+
+
+def concat_packed_ref(a, b):
+    """Packed cache of a's tokens followed by b's; a must hold whole groups."""
+    if a["k_codes"].shape[2] % GROUP:
+        raise ValueError("the first cache must end on a group boundary")
+    return {key: np.concatenate([a[key], b[key]], axis=2) for key in a}
+
+
+def stream_init_ref(k, v, idx):
+    """Streaming state from a selection idx [B, Hkv, n]: the first whole groups of
+    kept tokens packed (quant_pack_ref), the rest kept as they are (fp32 values)."""
+    k = np.asarray(k, dtype=np.float32)
+    v = np.asarray(v, dtype=np.float32)
+    idx = np.asarray(idx, dtype=np.int64)
+    B, Hkv, _, D = k.shape
+    n_pk, _ = stream_split_ref(idx.shape[-1])
+    packed = quant_pack_ref(k, v, idx[..., :n_pk]) if n_pk else _empty_packed(B, Hkv, D)
+    rest = idx[..., n_pk:, None]
+    return {"packed": packed, "k_res": np.take_along_axis(k, rest, axis=2),
+            "v_res": np.take_along_axis(v, rest, axis=2)}
+
+
+def stream_append_ref(state, k_new, v_new):
+    """One generated token per (sequence, KV head), k_new / v_new [B, Hkv, D], joins
+    the residual; when the residual reaches 32 tokens it is packed as the next group."""
+    k_res = np.concatenate([state["k_res"], np.asarray(k_new, np.float32)[:, :, None]], axis=2)
+    v_res = np.concatenate([state["v_res"], np.asarray(v_new, np.float32)[:, :, None]], axis=2)
+    packed = state["packed"]
+    if k_res.shape[2] == GROUP:
+        packed = concat_packed_ref(packed, quant_pack_ref(k_res, v_res))
+        k_res, v_res = k_res[:, :, :0], v_res[:, :, :0]
+    return {"packed": packed, "k_res": k_res, "v_res": v_res}
+
+
+def stream_decode_ref(q, state, sm_scale=None):
+    """Single-query attention over the packed tokens (dequantised) followed by the
+    residual tokens (exact), fp64: the softmax runs over both sets together."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    k_res = np.asarray(state["k_res"], np.float64)
+    v_res = np.asarray(state["v_res"], np.float64)
+    Hkv = k_res.shape[1]
+    if state["packed"]["k_codes"].shape[2]:
+        k_hat, v_hat = dequant_ref(state["packed"])
+        keys = np.concatenate([k_hat, k_res], axis=2)
+        vals = np.concatenate([v_hat, v_res], axis=2)
+    else:
+        keys, vals = k_res, v_res
+    r = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    out = np.empty((B, Hq, D))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // r
+            logits = (keys[b, g] @ q[b, h]) * scale
+            p = np.exp(logits - logits.max())
+            out[b, h] = (p / p.sum()) @ vals[b, g]
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Bit accounting of the compact layout.
 # ---------------------------------------------------------------------------
 
