@@ -9,6 +9,7 @@ include/minikv.h).  This package is the thin Python binding.
 from ._lib import MinikvError, lib, status_string  # noqa: F401
 from .api import (  # noqa: F401
     PackedCache,
+    StreamCache,
     decode_attn,
     decode_ws_bytes,
     keep_count,

@@ -49,6 +49,11 @@ SIGNATURES = {
     "minikv_select_topk": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "minikv_quant_pack": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(PackedT), _vp]),
     "minikv_decode_attn": (_i, [_vp, ctypes.POINTER(PackedT), _i, _f, _vp, _vp, _sz, _vp]),
+    "minikv_stream_pack": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "minikv_stream_append": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "minikv_stream_decode": (_i, [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _f, _vp, _vp,
+                                  _sz, _vp]),
+    "minikv_stream_decode_ws_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "minikv_packed_bytes": (_sz, [_i, _i, _i, _i]),
     "minikv_decode_ws_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "minikv_keep_count": (_i, [_i, _i]),

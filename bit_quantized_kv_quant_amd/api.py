@@ -179,6 +179,109 @@ def decode_attn(q, cache, sm_scale=None, out=None, ws=None):
     return out
 
 
+@dataclass
+class StreamCache:
+    """Streaming cache: a packed region laid out for `cap` tokens (whole 32-token
+    groups; the first n_packed are valid) and a bf16 residual window of 32 slots
+    per (sequence, KV head) (the first n_res are valid).  Generated tokens are
+    appended to the window; 32 of them are packed as the next group."""
+
+    k_codes: torch.Tensor  # uint8 [B, Hkv, cap, D/4]
+    k_sz: torch.Tensor     # int32 [B, Hkv, cap/32, D]
+    v_codes: torch.Tensor  # uint8 [B, Hkv, cap/32, D, 8]
+    v_sz: torch.Tensor     # int32 [B, Hkv, cap, D/32]
+    k_res: torch.Tensor    # bf16 [B, Hkv, 32, D]
+    v_res: torch.Tensor    # bf16 [B, Hkv, 32, D]
+    B: int
+    Hkv: int
+    cap: int
+    D: int
+    n_packed: int = 0
+    n_res: int = 0
+
+    @staticmethod
+    def alloc(B, Hkv, cap, D, device="cuda"):
+        if cap < _lib.GROUP or cap % _lib.GROUP:
+            raise ValueError("cap must be a positive multiple of 32")
+        G = cap // _lib.GROUP
+        return StreamCache(
+            torch.empty((B, Hkv, cap, D // 4), dtype=torch.uint8, device=device),
+            torch.empty((B, Hkv, G, D), dtype=torch.int32, device=device),
+            torch.empty((B, Hkv, G, D, 8), dtype=torch.uint8, device=device),
+            torch.empty((B, Hkv, cap, D // _lib.GROUP), dtype=torch.int32, device=device),
+            torch.empty((B, Hkv, _lib.GROUP, D), dtype=torch.bfloat16, device=device),
+            torch.empty((B, Hkv, _lib.GROUP, D), dtype=torch.bfloat16, device=device),
+            B, Hkv, cap, D)
+
+    def _pack(self, k, v, idx, idx_stride, n, T):
+        dt = _lib.BF16 if k.dtype == torch.bfloat16 else _lib.F32
+        idx_ptr = None if idx is None else idx
+        st = _lib.lib().minikv_stream_pack(_ptr(k), _ptr(v), dt, idx_ptr, int(idx_stride), self.B, self.Hkv, int(T),
+                                           self.D, int(n), self.cap, self.n_packed, _ptr(self.k_codes),
+                                           _ptr(self.k_sz), _ptr(self.v_codes), _ptr(self.v_sz), _stream())
+        _lib.check("minikv_stream_pack", st)
+        self.n_packed += n
+
+    def init(self, k, v, idx):
+        """Start from a selection idx int32 [B, Hkv, n] of bf16 k, v [B, Hkv, T, D]:
+        its first whole groups are packed, the rest go to the window."""
+        B, Hkv, T, D = k.shape
+        _need(k, torch.bfloat16, (self.B, self.Hkv, T, self.D), "k")
+        _need(v, torch.bfloat16, (self.B, self.Hkv, T, self.D), "v")
+        n = idx.shape[-1]
+        _need(idx, torch.int32, (self.B, self.Hkv, n), "idx")
+        n_pk = _lib.GROUP * (n // _lib.GROUP)
+        self.n_packed, self.n_res = 0, 0
+        if n_pk > self.cap:
+            raise ValueError("selection larger than the cache capacity")
+        if n_pk:
+            self._pack(k, v, idx.data_ptr(), n, n_pk, T)
+        if n > n_pk:
+            st = _lib.lib().minikv_stream_append(_ptr(k), _ptr(v), idx.data_ptr() + 4 * n_pk, n, self.B, self.Hkv,
+                                                 T, self.D, n - n_pk, 0, _ptr(self.k_res), _ptr(self.v_res),
+                                                 _stream())
+            _lib.check("minikv_stream_append", st)
+            self.n_res = n - n_pk
+        return self
+
+    def append(self, k_new, v_new):
+        """One generated token per (sequence, KV head): k_new, v_new bf16 [B, Hkv, D].
+        Packs the window as the next group when it fills."""
+        _need(k_new, torch.bfloat16, (self.B, self.Hkv, self.D), "k_new")
+        _need(v_new, torch.bfloat16, (self.B, self.Hkv, self.D), "v_new")
+        st = _lib.lib().minikv_stream_append(_ptr(k_new), _ptr(v_new), None, 1, self.B, self.Hkv, 1, self.D, 1,
+                                             self.n_res, _ptr(self.k_res), _ptr(self.v_res), _stream())
+        _lib.check("minikv_stream_append", st)
+        self.n_res += 1
+        if self.n_res == _lib.GROUP:
+            if self.n_packed + _lib.GROUP > self.cap:
+                raise ValueError("streaming cache is full")
+            self._pack(self.k_res, self.v_res, None, _lib.GROUP, _lib.GROUP, _lib.GROUP)
+            self.n_res = 0
+        return self
+
+    def ws_bytes(self, Hq):
+        return int(_lib.lib().minikv_stream_decode_ws_bytes(self.B, Hq, self.Hkv, self.n_packed, self.n_res, self.D))
+
+    def decode(self, q, sm_scale=None, out=None, ws=None):
+        """Single-query attention over the packed and the residual tokens: q bf16 [B, Hq, D]."""
+        B, Hq, D = q.shape
+        _need(q, torch.bfloat16, (self.B, Hq, self.D), "q")
+        if out is None:
+            out = torch.empty_like(q)
+        _need(out, torch.bfloat16, (self.B, Hq, self.D), "out")
+        need = self.ws_bytes(Hq)
+        if ws is None:
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        st = _lib.lib().minikv_stream_decode(_ptr(q), self.B, Hq, self.Hkv, self.D, self.cap, self.n_packed,
+                                             _ptr(self.k_codes), _ptr(self.k_sz), _ptr(self.v_codes),
+                                             _ptr(self.v_sz), _ptr(self.k_res), _ptr(self.v_res), self.n_res,
+                                             float(sm_scale or 0.0), _ptr(out), _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream())
+        _lib.check("minikv_stream_decode", st)
+        return out
+
+
 def packed_bytes(B, Hkv, n_keep, D):
     return int(_lib.lib().minikv_packed_bytes(B, Hkv, n_keep, D))
 

@@ -164,4 +164,66 @@ int minikv_decode_attn(const void* q, const minikv_packed_t* cache, int Hq, floa
                                            as_stream(stream)));
 }
 
+int minikv_stream_pack(const void* k, const void* v, int in_dtype, const int32_t* idx, int idx_stride, int B,
+                       int Hkv, int T, int D, int n, int cap, int tok0, uint8_t* k_codes, uint32_t* k_sz,
+                       uint8_t* v_codes, uint32_t* v_sz, void* stream) {
+    if (!k || !v || !k_codes || !k_sz || !v_codes || !v_sz) return MINIKV_ERR_NULL;
+    if (B < 1 || Hkv < 1 || T < 1 || n < 1 || cap < 1 || tok0 < 0) return MINIKV_ERR_SHAPE;
+    if (n % MINIKV_GROUP || tok0 % MINIKV_GROUP || cap % MINIKV_GROUP || tok0 + n > cap) return MINIKV_ERR_SHAPE;
+    if (idx ? idx_stride < n : n > T) return MINIKV_ERR_SHAPE;
+    if (!supported_d(D)) return MINIKV_ERR_UNSUPPORTED;
+    if (in_dtype != MINIKV_F32 && in_dtype != MINIKV_BF16) return MINIKV_ERR_UNSUPPORTED;
+    if (misaligned(k) || misaligned(v) || misaligned(k_codes) || misaligned(k_sz) || misaligned(v_codes) ||
+        misaligned(v_sz))
+        return MINIKV_ERR_ALIGN;
+    return status_of(minikv::launch_stream_pack(k, v, in_dtype == MINIKV_BF16, idx, idx ? idx_stride : n, B, Hkv, T,
+                                                D, n, cap, tok0, k_codes, k_sz, v_codes, v_sz, as_stream(stream)));
+}
+
+int minikv_stream_append(const void* k, const void* v, const int32_t* idx, int idx_stride, int B, int Hkv, int T,
+                         int D, int n, int slot, void* k_res, void* v_res, void* stream) {
+    if (!k || !v || !k_res || !v_res) return MINIKV_ERR_NULL;
+    if (B < 1 || Hkv < 1 || T < 1 || n < 1 || slot < 0 || slot + n > MINIKV_GROUP) return MINIKV_ERR_SHAPE;
+    if (idx ? idx_stride < n : n > T) return MINIKV_ERR_SHAPE;
+    if (!supported_d(D)) return MINIKV_ERR_UNSUPPORTED;
+    if (misaligned(k) || misaligned(v) || misaligned(k_res) || misaligned(v_res)) return MINIKV_ERR_ALIGN;
+    return status_of(minikv::launch_stream_append(k, v, idx, idx ? idx_stride : n, B, Hkv, T, D, n, slot, k_res,
+                                                  v_res, as_stream(stream)));
+}
+
+size_t minikv_stream_decode_ws_bytes(int B, int Hq, int Hkv, int n_packed, int n_res, int D) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || n_packed < 0 || n_packed % MINIKV_GROUP || n_res < 0 ||
+        n_res >= MINIKV_GROUP || n_packed + n_res < 1 || !supported_d(D))
+        return 0;
+    const minikv::DecodePlan plan = minikv::decode_plan(B, Hq, Hkv, n_packed > 0 ? n_packed : 1, D);
+    const size_t b = minikv::stream_decode_ws_bytes(B, Hq, D, n_packed, n_res, plan);
+    return b ? b : 16;
+}
+
+int minikv_stream_decode(const void* q, int B, int Hq, int Hkv, int D, int cap, int n_packed,
+                         const uint8_t* k_codes, const uint32_t* k_sz, const uint8_t* v_codes,
+                         const uint32_t* v_sz, const void* k_res, const void* v_res, int n_res, float sm_scale,
+                         void* out, void* ws, size_t ws_bytes, void* stream) {
+    if (!q || !out) return MINIKV_ERR_NULL;
+    if (n_packed > 0 && (!k_codes || !k_sz || !v_codes || !v_sz)) return MINIKV_ERR_NULL;
+    if (n_res > 0 && (!k_res || !v_res)) return MINIKV_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || cap < 0 || cap % MINIKV_GROUP) return MINIKV_ERR_SHAPE;
+    if (n_packed < 0 || n_packed % MINIKV_GROUP || n_packed > cap || n_res < 0 || n_res >= MINIKV_GROUP ||
+        n_packed + n_res < 1)
+        return MINIKV_ERR_SHAPE;
+    if (!supported_d(D)) return MINIKV_ERR_UNSUPPORTED;
+    const int R = Hq / Hkv;
+    if (R != 1 && R != 2 && R != 4) return MINIKV_ERR_UNSUPPORTED;
+    if (misaligned(q) || misaligned(out) || (ws && misaligned(ws)) ||
+        (n_packed > 0 && (misaligned(k_codes) || misaligned(k_sz) || misaligned(v_codes) || misaligned(v_sz))) ||
+        (n_res > 0 && (misaligned(k_res) || misaligned(v_res))))
+        return MINIKV_ERR_ALIGN;
+    const minikv::DecodePlan plan = minikv::decode_plan(B, Hq, Hkv, n_packed > 0 ? n_packed : 1, D);
+    const size_t need = minikv::stream_decode_ws_bytes(B, Hq, D, n_packed, n_res, plan);
+    if (need > 0 && (!ws || ws_bytes < need)) return MINIKV_ERR_WORKSPACE;
+    return status_of(minikv::launch_stream_decode(q, k_codes, k_sz, v_codes, v_sz, B, Hq, Hkv, D, cap, n_packed,
+                                                  k_res, v_res, n_res, resolve_scale(sm_scale, D), out, ws, plan,
+                                                  as_stream(stream)));
+}
+
 }  // extern "C"

@@ -196,9 +196,9 @@ __device__ __forceinline__ void wave_sync_lds() {
 template <int D, int R>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes, const uint32_t* __restrict__ k_sz,
-    const uint8_t* __restrict__ v_codes, const uint32_t* __restrict__ v_sz, int n, int chunk, int splits,
-    int n_items, float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-    __bf16* __restrict__ out) {
+    const uint8_t* __restrict__ v_codes, const uint32_t* __restrict__ v_sz, int n, int tok_stride, int grp_stride,
+    int chunk, int splits, int ws_splits, int n_items, float scale_log2, float* __restrict__ ws_acc,
+    float* __restrict__ ws_ml, __bf16* __restrict__ out) {
     constexpr int NG = D / 32;  // 32-channel groups: key K blocks and value scale groups
     constexpr int NT = D / 16;  // 16-channel value tiles
     constexpr int GPL = NG * R / 4 > 1 ? NG * R / 4 : 1;  // value groups per lane in the weight prep
@@ -210,7 +210,6 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const int lane = threadIdx.x % kWave;
     const int col = lane % 16, blk = lane / 16;
     const int myh = blk % R;  // head of this lane's MFMA result rows
-    const int G = (n + kGroup - 1) / kGroup;
     const int nwaves = gridDim.x * 4;
     int item = blockIdx.x * 4 + wave;
     if (item >= n_items) return;  // wave-uniform; the kernel has no workgroup barrier
@@ -270,8 +269,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     auto load_keys = [&](const Pos& ps, Stage& st) {
         const int t0 = ps.step * kStep;
         const int nt = ps.t_end - t0;  // valid tokens from t0
-        const auto rk = rsrc(k_codes + ((size_t)ps.unit * n + t0) * (D / 4), nt * (D / 4));
-        const auto rs = rsrc(k_sz + ((size_t)ps.unit * G + t0 / kGroup) * D, (nt + kGroup - 1) / kGroup * D * 4);
+        const auto rk = rsrc(k_codes + ((size_t)ps.unit * tok_stride + t0) * (D / 4), nt * (D / 4));
+        const auto rs = rsrc(k_sz + ((size_t)ps.unit * grp_stride + t0 / kGroup) * D, (nt + kGroup - 1) / kGroup * D * 4);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             st.kc[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, (int)kc_off(j), 0, 0));
@@ -284,8 +283,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     auto load_values = [&](const Pos& ps, Stage& st) {
         const int t0 = ps.step * kStep;
         const int nt = ps.t_end - t0;
-        const auto rv = rsrc(v_codes + ((size_t)ps.unit * G + t0 / kGroup) * D * 8, (nt + kGroup - 1) / kGroup * D * 8);
-        const auto rz = rsrc(v_sz + ((size_t)ps.unit * n + t0) * NG, nt * NG * 4);
+        const auto rv = rsrc(v_codes + ((size_t)ps.unit * grp_stride + t0 / kGroup) * D * 8, (nt + kGroup - 1) / kGroup * D * 8);
+        const auto rz = rsrc(v_sz + ((size_t)ps.unit * tok_stride + t0) * NG, nt * NG * 4);
 #pragma unroll
         for (int T = 0; T < NT; ++T)
             st.vc[T] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(voff + 128 * T), 0, 0));
@@ -487,14 +486,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 #pragma unroll
             for (int T = 0; T < NT; ++T) {
                 const float x = acc[T] + s_z[wave][blk][T / 2];
-                if (splits == 1)
+                if (ws_splits == 1)
                     out[row * D + 16 * T + col] = (__bf16)(x / lsum);
                 else
-                    ws_acc[(row * splits + split) * D + 16 * T + col] = x;
+                    ws_acc[(row * ws_splits + split) * D + 16 * T + col] = x;
             }
-            if (splits > 1 && col == 0) {
-                ws_ml[(row * splits + split) * 2 + 0] = m_run;
-                ws_ml[(row * splits + split) * 2 + 1] = lsum;
+            if (ws_splits > 1 && col == 0) {
+                ws_ml[(row * ws_splits + split) * 2 + 0] = m_run;
+                ws_ml[(row * ws_splits + split) * 2 + 1] = lsum;
             }
         }
         wave_sync_lds();  // s_z is rewritten by the next item
@@ -551,6 +550,64 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     out[(size_t)bh * D + t] = (__bf16)(((o0 + o1) + (o2 + o3)) / L);
 }
 
+// Exact part of a streaming decode: the residual tokens (bf16 K / V, at most
+// 31, slots [B][Hkv][res_stride][D]) of one (sequence, query head) per wave.
+// Writes partial `slot` in the merge format (sum of 2^(l - m) v, m, sum of
+// 2^(l - m); l in log2 units), or the normalised output when it is the only
+// part (ws_splits == 1).  Lane l holds channels l, l + 64 (D = 128) or l.
+template <int D>
+__global__ __launch_bounds__(64) void decode_residual_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_res, const uint16_t* __restrict__ v_res,
+    int res_stride, int n_res, int Hq, int Hkv, float scale_log2, float* __restrict__ ws_acc,
+    float* __restrict__ ws_ml, int ws_splits, int slot, __bf16* __restrict__ out) {
+    constexpr int C = D / kWave;  // channels per lane
+    const int row = blockIdx.x;   // b * Hq + h
+    const int b = row / Hq, h = row % Hq;
+    const int g = h / (Hq / Hkv);
+    const int lane = threadIdx.x;
+    const uint16_t* kr = k_res + ((size_t)b * Hkv + g) * res_stride * D;
+    const uint16_t* vr = v_res + ((size_t)b * Hkv + g) * res_stride * D;
+    float qc[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) qc[c] = bf16_bits_to_f32(q[(size_t)row * D + lane + kWave * c]);
+    float l[kGroup];
+    float m = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kGroup - 1; ++t) {
+        l[t] = -INFINITY;
+        if (t < n_res) {
+            float d = 0.0f;
+#pragma unroll
+            for (int c = 0; c < C; ++c) d = fmaf(qc[c], bf16_bits_to_f32(kr[(size_t)t * D + lane + kWave * c]), d);
+            l[t] = dpp_sum<kWave>(d) * scale_log2;
+            m = fmaxf(m, l[t]);
+        }
+    }
+    float lsum = 0.0f, x[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) x[c] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kGroup - 1; ++t) {
+        if (t < n_res) {
+            const float p = exp2f(l[t] - m);
+            lsum += p;
+#pragma unroll
+            for (int c = 0; c < C; ++c) x[c] = fmaf(p, bf16_bits_to_f32(vr[(size_t)t * D + lane + kWave * c]), x[c]);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        if (ws_splits == 1)
+            out[(size_t)row * D + lane + kWave * c] = (__bf16)(x[c] / lsum);
+        else
+            ws_acc[((size_t)row * ws_splits + slot) * D + lane + kWave * c] = x[c];
+    }
+    if (ws_splits > 1 && lane == 0) {
+        ws_ml[((size_t)row * ws_splits + slot) * 2 + 0] = m;
+        ws_ml[((size_t)row * ws_splits + slot) * 2 + 1] = lsum;
+    }
+}
+
 // Resident workgroups of a decode instantiation on the current device: the
 // persistent grid is sized to it.  Host-side queries only, cached.
 template <int D, int R>
@@ -572,32 +629,56 @@ int resident_workgroups() {
     return per_cu * c;
 }
 
+// Where a decode reads: the packed region (n tokens; strides of its layout)
+// and an optional exact residual (n_res tokens of res_stride slots).
+struct DecodeSrc {
+    const uint8_t* k_codes;
+    const uint32_t* k_sz;
+    const uint8_t* v_codes;
+    const uint32_t* v_sz;
+    int n, tok_stride, grp_stride;
+    const uint16_t* k_res;
+    const uint16_t* v_res;
+    int res_stride, n_res;
+};
+
 template <int D, int R>
-hipError_t launch_dr(const void* q, const uint8_t* k_codes, const uint32_t* k_sz, const uint8_t* v_codes,
-                     const uint32_t* v_sz, int B, int Hq, int Hkv, int n, float scale_log2, void* out,
+hipError_t launch_dr(const void* q, const DecodeSrc& src, int B, int Hq, int Hkv, float scale_log2, void* out,
                      void* ws, const DecodePlan& plan, hipStream_t stream) {
+    const int packed_parts = src.n > 0 ? plan.splits : 0;
+    const int parts = packed_parts + (src.n_res > 0 ? 1 : 0);
     float* ws_acc = static_cast<float*>(ws);
-    float* ws_ml = ws_acc + (size_t)B * Hq * plan.splits * D;
-    const long items = (long)B * Hkv * plan.splits;
-    const long grid = std::min<long>((items + 3) / 4, resident_workgroups<D, R>());
-    hipLaunchKernelGGL((decode_partial_kernel<D, R>), dim3((unsigned)grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), k_codes, k_sz, v_codes, v_sz, n, plan.chunk, plan.splits,
-                       (int)items, scale_log2, ws_acc, ws_ml, static_cast<__bf16*>(out));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || plan.splits == 1) return e;  // one split: the partial kernel wrote out
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(B * Hq), dim3(D), 0, stream, ws_acc, ws_ml,
-                       plan.splits, static_cast<__bf16*>(out));
+    float* ws_ml = ws_acc + (size_t)B * Hq * parts * D;
+    if (packed_parts) {
+        const long items = (long)B * Hkv * plan.splits;
+        const long grid = std::min<long>((items + 3) / 4, resident_workgroups<D, R>());
+        hipLaunchKernelGGL((decode_partial_kernel<D, R>), dim3((unsigned)grid), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(q), src.k_codes, src.k_sz, src.v_codes, src.v_sz, src.n,
+                           src.tok_stride, src.grp_stride, plan.chunk, plan.splits, parts, (int)items, scale_log2,
+                           ws_acc, ws_ml, static_cast<__bf16*>(out));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (src.n_res > 0) {
+        hipLaunchKernelGGL((decode_residual_kernel<D>), dim3(B * Hq), dim3(kWave), 0, stream,
+                           static_cast<const uint16_t*>(q), src.k_res, src.v_res, src.res_stride, src.n_res, Hq, Hkv,
+                           scale_log2, ws_acc, ws_ml, parts, parts - 1, static_cast<__bf16*>(out));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (parts == 1) return hipSuccess;  // a single part wrote out itself
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(B * Hq), dim3(D), 0, stream, ws_acc, ws_ml, parts,
+                       static_cast<__bf16*>(out));
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const void* q, const uint8_t* k_codes, const uint32_t* k_sz, const uint8_t* v_codes,
-                    const uint32_t* v_sz, int B, int Hq, int Hkv, int n, float scale_log2, void* out,
+hipError_t launch_d(const void* q, const DecodeSrc& src, int B, int Hq, int Hkv, float scale_log2, void* out,
                     void* ws, const DecodePlan& plan, hipStream_t stream) {
     switch (Hq / Hkv) {
-        case 1: return launch_dr<D, 1>(q, k_codes, k_sz, v_codes, v_sz, B, Hq, Hkv, n, scale_log2, out, ws, plan, stream);
-        case 2: return launch_dr<D, 2>(q, k_codes, k_sz, v_codes, v_sz, B, Hq, Hkv, n, scale_log2, out, ws, plan, stream);
-        case 4: return launch_dr<D, 4>(q, k_codes, k_sz, v_codes, v_sz, B, Hq, Hkv, n, scale_log2, out, ws, plan, stream);
+        case 1: return launch_dr<D, 1>(q, src, B, Hq, Hkv, scale_log2, out, ws, plan, stream);
+        case 2: return launch_dr<D, 2>(q, src, B, Hq, Hkv, scale_log2, out, ws, plan, stream);
+        case 4: return launch_dr<D, 4>(q, src, B, Hq, Hkv, scale_log2, out, ws, plan, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -611,7 +692,7 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int n_keep, int D) {
     const int steps = (n_keep + kStep - 1) / kStep;
     const long want = (4096 + units - 1) / units;  // aim for >= 4096 work items
     int splits = (int)(want < 1 ? 1 : (want > steps ? steps : want));
-    if (splits > kMaxSplits) splits = kMaxSplits;
+    if (splits > kMaxSplits - 1) splits = kMaxSplits - 1;  // one merge slot stays free for a residual part
     const int per = (steps + splits - 1) / splits;
     splits = (steps + per - 1) / per;
     return {splits, per * kStep};
@@ -621,13 +702,30 @@ size_t decode_ws_bytes(int B, int Hq, int D, const DecodePlan& plan) {
     return (size_t)B * Hq * plan.splits * (D + 2) * sizeof(float);
 }
 
+size_t stream_decode_ws_bytes(int B, int Hq, int D, int n_packed, int n_res, const DecodePlan& plan) {
+    const int parts = (n_packed > 0 ? plan.splits : 0) + (n_res > 0 ? 1 : 0);
+    return (size_t)B * Hq * parts * (D + 2) * sizeof(float);
+}
+
 hipError_t launch_decode(const void* q, const uint8_t* k_codes, const uint32_t* k_sz, const uint8_t* v_codes,
                          const uint32_t* v_sz, int B, int Hq, int Hkv, int n_keep, int D, float sm_scale,
                          void* out, void* ws, const DecodePlan& plan, hipStream_t stream) {
     const float scale_log2 = sm_scale * kLog2e;
-    if (D == 128)
-        return launch_d<128>(q, k_codes, k_sz, v_codes, v_sz, B, Hq, Hkv, n_keep, scale_log2, out, ws, plan, stream);
-    return launch_d<64>(q, k_codes, k_sz, v_codes, v_sz, B, Hq, Hkv, n_keep, scale_log2, out, ws, plan, stream);
+    const DecodeSrc src{k_codes, k_sz, v_codes, v_sz, n_keep, n_keep, (n_keep + kGroup - 1) / kGroup,
+                        nullptr, nullptr, 0, 0};
+    if (D == 128) return launch_d<128>(q, src, B, Hq, Hkv, scale_log2, out, ws, plan, stream);
+    return launch_d<64>(q, src, B, Hq, Hkv, scale_log2, out, ws, plan, stream);
+}
+
+hipError_t launch_stream_decode(const void* q, const uint8_t* k_codes, const uint32_t* k_sz, const uint8_t* v_codes,
+                                const uint32_t* v_sz, int B, int Hq, int Hkv, int D, int cap, int n_packed,
+                                const void* k_res, const void* v_res, int n_res, float sm_scale, void* out,
+                                void* ws, const DecodePlan& plan, hipStream_t stream) {
+    const float scale_log2 = sm_scale * kLog2e;
+    const DecodeSrc src{k_codes, k_sz, v_codes, v_sz, n_packed, cap, cap / kGroup,
+                        static_cast<const uint16_t*>(k_res), static_cast<const uint16_t*>(v_res), kGroup, n_res};
+    if (D == 128) return launch_d<128>(q, src, B, Hq, Hkv, scale_log2, out, ws, plan, stream);
+    return launch_d<64>(q, src, B, Hq, Hkv, scale_log2, out, ws, plan, stream);
 }
 
 }  // namespace minikv

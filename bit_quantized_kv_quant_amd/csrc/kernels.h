@@ -12,6 +12,16 @@ hipError_t launch_quant_pack(const void* k, const void* v, bool bf16, const int3
                              int Hkv, int T_ctx, int D, int n_keep, uint8_t* k_codes, uint32_t* k_sz,
                              uint8_t* v_codes, uint32_t* v_sz, hipStream_t stream);
 
+// Streaming: pack n tokens (selection idx with row stride idx_stride, or the
+// first n rows) into tokens tok0.. of a layout for cap tokens per head.
+hipError_t launch_stream_pack(const void* k, const void* v, bool bf16, const int32_t* idx, int idx_stride, int B,
+                              int Hkv, int T_ctx, int D, int n, int cap, int tok0, uint8_t* k_codes,
+                              uint32_t* k_sz, uint8_t* v_codes, uint32_t* v_sz, hipStream_t stream);
+
+// Streaming: copy n bf16 rows (idx or the first n) into residual slots slot.. (32 per head).
+hipError_t launch_stream_append(const void* k, const void* v, const int32_t* idx, int idx_stride, int B, int Hkv,
+                                int T_ctx, int D, int n, int slot, void* k_res, void* v_res, hipStream_t stream);
+
 hipError_t launch_select_topk(const float* scores, int B, int Hkv, int T_ctx, int n_heavy,
                               int n_recent, int32_t* idx, hipStream_t stream);
 
@@ -22,11 +32,19 @@ struct DecodePlan {
 };
 DecodePlan decode_plan(int B, int Hq, int Hkv, int n_keep, int D);
 size_t decode_ws_bytes(int B, int Hq, int D, const DecodePlan& plan);
+size_t stream_decode_ws_bytes(int B, int Hq, int D, int n_packed, int n_res, const DecodePlan& plan);
 
 hipError_t launch_decode(const void* q, const uint8_t* k_codes, const uint32_t* k_sz,
                          const uint8_t* v_codes, const uint32_t* v_sz, int B, int Hq, int Hkv,
                          int n_keep, int D, float sm_scale, void* out, void* ws,
                          const DecodePlan& plan, hipStream_t stream);
+
+// Streaming decode: n_packed tokens of a layout for cap tokens per head, then
+// n_res exact residual tokens (bf16, 32 slots per head).
+hipError_t launch_stream_decode(const void* q, const uint8_t* k_codes, const uint32_t* k_sz, const uint8_t* v_codes,
+                                const uint32_t* v_sz, int B, int Hq, int Hkv, int D, int cap, int n_packed,
+                                const void* k_res, const void* v_res, int n_res, float sm_scale, void* out,
+                                void* ws, const DecodePlan& plan, hipStream_t stream);
 
 hipError_t launch_prefill(const void* q, const void* k, const void* v, int B, int T_ctx, int Hq,
                           int Hkv, int D, float sm_scale, void* o, float* lse, hipStream_t stream);

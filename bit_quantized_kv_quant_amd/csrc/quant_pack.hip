@@ -79,6 +79,14 @@ __device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
            (uint32_t)(fmaf(-2.5f, p.s, d) > p.e3);
 }
 
+// Where one call packs: tokens 0..n-1 of its selection (index row stride
+// idx_stride) go to tokens tok0.. of a destination laid out for tok_stride
+// tokens and grp_stride key groups per (sequence, KV head); tok0 is a multiple
+// of 32, so destination groups are whole.
+struct PackGeom {
+    int n, idx_stride, tok_stride, grp_stride, tok0;
+};
+
 // OR over aligned groups of 8 lanes: quad swaps, then the mirrored half row.
 __device__ __forceinline__ uint32_t or8(uint32_t x) {
     x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
@@ -91,18 +99,17 @@ __device__ __forceinline__ uint32_t or8(uint32_t x) {
 // Lane l owns channels 2l, 2l+1 (D/2 active lanes).
 template <typename T, int D>
 __device__ __forceinline__ void pack_keys(
-    const T* __restrict__ k, const int32_t* __restrict__ idx, int T_ctx, int n_keep, int Hkv,
+    const T* __restrict__ k, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int Hkv,
     uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz) {
     const int gi = blockIdx.x;
     const int unit = blockIdx.z * Hkv + blockIdx.y;
     const int lane = threadIdx.x % kWave;
     const bool active = lane < D / 2;
     const int c = 2 * (active ? lane : 0);
-    const int G = (n_keep + kGroup - 1) / kGroup;
     const int t0 = gi * kGroup;
-    const int cnt = min(kGroup, n_keep - t0);
+    const int cnt = min(kGroup, pg.n - t0);
     const T* base = k + (size_t)unit * T_ctx * D;
-    const int32_t* ids = idx ? idx + (size_t)unit * n_keep + t0 : nullptr;
+    const int32_t* ids = idx ? idx + (size_t)unit * pg.idx_stride + t0 : nullptr;
 
     Pair x[kGroup];
     float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
@@ -121,9 +128,9 @@ __device__ __forceinline__ void pack_keys(
     const GroupParams p1 = group_params(mn1, mx1);
     if (active) {
         uint2 w = make_uint2(p0.word, p1.word);
-        *reinterpret_cast<uint2*>(k_sz + ((size_t)unit * G + gi) * D + c) = w;
+        *reinterpret_cast<uint2*>(k_sz + ((size_t)unit * pg.grp_stride + pg.tok0 / kGroup + gi) * D + c) = w;
     }
-    uint8_t* crow = k_codes + ((size_t)unit * n_keep + t0) * (D / 4);
+    uint8_t* crow = k_codes + ((size_t)unit * pg.tok_stride + pg.tok0 + t0) * (D / 4);
 #pragma unroll
     for (int t = 0; t < kGroup; ++t) {
         if (t < cnt) {  // uniform across the wave
@@ -140,21 +147,20 @@ __device__ __forceinline__ void pack_keys(
 // group, so each token's min / max is a row reduction.  The codes are gathered
 // along tokens: the lane ends with the 32 codes of each of its two channels
 // (8 bytes each, the block's token 4m+j in bits 2j..2j+1 of byte m) and stores
-// both in one 16-byte write; tokens past n_keep stay code 0.
+// both in one 16-byte write; tokens past the call's count stay code 0.
 template <typename T, int D>
 __device__ __forceinline__ void pack_values(
-    const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, int n_keep, int Hkv,
+    const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int Hkv,
     uint8_t* __restrict__ v_codes, uint32_t* __restrict__ v_sz) {
     const int gi = blockIdx.x;
     const int unit = blockIdx.z * Hkv + blockIdx.y;
     const int lane = threadIdx.x % kWave;
     const bool active = lane < D / 2;
     const int c = 2 * (active ? lane : 0);
-    const int G = (n_keep + kGroup - 1) / kGroup;
     const int t0 = gi * kGroup;
-    const int cnt = min(kGroup, n_keep - t0);
+    const int cnt = min(kGroup, pg.n - t0);
     const T* base = v + (size_t)unit * T_ctx * D;
-    const int32_t* ids = idx ? idx + (size_t)unit * n_keep + t0 : nullptr;
+    const int32_t* ids = idx ? idx + (size_t)unit * pg.idx_stride + t0 : nullptr;
 
     Pair x[kGroup];
 #pragma unroll
@@ -175,11 +181,11 @@ __device__ __forceinline__ void pack_values(
             wa[t / 16] |= code_of(x[t].a, p) << (2 * (t % 16));
             wb[t / 16] |= code_of(x[t].b, p) << (2 * (t % 16));
             if (active && (lane & 15) == 0)
-                v_sz[((size_t)unit * n_keep + t0 + t) * (D / 32) + (lane >> 4)] = p.word;
+                v_sz[((size_t)unit * pg.tok_stride + pg.tok0 + t0 + t) * (D / 32) + (lane >> 4)] = p.word;
         }
     }
     if (active)
-        *reinterpret_cast<uint4*>(v_codes + (((size_t)unit * G + gi) * D + c) * 8) =
+        *reinterpret_cast<uint4*>(v_codes + (((size_t)unit * pg.grp_stride + pg.tok0 / kGroup + gi) * D + c) * 8) =
             make_uint4(wa[0], wa[1], wb[0], wb[1]);
 }
 
@@ -200,11 +206,11 @@ template <> __device__ __forceinline__ Pair load_pair_buf<uint16_t>(__amdgpu_buf
 
 template <typename T, int D>
 __device__ __forceinline__ void gather_full(const T* __restrict__ x, const int32_t* __restrict__ idx, int T_ctx,
-                                            int n_keep, int unit, int t0, int c, Pair (&out)[kGroup]) {
+                                            int idx_stride, int unit, int t0, int c, Pair (&out)[kGroup]) {
     const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(x + (size_t)unit * T_ctx * D), 0,
                                                      T_ctx * D * (int)sizeof(T), 0x00020000);
     if (idx) {  // one branch per wave: the positions are read once, as scalars
-        const int32_t* ids = idx + (size_t)unit * n_keep + t0;
+        const int32_t* ids = idx + (size_t)unit * idx_stride + t0;
         int pos[kGroup];
 #pragma unroll
         for (int t = 0; t < kGroup; ++t) pos[t] = ids[t];
@@ -218,17 +224,16 @@ __device__ __forceinline__ void gather_full(const T* __restrict__ x, const int32
 
 template <typename T, int D>
 __device__ __forceinline__ void pack_keys_full(
-    const T* __restrict__ k, const int32_t* __restrict__ idx, int T_ctx, int n_keep, int Hkv,
+    const T* __restrict__ k, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int Hkv,
     uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz) {
     const int gi = blockIdx.x;
     const int unit = blockIdx.z * Hkv + blockIdx.y;
     const int lane = threadIdx.x % kWave;
     const bool active = lane < D / 2;
     const int c = 2 * (active ? lane : 0);
-    const int G = (n_keep + kGroup - 1) / kGroup;
     const int t0 = gi * kGroup;
     Pair x[kGroup];
-    gather_full<T, D>(k, idx, T_ctx, n_keep, unit, t0, c, x);
+    gather_full<T, D>(k, idx, T_ctx, pg.idx_stride, unit, t0, c, x);
     float mn0 = x[0].a, mx0 = x[0].a, mn1 = x[0].b, mx1 = x[0].b;
 #pragma unroll
     for (int t = 1; t < kGroup; ++t) {
@@ -237,7 +242,7 @@ __device__ __forceinline__ void pack_keys_full(
     }
     const GroupParams p0 = group_params(mn0, mx0);
     const GroupParams p1 = group_params(mn1, mx1);
-    if (active) *reinterpret_cast<uint2*>(k_sz + ((size_t)unit * G + gi) * D + c) = make_uint2(p0.word, p1.word);
+    if (active) *reinterpret_cast<uint2*>(k_sz + ((size_t)unit * pg.grp_stride + pg.tok0 / kGroup + gi) * D + c) = make_uint2(p0.word, p1.word);
     // Token t's word for channel block lane / 8 is kept by the lane with lane % 8 == t % 8.
     uint32_t kw[kGroup / 8] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -246,7 +251,7 @@ __device__ __forceinline__ void pack_keys_full(
         const uint32_t word = or8(nib << (4 * (lane & 7)));
         kw[t / 8] = (lane & 7) == (t & 7) ? word : kw[t / 8];
     }
-    uint8_t* crow = k_codes + ((size_t)unit * n_keep + t0) * (D / 4);
+    uint8_t* crow = k_codes + ((size_t)unit * pg.tok_stride + pg.tok0 + t0) * (D / 4);
     if (active) {
 #pragma unroll
         for (int m = 0; m < kGroup / 8; ++m)
@@ -256,17 +261,16 @@ __device__ __forceinline__ void pack_keys_full(
 
 template <typename T, int D>
 __device__ __forceinline__ void pack_values_full(
-    const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, int n_keep, int Hkv,
+    const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int Hkv,
     uint8_t* __restrict__ v_codes, uint32_t* __restrict__ v_sz) {
     const int gi = blockIdx.x;
     const int unit = blockIdx.z * Hkv + blockIdx.y;
     const int lane = threadIdx.x % kWave;
     const bool active = lane < D / 2;
     const int c = 2 * (active ? lane : 0);
-    const int G = (n_keep + kGroup - 1) / kGroup;
     const int t0 = gi * kGroup;
     Pair x[kGroup];
-    gather_full<T, D>(v, idx, T_ctx, n_keep, unit, t0, c, x);
+    gather_full<T, D>(v, idx, T_ctx, pg.idx_stride, unit, t0, c, x);
     // Token t's parameter word of row lane / 16 is kept by the lane with lane % 16 == t % 16.
     uint32_t wa[2] = {0u, 0u}, wb[2] = {0u, 0u}, vw[2] = {0u, 0u};
 #pragma unroll
@@ -279,10 +283,10 @@ __device__ __forceinline__ void pack_values_full(
         vw[t / 16] = (lane & 15) == (t & 15) ? p.word : vw[t / 16];
     }
     if (active) {
-        *reinterpret_cast<uint4*>(v_codes + (((size_t)unit * G + gi) * D + c) * 8) = make_uint4(wa[0], wa[1], wb[0], wb[1]);
+        *reinterpret_cast<uint4*>(v_codes + (((size_t)unit * pg.grp_stride + pg.tok0 / kGroup + gi) * D + c) * 8) = make_uint4(wa[0], wa[1], wb[0], wb[1]);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            v_sz[((size_t)unit * n_keep + t0 + 16 * h + (lane & 15)) * (D / 32) + (lane >> 4)] = vw[h];
+            v_sz[((size_t)unit * pg.tok_stride + pg.tok0 + t0 + 16 * h + (lane & 15)) * (D / 32) + (lane >> 4)] = vw[h];
     }
 }
 
@@ -290,27 +294,38 @@ __device__ __forceinline__ void pack_values_full(
 // the keys, wave 1 the values.
 template <typename T, int D>
 __global__ __launch_bounds__(128) void quant_pack_kernel(
-    const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, int n_keep,
+    const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, PackGeom pg,
     int Hkv, uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz, uint8_t* __restrict__ v_codes,
     uint32_t* __restrict__ v_sz) {
-    const bool full = (blockIdx.x + 1) * kGroup <= n_keep;
+    const bool full = (blockIdx.x + 1) * kGroup <= pg.n;
     if (threadIdx.x < kWave) {
-        if (full) pack_keys_full<T, D>(k, idx, T_ctx, n_keep, Hkv, k_codes, k_sz);
-        else pack_keys<T, D>(k, idx, T_ctx, n_keep, Hkv, k_codes, k_sz);
+        if (full) pack_keys_full<T, D>(k, idx, T_ctx, pg, Hkv, k_codes, k_sz);
+        else pack_keys<T, D>(k, idx, T_ctx, pg, Hkv, k_codes, k_sz);
     } else {
-        if (full) pack_values_full<T, D>(v, idx, T_ctx, n_keep, Hkv, v_codes, v_sz);
-        else pack_values<T, D>(v, idx, T_ctx, n_keep, Hkv, v_codes, v_sz);
+        if (full) pack_values_full<T, D>(v, idx, T_ctx, pg, Hkv, v_codes, v_sz);
+        else pack_values<T, D>(v, idx, T_ctx, pg, Hkv, v_codes, v_sz);
     }
 }
 
 template <typename T, int D>
 hipError_t launch_typed(const void* k, const void* v, const int32_t* idx, int B, int Hkv, int T_ctx,
-                        int n_keep, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes, uint32_t* v_sz,
+                        const PackGeom& pg, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes, uint32_t* v_sz,
                         hipStream_t stream) {
-    const int G = (n_keep + kGroup - 1) / kGroup;
+    const int G = (pg.n + kGroup - 1) / kGroup;
     hipLaunchKernelGGL((quant_pack_kernel<T, D>), dim3(G, Hkv, B), dim3(128), 0, stream, static_cast<const T*>(k),
-                       static_cast<const T*>(v), idx, T_ctx, n_keep, Hkv, k_codes, k_sz, v_codes, v_sz);
+                       static_cast<const T*>(v), idx, T_ctx, pg, Hkv, k_codes, k_sz, v_codes, v_sz);
     return hipGetLastError();
+}
+
+hipError_t launch_geom(const void* k, const void* v, bool bf16, const int32_t* idx, int B, int Hkv, int T_ctx,
+                       int D, const PackGeom& pg, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes,
+                       uint32_t* v_sz, hipStream_t stream) {
+    if (bf16) {
+        if (D == 128) return launch_typed<uint16_t, 128>(k, v, idx, B, Hkv, T_ctx, pg, k_codes, k_sz, v_codes, v_sz, stream);
+        return launch_typed<uint16_t, 64>(k, v, idx, B, Hkv, T_ctx, pg, k_codes, k_sz, v_codes, v_sz, stream);
+    }
+    if (D == 128) return launch_typed<float, 128>(k, v, idx, B, Hkv, T_ctx, pg, k_codes, k_sz, v_codes, v_sz, stream);
+    return launch_typed<float, 64>(k, v, idx, B, Hkv, T_ctx, pg, k_codes, k_sz, v_codes, v_sz, stream);
 }
 
 }  // namespace
@@ -318,12 +333,15 @@ hipError_t launch_typed(const void* k, const void* v, const int32_t* idx, int B,
 hipError_t launch_quant_pack(const void* k, const void* v, bool bf16, const int32_t* idx, int B,
                              int Hkv, int T_ctx, int D, int n_keep, uint8_t* k_codes, uint32_t* k_sz,
                              uint8_t* v_codes, uint32_t* v_sz, hipStream_t stream) {
-    if (bf16) {
-        if (D == 128) return launch_typed<uint16_t, 128>(k, v, idx, B, Hkv, T_ctx, n_keep, k_codes, k_sz, v_codes, v_sz, stream);
-        return launch_typed<uint16_t, 64>(k, v, idx, B, Hkv, T_ctx, n_keep, k_codes, k_sz, v_codes, v_sz, stream);
-    }
-    if (D == 128) return launch_typed<float, 128>(k, v, idx, B, Hkv, T_ctx, n_keep, k_codes, k_sz, v_codes, v_sz, stream);
-    return launch_typed<float, 64>(k, v, idx, B, Hkv, T_ctx, n_keep, k_codes, k_sz, v_codes, v_sz, stream);
+    const PackGeom pg{n_keep, n_keep, n_keep, (n_keep + kGroup - 1) / kGroup, 0};
+    return launch_geom(k, v, bf16, idx, B, Hkv, T_ctx, D, pg, k_codes, k_sz, v_codes, v_sz, stream);
+}
+
+hipError_t launch_stream_pack(const void* k, const void* v, bool bf16, const int32_t* idx, int idx_stride, int B,
+                              int Hkv, int T_ctx, int D, int n, int cap, int tok0, uint8_t* k_codes,
+                              uint32_t* k_sz, uint8_t* v_codes, uint32_t* v_sz, hipStream_t stream) {
+    const PackGeom pg{n, idx_stride, cap, cap / kGroup, tok0};
+    return launch_geom(k, v, bf16, idx, B, Hkv, T_ctx, D, pg, k_codes, k_sz, v_codes, v_sz, stream);
 }
 
 }  // namespace minikv

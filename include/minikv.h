@@ -156,6 +156,70 @@ int minikv_quant_pack(const void *k, const void *v, int in_dtype, const int32_t 
 int minikv_decode_attn(const void *q, const minikv_packed_t *cache, int Hq, float sm_scale,
                        void *out, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- streaming decode: generated tokens join the cache ----
+ *
+ * Keys are quantised per channel over 32-token groups (method details), so a
+ * key group needs 32 whole tokens.  Streaming layout per (sequence, KV head):
+ *   - a packed region laid out for `cap` tokens (cap a multiple of 32):
+ *       k_codes [B][Hkv][cap][D/4], k_sz [B][Hkv][cap/32][D],
+ *       v_codes [B][Hkv][cap/32][D][8], v_sz [B][Hkv][cap][D/32]
+ *     (the minikv_quant_pack layout with cap in place of n_keep), of which the
+ *     first n_packed tokens (a multiple of 32) are valid;
+ *   - a residual window k_res, v_res bf16 [B][Hkv][32][D] whose first n_res
+ *     (0..31) slots hold tokens kept exactly.
+ * A selection of n_keep tokens starts with its first 32*floor(n_keep/32)
+ * tokens packed (minikv_stream_pack) and the rest in the window
+ * (minikv_stream_append with idx).  Each generated token is appended to the
+ * window; when the window holds 32 tokens the caller packs it at token
+ * n_packed (minikv_stream_pack, idx NULL, T = 32) and empties it.  The caller
+ * owns every buffer and tracks n_packed and n_res (all sequences of a batch
+ * advance together).
+ */
+
+/*
+ * Quantise-and-pack n tokens (n and tok0 multiples of 32, tok0 + n <= cap)
+ * into tokens tok0 .. tok0+n-1 of a streaming layout for cap tokens.  Source:
+ * k, v [B][Hkv][T][D] (in_dtype as for minikv_quant_pack), rows idx[b][g][j]
+ * (int32, row stride idx_stride >= n) or, with idx NULL, rows 0..n-1 (n <= T).
+ * Same rule as minikv_quant_pack; the packed bytes of whole groups do not
+ * depend on where they are placed.
+ * Errors: NULL; SHAPE (sizes < 1, n or tok0 not multiples of 32, tok0 + n > cap,
+ * cap not a multiple of 32, idx_stride < n, n > T with idx NULL);
+ * UNSUPPORTED (D, in_dtype); ALIGN; LAUNCH.
+ */
+int minikv_stream_pack(const void *k, const void *v, int in_dtype, const int32_t *idx, int idx_stride,
+                       int B, int Hkv, int T, int D, int n, int cap, int tok0,
+                       uint8_t *k_codes, uint32_t *k_sz, uint8_t *v_codes, uint32_t *v_sz,
+                       void *stream);
+
+/*
+ * Copy n bf16 tokens into residual slots slot .. slot+n-1 (slot + n <= 32) of
+ * k_res, v_res bf16 [B][Hkv][32][D]: rows idx[b][g][j] (row stride idx_stride)
+ * of k, v bf16 [B][Hkv][T][D], or rows 0..n-1 with idx NULL (a generated token:
+ * T = 1, n = 1).  Errors: NULL; SHAPE; UNSUPPORTED (D); ALIGN; LAUNCH.
+ */
+int minikv_stream_append(const void *k, const void *v, const int32_t *idx, int idx_stride,
+                         int B, int Hkv, int T, int D, int n, int slot,
+                         void *k_res, void *v_res, void *stream);
+
+/*
+ * Single-query decode over a streaming cache: the softmax runs over the
+ * n_packed packed tokens (dequantised in registers, as minikv_decode_attn)
+ * and the n_res residual tokens (exact) together.  q bf16 [B][Hq][D] -> out
+ * bf16 [B][Hq][D].  ws: at least minikv_stream_decode_ws_bytes(...) bytes.
+ * sm_scale <= 0 means 1/sqrt(D).
+ * Errors: NULL; SHAPE (Hq % Hkv, n_packed not a multiple of 32 or > cap,
+ * n_res outside 0..31, n_packed + n_res < 1); UNSUPPORTED (D, Hq/Hkv not 1,
+ * 2 or 4); ALIGN; WORKSPACE; LAUNCH.
+ */
+int minikv_stream_decode(const void *q, int B, int Hq, int Hkv, int D, int cap, int n_packed,
+                         const uint8_t *k_codes, const uint32_t *k_sz, const uint8_t *v_codes,
+                         const uint32_t *v_sz, const void *k_res, const void *v_res, int n_res,
+                         float sm_scale, void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes minikv_stream_decode needs (0 for invalid sizes). */
+size_t minikv_stream_decode_ws_bytes(int B, int Hq, int Hkv, int n_packed, int n_res, int D);
+
 /* ---- host helpers (no GPU work) ---- */
 
 /* Bytes of the packed cache: per (sequence, KV head), G = ceil(n/32):

@@ -120,6 +120,74 @@ def test_decode_validation(L):
     assert f(A, byref(p), 8, 0.0, A, None, need, None) == _lib.ERR_WORKSPACE
 
 
+def test_stream_pack_validation(L):
+    f = L.minikv_stream_pack
+    ok = (A, A, _lib.BF16, A, 96, 2, 4, 256, 128, 64, 128, 32, A, A, A, A, None)
+    args = list(ok)
+
+    def call(**kw):
+        a = list(ok)
+        pos = {"k": 0, "idx": 3, "idx_stride": 4, "T": 7, "D": 8, "n": 9, "cap": 10, "tok0": 11, "k_codes": 12,
+               "dtype": 2}
+        for name, val in kw.items():
+            a[pos[name]] = val
+        return f(*a)
+
+    assert call(k=None) == _lib.ERR_NULL
+    assert call(k_codes=None) == _lib.ERR_NULL
+    assert call(n=48) == _lib.ERR_SHAPE          # not whole groups
+    assert call(tok0=16) == _lib.ERR_SHAPE       # not on a group boundary
+    assert call(cap=80) == _lib.ERR_SHAPE        # capacity not whole groups
+    assert call(tok0=96) == _lib.ERR_SHAPE       # 96 + 64 > 128
+    assert call(idx_stride=32) == _lib.ERR_SHAPE  # index rows shorter than n
+    assert call(idx=None, T=32) == _lib.ERR_SHAPE  # identity rows beyond T
+    assert call(D=96) == _lib.ERR_UNSUPPORTED
+    assert call(dtype=7) == _lib.ERR_UNSUPPORTED
+    assert call(k=MIS) == _lib.ERR_ALIGN
+    assert call(k_codes=MIS) == _lib.ERR_ALIGN
+    assert len(args) == 17
+
+
+def test_stream_append_validation(L):
+    f = L.minikv_stream_append
+    assert f(None, A, None, 1, 2, 4, 1, 128, 1, 0, A, A, None) == _lib.ERR_NULL
+    assert f(A, A, None, 1, 2, 4, 1, 128, 1, 0, None, A, None) == _lib.ERR_NULL
+    assert f(A, A, None, 1, 2, 4, 1, 128, 1, 32, A, A, None) == _lib.ERR_SHAPE   # slot past the window
+    assert f(A, A, A, 20, 2, 4, 600, 128, 8, 28, A, A, None) == _lib.ERR_SHAPE   # 28 + 8 > 32
+    assert f(A, A, A, 4, 2, 4, 600, 128, 8, 0, A, A, None) == _lib.ERR_SHAPE     # idx stride < n
+    assert f(A, A, None, 1, 2, 4, 1, 128, 2, 0, A, A, None) == _lib.ERR_SHAPE    # 2 rows of a 1-row source
+    assert f(A, A, None, 1, 2, 4, 1, 96, 1, 0, A, A, None) == _lib.ERR_UNSUPPORTED
+    assert f(A, MIS, None, 1, 2, 4, 1, 128, 1, 0, A, A, None) == _lib.ERR_ALIGN
+
+
+def test_stream_decode_validation(L):
+    f = L.minikv_stream_decode
+    need = L.minikv_stream_decode_ws_bytes(2, 8, 4, 64, 5, 128)
+    assert need > 0
+    assert L.minikv_stream_decode_ws_bytes(2, 8, 4, 48, 5, 128) == 0   # packed tokens not whole groups
+    assert L.minikv_stream_decode_ws_bytes(2, 8, 4, 64, 32, 128) == 0  # residual holds at most 31
+    assert L.minikv_stream_decode_ws_bytes(2, 8, 4, 0, 0, 128) == 0    # nothing to attend
+
+    def call(q=A, Hq=8, cap=128, n_packed=64, k_codes=A, k_res=A, n_res=5, out=A, ws=A, ws_bytes=need, D=128):
+        return f(q, 2, Hq, 4, D, cap, n_packed, k_codes, A, A, A, k_res, A, n_res, 0.0, out, ws, ws_bytes, None)
+
+    assert call(q=None) == _lib.ERR_NULL
+    assert call(k_codes=None) == _lib.ERR_NULL
+    assert call(k_res=None) == _lib.ERR_NULL
+    assert call(Hq=6) == _lib.ERR_SHAPE
+    assert call(n_packed=48) == _lib.ERR_SHAPE
+    assert call(n_packed=160) == _lib.ERR_SHAPE      # beyond the capacity
+    assert call(n_res=32) == _lib.ERR_SHAPE
+    assert call(n_packed=0, n_res=0) == _lib.ERR_SHAPE
+    assert call(cap=100) == _lib.ERR_SHAPE
+    assert call(Hq=32) == _lib.ERR_UNSUPPORTED        # 8 query heads per KV head
+    assert call(D=96) == _lib.ERR_UNSUPPORTED
+    assert call(q=MIS) == _lib.ERR_ALIGN
+    assert call(k_res=MIS) == _lib.ERR_ALIGN
+    assert call(ws_bytes=need - 4) == _lib.ERR_WORKSPACE
+    assert call(ws=None) == _lib.ERR_WORKSPACE
+
+
 def test_host_budget_helpers_match_oracle(L):
     for T in (1, 7, 256, 4096, 8192, 16384, 44000, 65536):
         for pct in (5, 15, 30, 100):

@@ -1,0 +1,119 @@
+"""GPU parity of streaming decode (generated tokens joining the cache) against the oracle.
+
+A selection starts the cache (whole 32-token groups packed, the rest in the
+exact residual window); generated tokens are appended one per step and every
+32nd packs the window as the next group.  Packed bytes must equal the oracle's
+bit for bit after every flush; decode over packed + residual tokens is within
+max(2e-3, 1 bf16 ulp) of the fp64 oracle at every step.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import bit_quantized_kv_quant_amd as mk
+from gpu_util import assert_attn_close, assert_packed_equal, require_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def stream_packed_np(c):
+    """The valid packed region of a StreamCache as the oracle's packed dict."""
+    n, G = c.n_packed, c.n_packed // 32
+    ksz = c.k_sz[:, :, :G].cpu().numpy().view(np.uint32)
+    vsz = c.v_sz[:, :, :n].cpu().numpy().view(np.uint32)
+    half = lambda w: (w & 0xFFFF).astype(np.uint16).view(np.float16)  # noqa: E731
+    return {"k_codes": c.k_codes[:, :, :n].cpu().numpy(), "k_scale": half(ksz), "k_zero": half(ksz >> 16),
+            "v_codes": c.v_codes[:, :, :G].cpu().numpy(), "v_scale": half(vsz), "v_zero": half(vsz >> 16)}
+
+
+def _inputs(seed, B, Hkv, T, D):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+    k[..., :: D // 4] *= 8.0  # outlier key channels
+    v = rng.standard_normal((B, Hkv, T, D)).astype(np.float32) * 0.5
+    return rng, synth.bf16_round(k), synth.bf16_round(v)
+
+
+def _check_state(c, st):
+    assert c.n_packed == st["packed"]["k_codes"].shape[2] and c.n_res == st["k_res"].shape[2]
+    if c.n_packed:
+        assert_packed_equal(stream_packed_np(c), st["packed"])
+    if c.n_res:
+        assert np.array_equal(to_np(c.k_res[:, :, :c.n_res]), st["k_res"])
+        assert np.array_equal(to_np(c.v_res[:, :, :c.n_res]), st["v_res"])
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,n_sel,steps", [(2, 2, 128, 150, 45), (8, 2, 128, 614, 40), (4, 4, 64, 20, 50)])
+def test_stream_generation_matches_oracle(dev, Hq, Hkv, D, n_sel, steps):
+    say("stream Hq", Hq, "Hkv", Hkv, "D", D, "selection", n_sel, "steps", steps)
+    B, T = 2, 700
+    rng, k, v = _inputs(n_sel, B, Hkv, T, D)
+    idx = np.sort(np.stack([[rng.choice(T, n_sel, replace=False) for _ in range(Hkv)] for _ in range(B)]), -1)
+    kd = torch.from_numpy(k).to(dev).to(torch.bfloat16)
+    vd = torch.from_numpy(v).to(dev).to(torch.bfloat16)
+    idd = torch.from_numpy(idx.astype(np.int32)).to(dev)
+    cap = 32 * ((n_sel + steps) // 32 + 1)
+    c = mk.StreamCache.alloc(B, Hkv, cap, D, dev).init(kd, vd, idd)
+    st = oracle.stream_init_ref(k, v, idx)
+    torch.cuda.synchronize()
+    _check_state(c, st)
+    flushes = 0
+    for step in range(steps):
+        kn = synth.bf16_round(rng.standard_normal((B, Hkv, D)).astype(np.float32))
+        vn = synth.bf16_round(rng.standard_normal((B, Hkv, D)).astype(np.float32) * 0.5)
+        before = c.n_packed
+        c.append(torch.from_numpy(kn).to(dev).to(torch.bfloat16), torch.from_numpy(vn).to(dev).to(torch.bfloat16))
+        st = oracle.stream_append_ref(st, kn, vn)
+        q = synth.bf16_round(rng.standard_normal((B, Hq, D)).astype(np.float32))
+        out = c.decode(torch.from_numpy(q).to(dev).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        if c.n_packed != before:
+            flushes += 1
+            _check_state(c, st)
+        assert_attn_close(to_np(out), oracle.stream_decode_ref(q, st), f"stream decode step {step}")
+    _check_state(c, st)
+    assert flushes == (n_sel % 32 + steps) // 32
+
+
+def test_stream_decode_without_residual_equals_packed_decode(dev):
+    say("stream decode, whole groups only, vs decode_attn")
+    B, Hq, Hkv, T, D = 4, 8, 2, 1000, 128
+    rng, k, v = _inputs(3, B, Hkv, T, D)
+    idx = np.sort(np.stack([[rng.choice(T, 256, replace=False) for _ in range(Hkv)] for _ in range(B)]), -1)
+    kd = torch.from_numpy(k).to(dev).to(torch.bfloat16)
+    vd = torch.from_numpy(v).to(dev).to(torch.bfloat16)
+    idd = torch.from_numpy(idx.astype(np.int32)).to(dev)
+    c = mk.StreamCache.alloc(B, Hkv, 512, D, dev).init(kd, vd, idd)
+    assert c.n_res == 0 and c.n_packed == 256
+    q = torch.from_numpy(synth.bf16_round(rng.standard_normal((B, Hq, D)).astype(np.float32))).to(dev).to(torch.bfloat16)
+    a = c.decode(q)
+    b = mk.decode_attn(q, mk.quant_pack(kd, vd, idd))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_stream_residual_only(dev):
+    say("stream decode, residual tokens only")
+    B, Hq, Hkv, T, D = 3, 4, 4, 100, 128
+    rng, k, v = _inputs(4, B, Hkv, T, D)
+    idx = np.sort(np.stack([[rng.choice(T, 17, replace=False) for _ in range(Hkv)] for _ in range(B)]), -1)
+    kd = torch.from_numpy(k).to(dev).to(torch.bfloat16)
+    vd = torch.from_numpy(v).to(dev).to(torch.bfloat16)
+    c = mk.StreamCache.alloc(B, Hkv, 64, D, dev).init(kd, vd, torch.from_numpy(idx.astype(np.int32)).to(dev))
+    assert c.n_packed == 0 and c.n_res == 17
+    q = synth.bf16_round(rng.standard_normal((B, Hq, D)).astype(np.float32))
+    out = c.decode(torch.from_numpy(q).to(dev).to(torch.bfloat16))
+    torch.cuda.synchronize()
+    assert_attn_close(to_np(out), oracle.stream_decode_ref(q, oracle.stream_init_ref(k, v, idx)), "residual only")
