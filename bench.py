@@ -22,7 +22,10 @@ budget 30 % -> 5 %) at a batch that fills about 227 GB of HBM, and the
 Mistral-7B-shaped GQA cache (32 layers, 32 / 8 heads, 6600 kept tokens of a
 44000-token prompt, batch 4).  A decode step there is one query per sequence
 through every layer; kept-token K/V are drawn directly from the workload's
-distributions and packed by the library.  Then two single-layer prefill lines
+distributions and packed by the library.  The Mistral-shaped cache is also run
+as generation (decode_stream): 256 steps, each appending one new token per
+layer to a streaming cache (every 32nd packs the residual window) and decoding
+through all 32 layers.  Then two single-layer prefill lines
 (1 x 32 heads x 16384 tokens, and one layer of the Mistral-7B-shaped GQA
 prompt, 4 x 32 / 8 heads x 44000 tokens): passes 1 and 2, selection and
 packing, each timed alone.
@@ -146,6 +149,50 @@ def prefill_layer(torch, mk, synth, wl, reps):
     del q, k, v, o, lse, scores, idx, cache
     torch.cuda.empty_cache()
     return res
+
+
+def decode_stream(torch, mk, synth, wl, steps):
+    """Generation over a streaming cache per layer: each step appends one token per
+    (sequence, KV head) to every layer (packing every 32nd) and decodes one query per
+    sequence through all layers.  Kept-token K/V of the prompt are drawn directly."""
+    dev = torch.device("cuda:0")
+    B, n = wl.B, mk.keep_count(wl.T, wl.budget_pct)
+    cap = 32 * ((n + steps) // 32 + 1)
+    caches = []
+    for l in range(wl.layers):
+        k, v = synth.make_kept_kv(wl, n, dev, seed=wl.seed * 100000 + l * 1000 + 7, B=B)
+        idx = torch.arange(n, dtype=torch.int32, device=dev).expand(B, wl.Hkv, n).contiguous()
+        caches.append(mk.StreamCache.alloc(B, wl.Hkv, cap, wl.D, dev).init(k, v, idx))
+        del k, v, idx
+    g = torch.Generator(device=dev).manual_seed(wl.seed * 31 + 5)
+    pool = 8  # distinct new tokens / queries, cycled
+    kn = [torch.randn((B, wl.Hkv, wl.D), generator=g, device=dev).to(torch.bfloat16) for _ in range(pool)]
+    vn = [torch.randn((B, wl.Hkv, wl.D), generator=g, device=dev).to(torch.bfloat16) for _ in range(pool)]
+    qs = [synth.make_decode_q(wl, dev, step=i, B=B) for i in range(pool)]
+    out = torch.empty_like(qs[0])
+    ws = torch.empty(max(16, max(mk.decode_ws_bytes(B, wl.Hq, wl.Hkv, cap, wl.D), 1) * 2), dtype=torch.uint8,
+                     device=dev)
+    res0 = caches[0].n_res
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for s in range(steps):
+        for c in caches:
+            c.append(kn[s % pool], vn[s % pool])
+            c.decode(qs[s % pool], out=out, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / steps
+    packed_bytes = sum(mk.packed_bytes(B, wl.Hkv, c.n_packed, wl.D) for c in caches)
+    flushes = (res0 + steps) // 32
+    del caches
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "batch": B, "layers": wl.layers, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+            "prompt_kept_tokens": n, "steps": steps, "packs_per_layer": flushes,
+            "packed_GB_at_end": packed_bytes / 1e9, "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3),
+            "host_ms_per_step": wall * 1e3 / steps}
 
 
 class StageTimer:
@@ -379,6 +426,10 @@ def main():
         budgets = [mk.keep_count(gw.T, gw.budget_pct)] * gw.layers
         res["decode_gqa"] = decode_layers(torch, mk, synth, gw, gw.B, budgets, reps=20)
         print(f"# gqa decode: {json.dumps(res['decode_gqa'])}", file=sys.stderr, flush=True)
+    if not args.no_gqa_sweep:
+        gw = synth.WORKLOADS["mistral_44k"]
+        res["decode_stream"] = decode_stream(torch, mk, synth, gw, gw.decode_steps)
+        print(f"# streaming decode: {json.dumps(res['decode_stream'])}", file=sys.stderr, flush=True)
     if not args.no_prefill_sweep:
         res["prefill_16k"] = prefill_layer(torch, mk, synth, synth.WORKLOADS["prefill_16k"], reps=10)
         print(f"# prefill 16k: {json.dumps(res['prefill_16k'])}", file=sys.stderr, flush=True)
