@@ -95,15 +95,39 @@ def decode_layers(torch, mk, synth, wl, B, budgets, reps=3, chunk=64):
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / reps
+    # The same step replayed as one HIP graph (how a serving loop issues it): no
+    # per-call host work between the layers' launches.
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in caches:
+            mk.decode_attn(q, c, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        for c in caches:
+            mk.decode_attn(q, c, out=out, ws=ws)
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    gms = ev0.elapsed_time(ev1) / reps
+    del graph
     cache_bytes = sum(c.nbytes() for c in caches)
     qo_bytes = 2 * B * wl.Hq * wl.D * 2 * len(caches)
     gbs = (cache_bytes + qo_bytes) / (ms * 1e-3) / 1e9
+    ggbs = (cache_bytes + qo_bytes) / (gms * 1e-3) / 1e9
     del caches
     torch.cuda.empty_cache()
     return {"workload": wl.name, "batch": B, "layers": len(budgets), "q_heads": wl.Hq, "kv_heads": wl.Hkv,
             "kept_tokens_first_last": [int(budgets[0]), int(budgets[-1])], "packed_GB": cache_bytes / 1e9,
             "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3), "achieved_GBs": gbs,
-            "hbm_frac": gbs / PEAK_HBM_GBS}
+            "hbm_frac": gbs / PEAK_HBM_GBS,
+            "graph_ms_per_step": gms, "graph_tokens_per_s": B / (gms * 1e-3), "graph_achieved_GBs": ggbs,
+            "graph_hbm_frac": ggbs / PEAK_HBM_GBS}
 
 
 def prefill_layer(torch, mk, synth, wl, reps):

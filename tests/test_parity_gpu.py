@@ -393,3 +393,41 @@ def test_gqa_44k_chain_sampled(dev):
     got = packed_to_np(cache)
     assert_packed_equal(got, oracle.quant_pack_ref(to_np(k), to_np(v), idx_np))
     assert_attn_close(to_np(out), oracle.decode_ref(to_np(qdec), got), "gqa decode")
+
+
+def test_decode_graph_replay_matches_eager(dev):
+    """Decode through several layers captured as one HIP graph: every replay,
+    with eager work on the stream between replays, equals the eager result."""
+    say("decode: graph capture of 4 layers, 3 replays")
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, D = 2, 8, 2, 128
+    caches = []
+    for n in (300, 257, 64, 1000):
+        k = torch.from_numpy(synth.bf16_round(rng.standard_normal((B, Hkv, n, D)).astype(np.float32))).to(dev)
+        v = torch.from_numpy(synth.bf16_round(rng.standard_normal((B, Hkv, n, D)).astype(np.float32))).to(dev)
+        caches.append(mk.quant_pack(k.to(torch.bfloat16), v.to(torch.bfloat16)))
+    q = torch.from_numpy(synth.bf16_round(rng.standard_normal((B, Hq, D)).astype(np.float32))).to(dev).to(torch.bfloat16)
+    outs = [torch.empty_like(q) for _ in caches]
+    ws = torch.empty(max(mk.decode_ws_bytes(B, Hq, Hkv, c.n_keep, D) for c in caches) + 16, dtype=torch.uint8, device=dev)
+    for c, o in zip(caches, outs):
+        mk.decode_attn(q, c, out=o, ws=ws)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c, o in zip(caches, outs):
+            mk.decode_attn(q, c, out=o, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        for c, o in zip(caches, outs):
+            mk.decode_attn(q, c, out=o, ws=ws)
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        mk.decode_attn(q, caches[3], out=torch.empty_like(q), ws=torch.empty_like(ws))  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, e), f"replay {rep}, layer {i}"
