@@ -28,7 +28,12 @@ layer to a streaming cache (every 32nd packs the residual window) and decoding
 through all 32 layers.  Then two single-layer prefill lines
 (1 x 32 heads x 16384 tokens, and one layer of the Mistral-7B-shaped GQA
 prompt, 4 x 32 / 8 heads x 44000 tokens): passes 1 and 2, selection and
-packing, each timed alone.
+packing, each timed alone.  Before the sweeps, the cache policies of the
+pages' comparison tables run on the chain's prompt (variants): KIVI-like
+(every token at 2 bits), H2O-like (scores from every prompt row), MiniKV
+(32-row window, 15 %) and MiniKV Pyramid (30 % -> 5 % over 32 layers), each
+with its compression, compress / decode time and decode error against exact
+attention over the full 16-bit cache.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -59,6 +64,8 @@ def parse():
     ap.add_argument("--pyramid-batch", type=int, default=1024,
                     help="batch of the 40-layer pyramid decode sweep (1024 fills about 227 GB; 0 skips it)")
     ap.add_argument("--no-gqa-sweep", action="store_true", help="skip the 32-layer GQA decode sweep")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the comparison of cache policies (KIVI-like, H2O-like, MiniKV, Pyramid)")
     ap.add_argument("--no-prefill-sweep", action="store_true",
                     help="skip the single-layer prefill lines (1 x 32 x 16384 and the 44k-token GQA layer)")
     return ap.parse_args()
@@ -218,6 +225,86 @@ def decode_stream(torch, mk, synth, wl, steps):
             "packed_GB_at_end": packed_bytes / 1e9, "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3),
             "host_ms_per_step": wall * 1e3 / steps}
 
+
+
+def _attn_full_ref(torch, qd, k, v, idx=None):
+    """fp32 single-query attention over bf16 K/V (all tokens, or the selection idx): the
+    error reference for the policy comparison (16-bit storage has no kernel here)."""
+    B, Hq, D = qd.shape
+    r = Hq // k.shape[1]
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=qd.device)
+    for b in range(B):
+        kb, vb = k[b].float(), v[b].float()
+        if idx is not None:
+            ib = idx[b].long()[..., None].expand(-1, -1, D)
+            kb, vb = kb.gather(1, ib), vb.gather(1, ib)
+        kb, vb = kb.repeat_interleave(r, 0), vb.repeat_interleave(r, 0)
+        logits = (qd[b].float()[:, None, :] * kb).sum(-1) * D ** -0.5
+        p = torch.softmax(logits, -1)
+        out[b] = (p[..., None] * vb).sum(1)
+    return out
+
+
+def _rel_l2(torch, got, ref):
+    e = (got.float() - ref).norm(dim=-1) / ref.norm(dim=-1).clamp_min(1e-30)
+    return {"mean": float(e.mean()), "max": float(e.max())}
+
+
+def variants_compare(torch, mk, q, k, v, qd, n_layers, label, reps=3):
+    """The comparison-table policies on one prompt (q, k, v) and one decode query qd.
+
+    Per policy, averaged over the per-layer plans of an n_layers model (the same
+    synthetic layer stands in for every layer): kept tokens, packed bytes over
+    the 16-bit K/V bytes, time of compress() (pass 1, pass 2 with the policy's
+    window, selection, pack) and of decode, and the decode output's relative L2
+    error per (sequence, head) against exact attention over the full 16-bit
+    cache.  Evicting policies also report the same selection held at 16 bits
+    (eviction alone, as H2O / SnapKV store it), computed in fp32 torch.
+    """
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    full = _attn_full_ref(torch, qd, k, v)
+    bf16_bytes = 2 * B * Hkv * T * D * 2
+    res = {}
+    for name in mk.POLICIES:
+        layers = range(n_layers) if mk.POLICIES[name].schedule == "pyramid" else [0]
+        rows = []
+        for layer in layers:
+            _, n_keep, _, _ = mk.layer_plan(name, T, n_layers, layer)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            mk.compress(q, k, v, name, n_layers, layer)
+            ev[0].record()
+            for _ in range(reps):
+                _, idx, cache = mk.compress(q, k, v, name, n_layers, layer)
+            ev[1].record()
+            for _ in range(reps):
+                out = mk.decode_attn(qd, cache)
+            ev[2].record()
+            torch.cuda.synchronize()
+            row = {"n_keep": n_keep, "packed_share": cache.nbytes() / bf16_bytes,
+                   "compress_ms": ev[0].elapsed_time(ev[1]) / reps,
+                   "decode_ms": ev[1].elapsed_time(ev[2]) / reps,
+                   "err_2bit": _rel_l2(torch, out, full)}
+            if idx is not None:
+                row["err_16bit_same_selection"] = _rel_l2(torch, _attn_full_ref(torch, qd, k, v, idx), full)
+            rows.append(row)
+            del cache, idx, out
+        n = len(rows)
+        agg = {"layers_averaged": n,
+               "n_keep_mean": sum(r_["n_keep"] for r_ in rows) / n,
+               "compression": 1.0 - sum(r_["packed_share"] for r_ in rows) / n,
+               "compress_ms": sum(r_["compress_ms"] for r_ in rows) / n,
+               "decode_ms": sum(r_["decode_ms"] for r_ in rows) / n,
+               "err_2bit_mean": sum(r_["err_2bit"]["mean"] for r_ in rows) / n,
+               "err_2bit_max": max(r_["err_2bit"]["max"] for r_ in rows)}
+        if "err_16bit_same_selection" in rows[0]:
+            agg["err_16bit_same_selection_mean"] = sum(r_["err_16bit_same_selection"]["mean"] for r_ in rows) / n
+        res[name] = agg
+    torch.cuda.empty_cache()
+    return {"workload": label, "batch": B, "q_heads": Hq,
+            "kv_heads": Hkv, "context": T, "head_dim": D, "layers_in_plan": n_layers,
+            "error": "relative L2 of the decode output per (sequence, head) vs exact attention over all T "
+                     "16-bit tokens", "policies": res}
 
 class StageTimer:
     """HIP events around each call on the current stream; per-stage totals in ms."""
@@ -437,8 +524,21 @@ def main():
                    "rotation_bytes": n_rot * cache_bytes},
         "output_tokens_per_s": B / (ms_per_step * 1e-3),
     }
+    # ---- cache policies of the comparison tables on this prompt (32-layer plans) ----
+    del o, lse, scores, idx, cache, out, ws
+    torch.cuda.empty_cache()
+    if not args.no_variants:
+        res["variants"] = {"iid": variants_compare(
+            torch, mk, q, k, v, qdec, 32, "llama7b_decode prompt (iid Gaussian, outlier key channels), "
+            "one decode query per sequence")}
+        qh, kh, vh, qdh = synth.make_heavy_qkv(wl, dev)
+        res["variants"]["heavy_hitters"] = variants_compare(
+            torch, mk, qh, kh, vh, qdh, 32, "llama7b_decode shape, 5 % of keys and every query share a "
+            "direction (strength 7): attention concentrated on heavy hitters")
+        del qh, kh, vh, qdh
+        print(f"# variants: {json.dumps(res['variants'])}", file=sys.stderr, flush=True)
     # ---- multi-layer decode sweeps (the chain's buffers are released first) ----
-    del q, k, v, o, lse, scores, idx, cache, out, ws, qdec
+    del q, k, v, qdec
     torch.cuda.empty_cache()
     if args.pyramid_batch > 0:
         pw = synth.WORKLOADS["llama13b_pyramid"]

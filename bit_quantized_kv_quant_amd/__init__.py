@@ -22,3 +22,4 @@ from .api import (  # noqa: F401
     select_topk,
     split_heavy_recent,
 )
+from .variants import POLICIES, Policy, compress, layer_plan  # noqa: F401

@@ -16,6 +16,7 @@ from .workloads import (  # noqa: F401
     tiny_inputs,
     torch_generator,
     make_qkv,
+    make_heavy_qkv,
     make_decode_q,
     make_kept_kv,
     outlier_channels,

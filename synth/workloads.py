@@ -154,6 +154,37 @@ def make_kept_kv(wl, n_keep, device, seed, B=None):
     return k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
+
+def make_heavy_qkv(wl, device, heavy_frac=0.05, strength=7.0, seed=None):
+    """Seeded bf16 q [B,Hq,T,D], k, v [B,Hkv,T,D] and decode queries [B,Hq,D] whose
+    attention concentrates on a few positions (heavy hitters).
+
+    As make_qkv, plus: per (sequence, KV head) a random unit direction u and a
+    random ``heavy_frac`` share of the positions.  Those keys and every query
+    row (prompt and decode) of the heads that share the KV head get
+    ``strength * u`` added, so the marked keys draw a large share of every
+    row's attention.  Random draws only; which positions are marked is not an
+    input of the method.
+    """
+    import torch
+
+    s = (wl.seed if seed is None else seed) * 1000 + 900
+    q, k, v, _ = make_qkv(wl, device, seed=s, dtype=torch.float32)
+    g = torch_generator(device, s + 1)
+    B, Hkv, T, D = k.shape
+    r = wl.Hq // Hkv
+    u = torch.randn((B, Hkv, D), generator=g, device=device, dtype=torch.float32)
+    u = u / u.norm(dim=-1, keepdim=True)
+    n_heavy = max(1, int(heavy_frac * T))
+    pos = torch.rand((B, Hkv, T), generator=g, device=device).argsort(-1)[..., :n_heavy]
+    mark = torch.zeros((B, Hkv, T), device=device, dtype=torch.float32).scatter_(-1, pos, 1.0)
+    k = k + strength * mark[..., None] * u[:, :, None, :]
+    uq = u.repeat_interleave(r, 1)
+    q = q + strength * uq[:, :, None, :]
+    qd = torch.randn((B, wl.Hq, D), generator=g, device=device, dtype=torch.float32) + strength * uq
+    bf = torch.bfloat16
+    return q.to(bf), k.to(bf), v.to(bf), qd.to(bf)
+
 def bf16_round(x):
     """Round fp32 numpy values to bf16 (nearest even) and return them as fp32."""
     import torch

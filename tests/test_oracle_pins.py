@@ -380,6 +380,29 @@ def test_window_scores_sum_tiny_workload():
     assert (sc >= 0).all()
 
 
+
+@pytest.mark.parametrize("T,W", [(40, 40), (40, 9), (1, 1), (17, 1)])
+def test_window_scores_uniform_logits_closed_form(T, W):
+    """q = 0 makes every causal row uniform: row i gives each key j <= i exactly 1/(i+1).
+
+    Key j then collects, per query head, sum_{i = max(j, T-W)}^{T-1} 1/(i+1); with
+    W = T (every prompt row, the cumulative mass) that is H_T - H_j in harmonic
+    numbers.  Two query heads share each KV head here.
+    """
+    rng = np.random.default_rng(T * 100 + W)
+    q = np.zeros((1, 4, T, 8))
+    k = rng.standard_normal((1, 2, T, 8)) * 3
+    sc = oracle.window_scores_ref(q, k, W)
+    harmonic = [Fraction(0)]
+    for n in range(1, T + 1):
+        harmonic.append(harmonic[-1] + Fraction(1, n))
+    for j in range(T):
+        lo = max(j, T - W)
+        expect = 2 * (harmonic[T] - harmonic[lo])
+        assert sc[0, 0, j] == pytest.approx(float(expect), rel=1e-13, abs=1e-15)
+        assert sc[0, 1, j] == pytest.approx(float(expect), rel=1e-13, abs=1e-15)
+
+
 # ---------------------------------------------------------------------------
 # Selection: brute force over subsets, special cases
 # ---------------------------------------------------------------------------
