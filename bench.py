@@ -139,7 +139,8 @@ def decode_layers(torch, mk, synth, wl, B, budgets, reps=3, chunk=64):
 
 def prefill_layer(torch, mk, synth, wl, reps):
     """One layer of a prefill workload through the chain's first four steps,
-    each timed alone (HIP events, `reps` calls after one warm-up call)."""
+    each timed alone (HIP events, `reps` calls after one warm-up call), and the
+    single-pass call (window scores from inside pass 1) where it applies."""
     dev = torch.device("cuda:0")
     q, k, v, _ = synth.make_qkv(wl, dev)
     B, Hq, T, D = q.shape
@@ -157,6 +158,9 @@ def prefill_layer(torch, mk, synth, wl, reps):
         "select_topk": lambda: mk.select_topk(scores, n_heavy, n_recent, idx=idx),
         "quant_pack": lambda: mk.quant_pack(k, v, idx, out=cache),
     }
+    if mk.prefill_fuses_scores(B, T, Hq, Hkv, wl.window):  # single pass: both in one launch
+        calls["prefill_attn_scores"] = lambda: mk.prefill_attn_scores(q, k, v, wl.window, o=o, lse=lse,
+                                                                      scores=scores)
     ms = {}
     for name, fn in calls.items():
         fn()
@@ -415,16 +419,22 @@ def main():
     out = torch.empty_like(qdec)
     ws = torch.empty(mk.decode_ws_bytes(B, Hq, Hkv, n_keep, D), dtype=torch.uint8, device=dev)
 
-    stages = ["prefill_attn", "window_scores", "select_topk", "quant_pack", "decode_attn"]
+    # single pass: the window scores come out of the pass-1 kernel (one launch)
+    fused = mk.prefill_fuses_scores(B, T, Hq, Hkv, W)
+    stages = (["prefill_attn_scores"] if fused else ["prefill_attn", "window_scores"]) + \
+        ["select_topk", "quant_pack", "decode_attn"]
     timer = StageTimer(torch, stages)
 
     def step(t=None):
         if t:
             t.mark()
-        mk.prefill_attn(q, k, v, o=o, lse=lse)
-        if t:
-            t.mark()
-        mk.window_scores(q, k, lse, W, scores=scores)
+        if fused:
+            mk.prefill_attn_scores(q, k, v, W, o=o, lse=lse, scores=scores)
+        else:
+            mk.prefill_attn(q, k, v, o=o, lse=lse)
+            if t:
+                t.mark()
+            mk.window_scores(q, k, lse, W, scores=scores)
         if t:
             t.mark()
         mk.select_topk(scores, n_heavy, n_recent, idx=idx)
@@ -454,6 +464,26 @@ def main():
     per_stage = timer.totals(args.steps)
     print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
           file=sys.stderr, flush=True)
+
+    # ---- the two passes as separate launches, for comparison ----
+    two_pass = {}
+    if fused:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        reps2 = 5
+        for _ in range(2):
+            mk.prefill_attn(q, k, v, o=o, lse=lse)
+            mk.window_scores(q, k, lse, W, scores=scores)
+        ev[0].record()
+        for _ in range(reps2):
+            mk.prefill_attn(q, k, v, o=o, lse=lse)
+        ev[1].record()
+        for _ in range(reps2):
+            mk.window_scores(q, k, lse, W, scores=scores)
+        ev[2].record()
+        torch.cuda.synchronize()
+        two_pass = {"prefill_attn_ms": ev[0].elapsed_time(ev[1]) / reps2,
+                    "window_scores_ms": ev[1].elapsed_time(ev[2]) / reps2}
+        two_pass["sum_ms"] = two_pass["prefill_attn_ms"] + two_pass["window_scores_ms"]
 
     # ---- decode alone, rotating over >= 1 GB of distinct packed caches ----
     cache_bytes = cache.nbytes()
@@ -491,7 +521,9 @@ def main():
 
     # ---- roofline of the dominant kernel (prefill pass 1, MFMA-bound) ----
     flops = 2.0 * D * T * (T + 1) * Hq * B   # causal pairs only: QK^T and PV
-    k1_ms = per_stage["prefill_attn"]
+    if fused:  # plus the window rows' QK^T of the score pass (causal pairs)
+        flops += 2.0 * D * (W * T - W * (W - 1) / 2) * Hq * B
+    k1_ms = per_stage["prefill_attn_scores" if fused else "prefill_attn"]
     achieved = flops / (k1_ms * 1e-3) / 1e12
     tokens_per_step = B * (T + 1)
     value = tokens_per_step / (ms_per_step * 1e-3)
@@ -512,13 +544,16 @@ def main():
         "config": {"workload": "llama7b_decode chain: prefill + window scores + select + 2-bit pack + decode",
                    "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "context": T, "window": W,
                    "n_keep": n_keep, "n_heavy": n_heavy, "n_recent": n_recent, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "prefill_attn (fa_fwd_kernel)", "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": "fa_fwd_kernel (pass 1" + (" with the window scores)" if fused else ")"),
+                     "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": load_traffic(os.path.join(ROOT, "profiles", "fa_fwd_llama7b_hbm_traffic.md"),
                                              os.path.join(ROOT, "bit_quantized_kv_quant_amd", "csrc",
                                                           "prefill.hip")),
                      "flops_per_launch": flops},
         "stages_ms": per_stage,
+        "single_pass_scores": fused,
+        "two_pass_ms": two_pass or None,
         "decode": {"tokens_per_s": B / (dec_ms * 1e-3), "ms": dec_ms, "bytes": dec_bytes,
                    "achieved_GBs": dec_gbs, "hbm_frac": dec_gbs / PEAK_HBM_GBS, "rotated_caches": n_rot,
                    "rotation_bytes": n_rot * cache_bytes},

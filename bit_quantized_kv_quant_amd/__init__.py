@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     packed_bytes,
     prefill_attn,
     prefill_attn_scores,
+    prefill_fuses_scores,
     window_scores,
     pyramid_keep,
     quant_pack,

@@ -46,6 +46,7 @@ SIGNATURES = {
     "minikv_prefill_attn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]),
     "minikv_window_scores": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _vp]),
     "minikv_prefill_attn_scores": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp]),
+    "minikv_prefill_fuses_scores": (_i, [_i, _i, _i, _i, _i]),
     "minikv_select_topk": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "minikv_quant_pack": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(PackedT), _vp]),
     "minikv_decode_attn": (_i, [_vp, ctypes.POINTER(PackedT), _i, _f, _vp, _vp, _sz, _vp]),

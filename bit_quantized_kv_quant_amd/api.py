@@ -123,6 +123,11 @@ def prefill_attn_scores(q, k, v, window, sm_scale=None, with_o=True, o=None, lse
     return o, lse, scores
 
 
+def prefill_fuses_scores(B, T, Hq, Hkv, window):
+    """True where prefill_attn_scores runs as one launch (scores from inside pass 1)."""
+    return bool(_lib.lib().minikv_prefill_fuses_scores(int(B), int(T), int(Hq), int(Hkv), int(window)))
+
+
 def select_topk(scores, n_heavy, n_recent, idx=None):
     B, Hkv, T = scores.shape
     _need(scores, torch.float32, (B, Hkv, T), "scores")

@@ -90,8 +90,8 @@ int minikv_prefill_attn(const void* q, const void* k, const void* v, int B, int 
     const int st = check_prefill_args(q, k, v, B, T, Hq, Hkv, D);
     if (st != MINIKV_OK) return st;
     if (misaligned(lse) || (o && misaligned(o))) return MINIKV_ERR_ALIGN;
-    return status_of(minikv::launch_prefill(q, k, v, B, T, Hq, Hkv, D, resolve_scale(sm_scale, D), o, lse,
-                                            as_stream(stream)));
+    return status_of(minikv::launch_prefill(q, k, v, B, T, Hq, Hkv, D, resolve_scale(sm_scale, D), o, lse, 0,
+                                            nullptr, as_stream(stream)));
 }
 
 int minikv_window_scores(const void* q, const void* k, const float* lse, int B, int T, int Hq, int Hkv, int D,
@@ -113,9 +113,17 @@ int minikv_prefill_attn_scores(const void* q, const void* k, const void* v, int 
     if (st != MINIKV_OK) return st;
     if (window < 1 || window > T) return MINIKV_ERR_SHAPE;
     if (misaligned(lse) || misaligned(scores) || (o && misaligned(o))) return MINIKV_ERR_ALIGN;
+    if (minikv::prefill_fuses_scores(B, T, Hq, Hkv, window))  // one launch: scores from inside pass 1
+        return status_of(minikv::launch_prefill(q, k, v, B, T, Hq, Hkv, D, resolve_scale(sm_scale, D), o, lse,
+                                                window, scores, as_stream(stream)));
     st = minikv_prefill_attn(q, k, v, B, T, Hq, Hkv, D, sm_scale, o, lse, stream);
     if (st != MINIKV_OK) return st;
     return minikv_window_scores(q, k, lse, B, T, Hq, Hkv, D, window, sm_scale, scores, stream);
+}
+
+int minikv_prefill_fuses_scores(int B, int T, int Hq, int Hkv, int window) {
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || window < 1 || window > T) return 0;
+    return minikv::prefill_fuses_scores(B, T, Hq, Hkv, window) ? 1 : 0;
 }
 
 int minikv_select_topk(const float* scores, int B, int Hkv, int T, int n_heavy, int n_recent, int32_t* idx,

@@ -46,8 +46,12 @@ hipError_t launch_stream_decode(const void* q, const uint8_t* k_codes, const uin
                                 const void* k_res, const void* v_res, int n_res, float sm_scale, void* out,
                                 void* ws, const DecodePlan& plan, hipStream_t stream);
 
+// Pass 1; with window > 0 (only where prefill_fuses_scores) it also writes the
+// window scores of pass 2 in the same launch.
+bool prefill_fuses_scores(int B, int T_ctx, int Hq, int Hkv, int window);
 hipError_t launch_prefill(const void* q, const void* k, const void* v, int B, int T_ctx, int Hq,
-                          int Hkv, int D, float sm_scale, void* o, float* lse, hipStream_t stream);
+                          int Hkv, int D, float sm_scale, void* o, float* lse, int window, float* scores,
+                          hipStream_t stream);
 
 hipError_t launch_window_scores(const void* q, const void* k, const float* lse, int B, int T_ctx,
                                 int Hq, int Hkv, int D, int window, float sm_scale, float* scores,

@@ -24,10 +24,18 @@
 // key 16*half + v, which makes both operand layouts line up without shuffles.
 // Causal: tiles above the diagonal are never loaded; only tiles that cross it
 // apply the mask.  Query blocks are issued longest-first.
+//
+// Single-pass selective attention: when each KV head has one query head and
+// the W <= 32 observation rows all fall in a head's last query block, the
+// workgroup that finishes that block also computes the window scores
+// (window_mass.h, the second pass's arithmetic): its row lse values stay in
+// LDS, the 8 waves split the head's keys, re-read from L2 rather than HBM,
+// and no second launch or pass over K is needed.
 #include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
+#include "window_mass.h"
 
 namespace minikv {
 namespace {
@@ -38,6 +46,7 @@ namespace {
 constexpr int kFaWaves = MINIKV_FA_WAVES;  // waves per workgroup, 32 query rows each
 constexpr int kXcds = 8;                    // MI355X: 8 XCDs of 32 CUs, each with its own L2
 constexpr int kBN = 64;   // keys per tile
+constexpr int kMaxTails = 16;  // fused score passes one workgroup can hold
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -71,7 +80,7 @@ template <int D, bool kWithO, int WAVES>
 __device__ __forceinline__ void fa_block(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int T_ctx,
     int Hq, int Hkv, float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse, int hs, int qb,
-    uint16_t* __restrict__ sK, char* __restrict__ sV) {
+    uint16_t* __restrict__ sK, char* __restrict__ sV, int w0, float* __restrict__ s_wl) {
     constexpr int NT = 64 * WAVES;          // threads
     constexpr int BM = 32 * WAVES;          // query rows per workgroup
     constexpr int CH = D / 8;               // 16-byte chunks per row
@@ -334,7 +343,11 @@ __device__ __forceinline__ void fa_block(
 
     const float ltot = lsum + swap_halves(lsum);
     if (qi < T_ctx) {
-        if (half == 0) lse[qbase + qi] = (m_ref + __log2f(ltot)) * kLn2;
+        const float lse_i = (m_ref + __log2f(ltot)) * kLn2;
+        if (half == 0) lse[qbase + qi] = lse_i;
+        // observation rows of a fused score pass: the log2-domain lse the second
+        // pass would derive from the stored value, bit for bit
+        if (s_wl && half == 0 && qi >= w0) s_wl[qi - w0] = lse_i * wmass::kLog2e;
         if constexpr (kWithO) {
             const float inv = 1.0f / ltot;
 #pragma unroll
@@ -351,6 +364,50 @@ __device__ __forceinline__ void fa_block(
     }
 }
 
+// Window scores of (sequence, head) hs from inside pass 1: the W <= 32 rows
+// T-W..T-1 (Q operand from L2, lse from LDS) against every key; the waves of
+// the workgroup take contiguous runs of 32-key blocks, K blocks come through
+// two register sets (the next one loading while the current one is reduced).
+// One query head per KV head, so the scores row is the head's own.
+template <int D, int WAVES>
+__device__ __forceinline__ void window_tail(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int T_ctx,
+                                            int hs, int W, float scale_log2, const float* __restrict__ s_wl,
+                                            float* __restrict__ scores) {
+    constexpr int KS = D / 16;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int half = lane >> 5;
+    const size_t base = (size_t)hs * T_ctx;
+    const int w0 = T_ctx - W;
+    const int nkb = (T_ctx + 31) / 32;
+    const int per = (nkb + WAVES - 1) / WAVES;
+    const int kb0 = wave * per;
+    const int nb = min(per, nkb - kb0);
+    if (nb <= 0) return;
+    bf16x8 qa[KS];
+    float l2[16];
+    wmass::load_qrows<D>(q, base, w0, W, 0, lane, qa);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int m = wmass::acc_row(e, lane);
+        l2[e] = m < W ? s_wl[m] : INFINITY;
+    }
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k + base * D), 0, T_ctx * D * 2, 0x00020000);
+    auto emit = [&](int i, float a) {
+        a += swap_halves(a);
+        const int j = (kb0 + i) * 32 + (lane & 31);
+        if (half == 0 && j < T_ctx) scores[base + j] = a;
+    };
+    bf16x8 ka[KS], kb[KS];
+    wmass::load_kblock<D>(rk, kb0 * 32, lane, ka);
+    for (int i = 0; i < nb; i += 2) {
+        if (i + 1 < nb) wmass::load_kblock<D>(rk, (kb0 + i + 1) * 32, lane, kb);
+        emit(i, wmass::block_mass<D>(qa, ka, l2, scale_log2, w0, (kb0 + i) * 32, lane));
+        if (i + 2 < nb) wmass::load_kblock<D>(rk, (kb0 + i + 2) * 32, lane, ka);
+        if (i + 1 < nb) emit(i + 1, wmass::block_mass<D>(qa, kb, l2, scale_log2, w0, (kb0 + i + 1) * 32, lane));
+    }
+}
+
 // Persistent workgroups, one per CU, dispatched round-robin over the XCDs
 // (workgroup L on XCD L % 8).  Each XCD owns a contiguous run of (sequence,
 // head) pairs, so the K/V prefix a head's query blocks re-read stays in that
@@ -358,15 +415,21 @@ __device__ __forceinline__ void fa_block(
 // (qb, nqb - 1 - qb), which cost the same, and the pairs are dealt round-robin
 // to the XCD's workgroups: equal work per workgroup, and no re-dispatch gaps
 // between blocks (a block's output stores drain while the next one loads).
+// With fused window scores (W > 0) the pairs holding a head's last block are
+// dealt first, so each workgroup finishes at most kMaxTails of them (the host
+// checks); their observation rows' lse wait in LDS, and the score passes run
+// after the workgroup's last block, outside the attention loop.
 template <int D, bool kWithO, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int B_,
-    int T_ctx, int Hq, int Hkv, int nqb, float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse) {
+    int T_ctx, int Hq, int Hkv, int nqb, float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse,
+    int W, float* __restrict__ scores) {
     constexpr int TILE = kBN * kKStride<D>;
     constexpr int VT_BYTES = 32 * (D / 64) * kVtLine;
     // two LDS stages: tile t is read from one while tile t+1 is written to the other
     __shared__ __attribute__((aligned(16))) uint16_t sK[2 * TILE];
     __shared__ __attribute__((aligned(16))) char sV[kWithO ? 2 * VT_BYTES : 16];
+    __shared__ float s_wl[kMaxTails * 32];  // log2-domain lse of the observation rows (fused scores)
 
     const int heads = B_ * Hq;
     const int per = (heads + kXcds - 1) / kXcds;
@@ -380,15 +443,32 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     int p = slot;
     bool second = false;
     while (p < nh * pairs) {
-        const int hs = h0 + p / pairs;
-        const int j = p % pairs;
-        fa_block<D, kWithO, WAVES>(q, k, v, T_ctx, Hq, Hkv, scale_log2, o, lse, hs, second ? j : nqb - 1 - j, sK, sV);
+        int hs, j;
+        if (W == 0) {
+            hs = h0 + p / pairs;
+            j = p % pairs;
+        } else if (p < nh) {  // pairs with a score pass first
+            hs = h0 + p;
+            j = 0;
+        } else {
+            hs = h0 + (p - nh) / (pairs - 1);
+            j = 1 + (p - nh) % (pairs - 1);
+        }
+        const int qb = second ? j : nqb - 1 - j;
+        // a head's last block: its observation rows' lse go to tail slot p / nslots
+        float* wl = (W > 0 && qb == nqb - 1) ? s_wl + 32 * (p / nslots) : nullptr;
+        fa_block<D, kWithO, WAVES>(q, k, v, T_ctx, Hq, Hkv, scale_log2, o, lse, hs, qb, sK, sV, T_ctx - W, wl);
         if (!second && j != nqb - 1 - j) {
             second = true;
         } else {
             second = false;
             p += nslots;
         }
+    }
+    if (W > 0 && slot < nh) {  // the score passes of the heads whose last block ran here
+        __syncthreads();
+        for (int pt = slot, t = 0; pt < nh; pt += nslots, ++t)
+            window_tail<D, WAVES>(q, k, T_ctx, h0 + pt, W, scale_log2, s_wl + 32 * t, scores);
     }
 }
 
@@ -407,27 +487,39 @@ int cu_count() {
 
 template <int D, bool kWithO>
 hipError_t launch_fa(const void* q, const void* k, const void* v, int B, int T_ctx, int Hq, int Hkv,
-                     float sm_scale, void* o, float* lse, hipStream_t stream) {
+                     float sm_scale, void* o, float* lse, int W, float* scores, hipStream_t stream) {
     constexpr int WAVES = kFaWaves;
     const int nqb = (T_ctx + 32 * WAVES - 1) / (32 * WAVES);
     const int grid = max(kXcds, cu_count() / kXcds * kXcds);
     hipLaunchKernelGGL((fa_fwd_kernel<D, kWithO, WAVES>), dim3(grid), dim3(64 * WAVES), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), B, T_ctx, Hq, Hkv, nqb, sm_scale * kLog2e,
-                       static_cast<__bf16*>(o), lse);
+                       static_cast<__bf16*>(o), lse, W, scores);
     return hipGetLastError();
 }
 
 }  // namespace
 
+bool prefill_fuses_scores(int B, int T_ctx, int Hq, int Hkv, int window) {
+    constexpr int BM = 32 * kFaWaves;
+    const int last_rows = T_ctx - (T_ctx - 1) / BM * BM;  // rows of the last query block
+    const long long heads = (long long)B * Hq;
+    const long long per_xcd = (heads + kXcds - 1) / kXcds;
+    const long long slots = max(kXcds, cu_count() / kXcds * kXcds) / kXcds;
+    return Hq == Hkv && window >= 1 && window <= 32 && window <= last_rows &&
+           (per_xcd + slots - 1) / slots <= kMaxTails;
+}
+
 hipError_t launch_prefill(const void* q, const void* k, const void* v, int B, int T_ctx, int Hq, int Hkv,
-                          int D, float sm_scale, void* o, float* lse, hipStream_t stream) {
+                          int D, float sm_scale, void* o, float* lse, int window, float* scores,
+                          hipStream_t stream) {
+    if (window != 0 && (!scores || !prefill_fuses_scores(B, T_ctx, Hq, Hkv, window))) return hipErrorInvalidValue;
     if (D == 128) {
-        if (o) return launch_fa<128, true>(q, k, v, B, T_ctx, Hq, Hkv, sm_scale, o, lse, stream);
-        return launch_fa<128, false>(q, k, v, B, T_ctx, Hq, Hkv, sm_scale, o, lse, stream);
+        if (o) return launch_fa<128, true>(q, k, v, B, T_ctx, Hq, Hkv, sm_scale, o, lse, window, scores, stream);
+        return launch_fa<128, false>(q, k, v, B, T_ctx, Hq, Hkv, sm_scale, o, lse, window, scores, stream);
     }
-    if (o) return launch_fa<64, true>(q, k, v, B, T_ctx, Hq, Hkv, sm_scale, o, lse, stream);
-    return launch_fa<64, false>(q, k, v, B, T_ctx, Hq, Hkv, sm_scale, o, lse, stream);
+    if (o) return launch_fa<64, true>(q, k, v, B, T_ctx, Hq, Hkv, sm_scale, o, lse, window, scores, stream);
+    return launch_fa<64, false>(q, k, v, B, T_ctx, Hq, Hkv, sm_scale, o, lse, window, scores, stream);
 }
 
 }  // namespace minikv

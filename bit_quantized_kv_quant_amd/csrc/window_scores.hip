@@ -17,58 +17,22 @@
 // Summation order is fixed, so the scores are deterministic.
 #include "common.h"
 #include "kernels.h"
+#include "window_mass.h"
 
 namespace minikv {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
-// K^T operand of key block kt0: lane holds k[kt0 + lane % 32][16 kk + 8 half + 0..7]
-// (rows past T read as zeros through the buffer resource).
-template <int D>
-__device__ __forceinline__ void load_kblock(__amdgpu_buffer_rsrc_t rk, int kt0, int lane, bf16x8 (&kreg)[D / 16]) {
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-        kreg[kk] = __builtin_bit_cast(
-            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, ((kt0 + (lane & 31)) * D + 16 * kk + 8 * (lane >> 5)) * 2, 0, 0));
-}
-
-// Scores of key block kt0 against the window rows of one query head, given the
-// Q operand of row block rb (qa) and the lane's 16 row log-sum-exps (log2
-// domain, +inf for rows past the window).
-template <int D>
-__device__ __forceinline__ float block_mass(const bf16x8 (&qa)[D / 16], const bf16x8 (&kreg)[D / 16], const float (&l2)[16],
-                                            float scale_log2, int row0, int kt0, int lane) {
-    f32x16 sacc = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kreg[kk], sacc, 0, 0, 0);
-    const int half = lane >> 5;
-    const int j = kt0 + (lane & 31);
-    float acc = 0.0f;
-    if (kt0 + 31 <= row0) {  // every window row of the block sees every key of the block
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc += exp2f(fmaf(sacc[e], scale_log2, -l2[e]));
-    } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int i = row0 + 8 * (e >> 2) + 4 * half + (e & 3);
-            if (j <= i) acc += exp2f(fmaf(sacc[e], scale_log2, -l2[e]));
-        }
-    }
-    return acc;
-}
+using wmass::block_mass;
+using wmass::kLog2e;
+using wmass::load_kblock;
 
 template <int D>
 __device__ __forceinline__ void load_qblock(const uint16_t* __restrict__ q, const float* __restrict__ lse, size_t qbase,
                                             int w0, int W, int rb, int lane, bf16x8 (&qa)[D / 16], float (&l2)[16]) {
-    const int half = lane >> 5;
-    const int r = 32 * rb + (lane & 31);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-        qa[kk] = r < W ? *reinterpret_cast<const bf16x8*>(q + (qbase + w0 + r) * D + 16 * kk + 8 * half) : bf16x8{};
+    wmass::load_qrows<D>(q, qbase, w0, W, rb, lane, qa);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        const int m = 32 * rb + 8 * (e >> 2) + 4 * half + (e & 3);
+        const int m = 32 * rb + wmass::acc_row(e, lane);
         l2[e] = m < W ? lse[qbase + w0 + m] * kLog2e : INFINITY;
     }
 }

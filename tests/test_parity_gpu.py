@@ -200,6 +200,7 @@ def test_prefill_tiny(dev):
 
 @pytest.mark.parametrize("B,Hq,Hkv,T,D,W", [
     (2, 4, 2, 333, 128, 40), (1, 2, 2, 1, 64, 1), (1, 8, 2, 200, 128, 32), (1, 1, 1, 129, 128, 129),
+    (2, 4, 4, 1000, 128, 32), (1, 2, 2, 300, 64, 32), (3, 2, 2, 33, 128, 7),
 ])
 def test_prefill_ragged_gqa(dev, B, Hq, Hkv, T, D, W):
     say("prefill B", B, "Hq", Hq, "Hkv", Hkv, "T", T, "D", D, "W", W)
@@ -209,6 +210,33 @@ def test_prefill_ragged_gqa(dev, B, Hq, Hkv, T, D, W):
     k[..., :4] *= 8
     v = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
     _prefill_case(dev, q, k, v, W)
+
+
+@pytest.mark.parametrize("B,H,T,D,W", [
+    (1, 2, 256, 64, 16), (2, 4, 1000, 128, 32), (1, 2, 300, 64, 32), (1, 1, 1, 128, 1), (3, 2, 33, 128, 32),
+    (2, 3, 4100, 128, 4), (8, 32, 4096, 128, 32),
+])
+@pytest.mark.parametrize("with_o", [True, False])
+def test_single_pass_scores_equal_two_passes(dev, B, H, T, D, W, with_o):
+    """Scores from inside pass 1 are the second pass's bits; o and lse are pass 1's alone."""
+    say("single-pass scores B", B, "H", H, "T", T, "D", D, "W", W, "o", with_o)
+    assert mk.prefill_fuses_scores(B, T, H, H, W)
+    g = torch.Generator(device=dev).manual_seed(T * 7 + W)
+    q = torch.randn((B, H, T, D), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((B, H, T, D), generator=g, device=dev)
+    k[..., :3] *= 6
+    k = k.to(torch.bfloat16)
+    v = torch.randn((B, H, T, D), generator=g, device=dev).to(torch.bfloat16)
+    o1, l1, s1 = mk.prefill_attn_scores(q, k, v, W, with_o=with_o)
+    o2, l2 = mk.prefill_attn(q, k, v, with_o=with_o)
+    s2 = mk.window_scores(q, k, l2, W)
+    torch.cuda.synchronize()
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    if with_o:
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    r = torch.allclose(s1.sum(-1).double(), torch.full((B, H), float(W), dtype=torch.float64, device=dev), rtol=1e-4)
+    assert r
 
 
 def test_prefill_lse_only_matches(dev):
