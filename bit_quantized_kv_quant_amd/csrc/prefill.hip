@@ -27,10 +27,10 @@
 //
 // Single-pass selective attention: when each KV head has one query head and
 // the W <= 32 observation rows all fall in a head's last query block, the
-// workgroup that finishes that block also computes the window scores
-// (window_mass.h, the second pass's arithmetic): its row lse values stay in
-// LDS, the 8 waves split the head's keys, re-read from L2 rather than HBM,
-// and no second launch or pass over K is needed.
+// workgroup that finishes that block computes the head's window scores right
+// away (window_mass.h, the second pass's arithmetic): the rows' lse values
+// stay in LDS, the 8 waves split the head's keys, which the block has just
+// streamed and the Infinity Cache still holds, and no second launch is needed.
 #include <type_traits>
 
 #include "common.h"
@@ -46,7 +46,6 @@ namespace {
 constexpr int kFaWaves = MINIKV_FA_WAVES;  // waves per workgroup, 32 query rows each
 constexpr int kXcds = 8;                    // MI355X: 8 XCDs of 32 CUs, each with its own L2
 constexpr int kBN = 64;   // keys per tile
-constexpr int kMaxTails = 16;  // fused score passes one workgroup can hold
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -415,10 +414,10 @@ __device__ __forceinline__ void window_tail(const uint16_t* __restrict__ q, cons
 // (qb, nqb - 1 - qb), which cost the same, and the pairs are dealt round-robin
 // to the XCD's workgroups: equal work per workgroup, and no re-dispatch gaps
 // between blocks (a block's output stores drain while the next one loads).
-// With fused window scores (W > 0) the pairs holding a head's last block are
-// dealt first, so each workgroup finishes at most kMaxTails of them (the host
-// checks); their observation rows' lse wait in LDS, and the score passes run
-// after the workgroup's last block, outside the attention loop.
+// With fused window scores (W > 0) each head's pairs are rotated by the round
+// they run in, so the pair that carries a score pass lands on a different
+// workgroup in every round (one per workgroup when heads and pairs tile the
+// XCD evenly) and score passes overlap other workgroups' attention.
 template <int D, bool kWithO, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int B_,
@@ -429,7 +428,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     // two LDS stages: tile t is read from one while tile t+1 is written to the other
     __shared__ __attribute__((aligned(16))) uint16_t sK[2 * TILE];
     __shared__ __attribute__((aligned(16))) char sV[kWithO ? 2 * VT_BYTES : 16];
-    __shared__ float s_wl[kMaxTails * 32];  // log2-domain lse of the observation rows (fused scores)
+    __shared__ float s_wl[32];  // log2-domain lse of the observation rows (fused scores)
 
     const int heads = B_ * Hq;
     const int per = (heads + kXcds - 1) / kXcds;
@@ -443,32 +442,24 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     int p = slot;
     bool second = false;
     while (p < nh * pairs) {
-        int hs, j;
-        if (W == 0) {
-            hs = h0 + p / pairs;
-            j = p % pairs;
-        } else if (p < nh) {  // pairs with a score pass first
-            hs = h0 + p;
-            j = 0;
-        } else {
-            hs = h0 + (p - nh) / (pairs - 1);
-            j = 1 + (p - nh) % (pairs - 1);
-        }
+        const int hs = h0 + p / pairs;
+        // the rotation depends on the head alone, so it permutes the head's pairs
+        const int j = W == 0 ? p % pairs : (p % pairs + (p / pairs) * pairs / nslots) % pairs;
         const int qb = second ? j : nqb - 1 - j;
-        // a head's last block: its observation rows' lse go to tail slot p / nslots
-        float* wl = (W > 0 && qb == nqb - 1) ? s_wl + 32 * (p / nslots) : nullptr;
-        fa_block<D, kWithO, WAVES>(q, k, v, T_ctx, Hq, Hkv, scale_log2, o, lse, hs, qb, sK, sV, T_ctx - W, wl);
+        const bool tail = W > 0 && qb == nqb - 1;
+        fa_block<D, kWithO, WAVES>(q, k, v, T_ctx, Hq, Hkv, scale_log2, o, lse, hs, qb, sK, sV, T_ctx - W,
+                                   tail ? s_wl : nullptr);
+        if (tail) {
+            __syncthreads();  // the observation rows' lse are in s_wl
+            window_tail<D, WAVES>(q, k, T_ctx, hs, W, scale_log2, s_wl, scores);
+            __syncthreads();  // s_wl and the waves are free for the next block
+        }
         if (!second && j != nqb - 1 - j) {
             second = true;
         } else {
             second = false;
             p += nslots;
         }
-    }
-    if (W > 0 && slot < nh) {  // the score passes of the heads whose last block ran here
-        __syncthreads();
-        for (int pt = slot, t = 0; pt < nh; pt += nslots, ++t)
-            window_tail<D, WAVES>(q, k, T_ctx, h0 + pt, W, scale_log2, s_wl + 32 * t, scores);
     }
 }
 
@@ -501,13 +492,10 @@ hipError_t launch_fa(const void* q, const void* k, const void* v, int B, int T_c
 }  // namespace
 
 bool prefill_fuses_scores(int B, int T_ctx, int Hq, int Hkv, int window) {
+    (void)B;
     constexpr int BM = 32 * kFaWaves;
     const int last_rows = T_ctx - (T_ctx - 1) / BM * BM;  // rows of the last query block
-    const long long heads = (long long)B * Hq;
-    const long long per_xcd = (heads + kXcds - 1) / kXcds;
-    const long long slots = max(kXcds, cu_count() / kXcds * kXcds) / kXcds;
-    return Hq == Hkv && window >= 1 && window <= 32 && window <= last_rows &&
-           (per_xcd + slots - 1) / slots <= kMaxTails;
+    return Hq == Hkv && window >= 1 && window <= 32 && window <= last_rows;
 }
 
 hipError_t launch_prefill(const void* q, const void* k, const void* v, int B, int T_ctx, int Hq, int Hkv,

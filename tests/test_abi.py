@@ -208,3 +208,21 @@ def test_packed_bytes_matches_oracle(L):
         for D in (64, 128):
             assert L.minikv_packed_bytes(3, 5, n, D) == oracle.packed_bytes_ref(3, 5, n, D)
     assert L.minikv_packed_bytes(0, 1, 1, 128) == 0
+
+
+def test_single_pass_rule(L):
+    """Scores come out of pass 1 exactly for one query head per KV head, W <= 32,
+    and W rows inside the last 256-row query block; invalid sizes give 0."""
+    f = L.minikv_prefill_fuses_scores
+    assert f(8, 4096, 32, 32, 32) == 1
+    assert f(1, 16384, 32, 32, 32) == 1
+    assert f(1, 1, 1, 1, 1) == 1
+    assert f(4, 44000, 32, 8, 32) == 0          # four query heads per KV head
+    assert f(1, 4096, 2, 2, 33) == 0            # window beyond one row block
+    assert f(1, 4100, 2, 2, 4) == 1             # last block holds rows 4096..4099
+    assert f(1, 4100, 2, 2, 5) == 0
+    for T in (1, 255, 256, 257, 511, 44000):
+        last = T - (T - 1) // 256 * 256
+        for W in (1, 16, 32):
+            assert f(2, T, 4, 4, W) == int(W <= min(32, last, T))
+    assert f(0, 10, 1, 1, 1) == 0 and f(1, 10, 3, 2, 1) == 0 and f(1, 10, 1, 1, 11) == 0
