@@ -491,11 +491,15 @@ hipError_t launch_fa(const void* q, const void* k, const void* v, int B, int T_c
 
 }  // namespace
 
+// One score pass per head runs on the workgroup that finishes the head's last
+// query block, its 8 waves walking the head's keys; with fewer heads than
+// workgroups those few long passes would trail the kernel, and the stand-alone
+// pass, spread over the whole GPU, is faster.
 bool prefill_fuses_scores(int B, int T_ctx, int Hq, int Hkv, int window) {
-    (void)B;
     constexpr int BM = 32 * kFaWaves;
     const int last_rows = T_ctx - (T_ctx - 1) / BM * BM;  // rows of the last query block
-    return Hq == Hkv && window >= 1 && window <= 32 && window <= last_rows;
+    return Hq == Hkv && window >= 1 && window <= 32 && window <= last_rows &&
+           (long long)B * Hq >= cu_count();
 }
 
 hipError_t launch_prefill(const void* q, const void* k, const void* v, int B, int T_ctx, int Hq, int Hkv,

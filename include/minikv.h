@@ -96,16 +96,18 @@ typedef struct {
  *
  * minikv_prefill_attn_scores computes both.  Where
  * minikv_prefill_fuses_scores(B, T, Hq, Hkv, W) is 1 (one query head per KV
- * head, W <= 32, the W rows inside the last 256-row query block) it is a
- * single launch: the workgroup that finishes a head's last query block scores
- * that head's keys from its own lse right away, while K is still cached.  The
+ * head, W <= 32, the W rows inside the last 256-row query block, and at least
+ * as many heads B * Hq as the device has compute units) it is a single
+ * launch: the workgroup that finishes a head's last query block scores that
+ * head's keys from its own lse right away, while K is still cached.  The
  * results are bit-identical to minikv_prefill_attn followed by
  * minikv_window_scores.  Otherwise it enqueues the two passes.
  * sm_scale <= 0 means 1/sqrt(D).
  * Errors: NULL q/k/v/lse/scores; SHAPE if any size < 1, Hq % Hkv, W > T;
  * UNSUPPORTED if D is not 64 or 128; ALIGN; LAUNCH.
- * minikv_prefill_fuses_scores returns 1 or 0 (0 for invalid sizes too); it
- * makes no HIP call.
+ * minikv_prefill_fuses_scores returns 1 or 0 (0 for invalid sizes too); its
+ * only HIP call is a query of the current device's compute-unit count (256
+ * is assumed when there is no device).
  */
 int minikv_prefill_attn(const void *q, const void *k, const void *v,
                         int B, int T, int Hq, int Hkv, int D, float sm_scale,

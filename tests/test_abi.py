@@ -212,17 +212,18 @@ def test_packed_bytes_matches_oracle(L):
 
 def test_single_pass_rule(L):
     """Scores come out of pass 1 exactly for one query head per KV head, W <= 32,
-    and W rows inside the last 256-row query block; invalid sizes give 0."""
+    W rows inside the last 256-row query block and at least one head per
+    compute unit (256 assumed without a device); invalid sizes give 0."""
     f = L.minikv_prefill_fuses_scores
     assert f(8, 4096, 32, 32, 32) == 1
-    assert f(1, 16384, 32, 32, 32) == 1
-    assert f(1, 1, 1, 1, 1) == 1
+    assert f(1, 16384, 32, 32, 32) == 0         # 32 heads: the stand-alone pass is faster
+    assert f(256, 1, 1, 1, 1) == 1
     assert f(4, 44000, 32, 8, 32) == 0          # four query heads per KV head
-    assert f(1, 4096, 2, 2, 33) == 0            # window beyond one row block
-    assert f(1, 4100, 2, 2, 4) == 1             # last block holds rows 4096..4099
-    assert f(1, 4100, 2, 2, 5) == 0
+    assert f(8, 4096, 32, 32, 33) == 0          # window beyond one row block
+    assert f(16, 4100, 16, 16, 4) == 1          # last block holds rows 4096..4099
+    assert f(16, 4100, 16, 16, 5) == 0
     for T in (1, 255, 256, 257, 511, 44000):
         last = T - (T - 1) // 256 * 256
         for W in (1, 16, 32):
-            assert f(2, T, 4, 4, W) == int(W <= min(32, last, T))
+            assert f(64, T, 4, 4, W) == int(W <= min(32, last, T))
     assert f(0, 10, 1, 1, 1) == 0 and f(1, 10, 3, 2, 1) == 0 and f(1, 10, 1, 1, 11) == 0

@@ -200,7 +200,8 @@ def test_prefill_tiny(dev):
 
 @pytest.mark.parametrize("B,Hq,Hkv,T,D,W", [
     (2, 4, 2, 333, 128, 40), (1, 2, 2, 1, 64, 1), (1, 8, 2, 200, 128, 32), (1, 1, 1, 129, 128, 129),
-    (2, 4, 4, 1000, 128, 32), (1, 2, 2, 300, 64, 32), (3, 2, 2, 33, 128, 7),
+    (2, 4, 4, 1000, 128, 32), (1, 2, 2, 300, 64, 32), (3, 2, 2, 33, 128, 7), (64, 4, 4, 97, 64, 32),
+    (16, 16, 16, 270, 128, 13),
 ])
 def test_prefill_ragged_gqa(dev, B, Hq, Hkv, T, D, W):
     say("prefill B", B, "Hq", Hq, "Hkv", Hkv, "T", T, "D", D, "W", W)
@@ -213,14 +214,14 @@ def test_prefill_ragged_gqa(dev, B, Hq, Hkv, T, D, W):
 
 
 @pytest.mark.parametrize("B,H,T,D,W", [
-    (1, 2, 256, 64, 16), (2, 4, 1000, 128, 32), (1, 2, 300, 64, 32), (1, 1, 1, 128, 1), (3, 2, 33, 128, 32),
-    (2, 3, 4100, 128, 4), (8, 32, 4096, 128, 32),
+    (4, 64, 256, 64, 16), (32, 8, 1000, 128, 32), (64, 4, 300, 64, 32), (256, 1, 1, 128, 1), (128, 2, 33, 128, 32),
+    (16, 16, 4100, 128, 4), (8, 32, 4096, 128, 32), (86, 3, 520, 128, 8),
 ])
 @pytest.mark.parametrize("with_o", [True, False])
 def test_single_pass_scores_equal_two_passes(dev, B, H, T, D, W, with_o):
     """Scores from inside pass 1 are the second pass's bits; o and lse are pass 1's alone."""
     say("single-pass scores B", B, "H", H, "T", T, "D", D, "W", W, "o", with_o)
-    assert mk.prefill_fuses_scores(B, T, H, H, W)
+    assert mk.prefill_fuses_scores(B, T, H, H, W), "needs at least one head per compute unit"
     g = torch.Generator(device=dev).manual_seed(T * 7 + W)
     q = torch.randn((B, H, T, D), generator=g, device=dev).to(torch.bfloat16)
     k = torch.randn((B, H, T, D), generator=g, device=dev)
