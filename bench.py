@@ -56,7 +56,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--decode-rotation-gb", type=float, default=1.2)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -421,14 +421,17 @@ def main():
 
     # single pass: the window scores come out of the pass-1 kernel (one launch)
     fused = mk.prefill_fuses_scores(B, T, Hq, Hkv, W)
-    stages = (["prefill_attn_scores"] if fused else ["prefill_attn", "window_scores"]) + \
-        ["select_topk", "quant_pack", "decode_attn"]
-    timer = StageTimer(torch, stages)
 
-    def step(t=None):
+    def stage_names(single):
+        return (["prefill_attn_scores"] if single else ["prefill_attn", "window_scores"]) + \
+            ["select_topk", "quant_pack", "decode_attn"]
+
+    timer = StageTimer(torch, stage_names(fused))
+
+    def step(t=None, single=fused):
         if t:
             t.mark()
-        if fused:
+        if single:
             mk.prefill_attn_scores(q, k, v, W, o=o, lse=lse, scores=scores)
         else:
             mk.prefill_attn(q, k, v, o=o, lse=lse)
@@ -465,25 +468,22 @@ def main():
     print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
           file=sys.stderr, flush=True)
 
-    # ---- the two passes as separate launches, for comparison ----
+    # ---- the same chain with the two passes as separate launches, for comparison ----
     two_pass = {}
     if fused:
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        reps2 = 5
-        for _ in range(2):
-            mk.prefill_attn(q, k, v, o=o, lse=lse)
-            mk.window_scores(q, k, lse, W, scores=scores)
-        ev[0].record()
-        for _ in range(reps2):
-            mk.prefill_attn(q, k, v, o=o, lse=lse)
-        ev[1].record()
-        for _ in range(reps2):
-            mk.window_scores(q, k, lse, W, scores=scores)
-        ev[2].record()
+        timer2 = StageTimer(torch, stage_names(False))
+        for _ in range(args.warmup):
+            step(single=False)
         torch.cuda.synchronize()
-        two_pass = {"prefill_attn_ms": ev[0].elapsed_time(ev[1]) / reps2,
-                    "window_scores_ms": ev[1].elapsed_time(ev[2]) / reps2}
-        two_pass["sum_ms"] = two_pass["prefill_attn_ms"] + two_pass["window_scores_ms"]
+        e2 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e2[0].record()
+        for _ in range(args.steps):
+            step(timer2, single=False)
+        e2[1].record()
+        torch.cuda.synchronize()
+        two_pass = {"ms_per_step": e2[0].elapsed_time(e2[1]) / args.steps, "stages_ms": timer2.totals(args.steps)}
+        step()  # leave the single-pass outputs in place
+        torch.cuda.synchronize()
 
     # ---- decode alone, rotating over >= 1 GB of distinct packed caches ----
     cache_bytes = cache.nbytes()
@@ -553,7 +553,7 @@ def main():
                      "flops_per_launch": flops},
         "stages_ms": per_stage,
         "single_pass_scores": fused,
-        "two_pass_ms": two_pass or None,
+        "two_pass_chain": two_pass or None,
         "decode": {"tokens_per_s": B / (dec_ms * 1e-3), "ms": dec_ms, "bytes": dec_bytes,
                    "achieved_GBs": dec_gbs, "hbm_frac": dec_gbs / PEAK_HBM_GBS, "rotated_caches": n_rot,
                    "rotation_bytes": n_rot * cache_bytes},
