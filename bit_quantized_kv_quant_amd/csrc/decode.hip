@@ -288,10 +288,21 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 #pragma unroll
         for (int T = 0; T < NT; ++T)
             st.vc[T] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(voff + 128 * T), 0, 0));
+        // a token's GPL scale/zero words are adjacent: one load of GPL dwords
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (GPL == 4) {
+                const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, (int)vsz_off(j, 0), 0, 0));
 #pragma unroll
-            for (int i = 0; i < GPL; ++i) st.vsz[j][i] = __builtin_amdgcn_raw_buffer_load_b32(rz, (int)vsz_off(j, i), 0, 0);
+                for (int i = 0; i < 4; ++i) st.vsz[j][i] = w[i];
+            } else if constexpr (GPL == 2) {
+                const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rz, (int)vsz_off(j, 0), 0, 0));
+                st.vsz[j][0] = w[0];
+                st.vsz[j][1] = w[1];
+            } else {
+                st.vsz[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rz, (int)vsz_off(j, 0), 0, 0);
+            }
+        }
     };
     // the query of a KV unit: bf16 bits of channels c0, c0 + 2 for each of its R heads
     auto load_q = [&](int unit, uint32_t (&qb)[R][2]) {
@@ -466,10 +477,13 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         const Pos first_next = pos_of(next_item);
         const int step_end = (ps.t_end + kStep - 1) / kStep;
         for (; ps.step < step_end; ++ps.step) {
-            // next position: the next step, the next item's first step, or (past the
-            // last item) this step again, a harmless reload that keeps loads unconditional
+            // next position: the next step, the next item's first step, or (after the
+            // wave's last step) an empty range: the loads stay unconditional, and
+            // with a zero-size buffer resource they return zeros without touching
+            // memory
             const bool last = ps.step + 1 == step_end;
-            const Pos nx = !last ? Pos{ps.unit, ps.step + 1, ps.t_end} : (next_item < n_items ? first_next : ps);
+            const Pos nx = !last ? Pos{ps.unit, ps.step + 1, ps.t_end}
+                                 : (next_item < n_items ? first_next : Pos{ps.unit, ps.step, ps.step * kStep});
             load_q(nx.unit, qb);
             process(ps, st, nx);
         }
