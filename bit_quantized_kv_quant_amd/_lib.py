@@ -55,6 +55,11 @@ SIGNATURES = {
     "minikv_stream_decode": (_i, [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _f, _vp, _vp,
                                   _sz, _vp]),
     "minikv_stream_decode_ws_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "minikv_stream_set_counts": (_i, [_vp, _i, _i, _i, _vp]),
+    "minikv_stream_step_append": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "minikv_stream_step_decode_ws_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "minikv_stream_step_decode": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _sz,
+                                       _vp]),
     "minikv_packed_bytes": (_sz, [_i, _i, _i, _i]),
     "minikv_decode_ws_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "minikv_keep_count": (_i, [_i, _i]),

@@ -203,6 +203,7 @@ class StreamCache:
     D: int
     n_packed: int = 0
     n_res: int = 0
+    counts: torch.Tensor = None  # int32 [4] {n_packed, n_res, overflow, 0}: the device-side step's counts
 
     @staticmethod
     def alloc(B, Hkv, cap, D, device="cuda"):
@@ -267,6 +268,61 @@ class StreamCache:
 
     def ws_bytes(self, Hq):
         return int(_lib.lib().minikv_stream_decode_ws_bytes(self.B, Hq, self.Hkv, self.n_packed, self.n_res, self.D))
+
+    # ---- device-side generation step: the counts live in device memory, so a
+    # step (step_append + step_decode per layer) is a fixed launch sequence that a
+    # HIP graph can capture and replay ----
+
+    def to_device_counts(self):
+        """Copy the host counts into the device counts (allocated on first use)."""
+        if self.counts is None:
+            self.counts = torch.empty(4, dtype=torch.int32, device=self.k_res.device)
+        st = _lib.lib().minikv_stream_set_counts(_ptr(self.counts), self.n_packed, self.n_res, self.cap, _stream())
+        _lib.check("minikv_stream_set_counts", st)
+        return self
+
+    def from_device_counts(self):
+        """Read the device counts back into n_packed / n_res (synchronises); raises on overflow."""
+        n_packed, n_res, overflow, _ = (int(x) for x in self.counts.cpu())
+        if overflow:
+            raise ValueError("streaming cache is full (a window could not be packed)")
+        self.n_packed, self.n_res = n_packed, n_res
+        return self
+
+    def step_append(self, k_new, v_new):
+        """append() with the counts on the device (no host decision)."""
+        if self.counts is None:
+            raise ValueError("call to_device_counts() first")
+        _need(k_new, torch.bfloat16, (self.B, self.Hkv, self.D), "k_new")
+        _need(v_new, torch.bfloat16, (self.B, self.Hkv, self.D), "v_new")
+        st = _lib.lib().minikv_stream_step_append(_ptr(k_new), _ptr(v_new), self.B, self.Hkv, self.D, self.cap,
+                                                  _ptr(self.counts), _ptr(self.k_codes), _ptr(self.k_sz),
+                                                  _ptr(self.v_codes), _ptr(self.v_sz), _ptr(self.k_res),
+                                                  _ptr(self.v_res), _stream())
+        _lib.check("minikv_stream_step_append", st)
+        return self
+
+    def step_ws_bytes(self, Hq):
+        return int(_lib.lib().minikv_stream_step_decode_ws_bytes(self.B, Hq, self.Hkv, self.cap, self.D))
+
+    def step_decode(self, q, sm_scale=None, out=None, ws=None):
+        """decode() with the counts read on the device."""
+        if self.counts is None:
+            raise ValueError("call to_device_counts() first")
+        B, Hq, D = q.shape
+        _need(q, torch.bfloat16, (self.B, Hq, self.D), "q")
+        if out is None:
+            out = torch.empty_like(q)
+        _need(out, torch.bfloat16, (self.B, Hq, self.D), "out")
+        if ws is None:
+            ws = torch.empty(max(self.step_ws_bytes(Hq), 16), dtype=torch.uint8, device=q.device)
+        st = _lib.lib().minikv_stream_step_decode(_ptr(q), self.B, Hq, self.Hkv, self.D, self.cap, _ptr(self.counts),
+                                                  _ptr(self.k_codes), _ptr(self.k_sz), _ptr(self.v_codes),
+                                                  _ptr(self.v_sz), _ptr(self.k_res), _ptr(self.v_res),
+                                                  float(sm_scale or 0.0), _ptr(out), _ptr(ws),
+                                                  ws.numel() * ws.element_size(), _stream())
+        _lib.check("minikv_stream_step_decode", st)
+        return out
 
     def decode(self, q, sm_scale=None, out=None, ws=None):
         """Single-query attention over the packed and the residual tokens: q bf16 [B, Hq, D]."""

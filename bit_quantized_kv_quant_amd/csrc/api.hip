@@ -234,4 +234,54 @@ int minikv_stream_decode(const void* q, int B, int Hq, int Hkv, int D, int cap, 
                                                   as_stream(stream)));
 }
 
+int minikv_stream_set_counts(int32_t* counts, int n_packed, int n_res, int cap, void* stream) {
+    if (!counts) return MINIKV_ERR_NULL;
+    if (cap < MINIKV_GROUP || cap % MINIKV_GROUP || n_packed < 0 || n_packed % MINIKV_GROUP || n_packed > cap ||
+        n_res < 0 || n_res >= MINIKV_GROUP)
+        return MINIKV_ERR_SHAPE;
+    if (misaligned(counts)) return MINIKV_ERR_ALIGN;
+    return status_of(minikv::launch_stream_set_counts(counts, n_packed, n_res, as_stream(stream)));
+}
+
+int minikv_stream_step_append(const void* k_new, const void* v_new, int B, int Hkv, int D, int cap,
+                              int32_t* counts, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes, uint32_t* v_sz,
+                              void* k_res, void* v_res, void* stream) {
+    if (!k_new || !v_new || !counts || !k_codes || !k_sz || !v_codes || !v_sz || !k_res || !v_res)
+        return MINIKV_ERR_NULL;
+    if (B < 1 || Hkv < 1 || cap < MINIKV_GROUP || cap % MINIKV_GROUP) return MINIKV_ERR_SHAPE;
+    if (!supported_d(D)) return MINIKV_ERR_UNSUPPORTED;
+    if (misaligned(k_new) || misaligned(v_new) || misaligned(counts) || misaligned(k_codes) || misaligned(k_sz) ||
+        misaligned(v_codes) || misaligned(v_sz) || misaligned(k_res) || misaligned(v_res))
+        return MINIKV_ERR_ALIGN;
+    return status_of(minikv::launch_stream_step_append(k_new, v_new, B, Hkv, D, cap, counts, k_codes, k_sz, v_codes,
+                                                       v_sz, k_res, v_res, as_stream(stream)));
+}
+
+size_t minikv_stream_step_decode_ws_bytes(int B, int Hq, int Hkv, int cap, int D) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || cap < MINIKV_GROUP || cap % MINIKV_GROUP || !supported_d(D))
+        return 0;
+    const minikv::DecodePlan plan = minikv::decode_plan(B, Hq, Hkv, cap, D);
+    return minikv::stream_decode_ws_bytes(B, Hq, D, cap, MINIKV_GROUP - 1, plan);
+}
+
+int minikv_stream_step_decode(const void* q, int B, int Hq, int Hkv, int D, int cap, const int32_t* counts,
+                              const uint8_t* k_codes, const uint32_t* k_sz, const uint8_t* v_codes,
+                              const uint32_t* v_sz, const void* k_res, const void* v_res, float sm_scale, void* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+    if (!q || !out || !counts || !k_codes || !k_sz || !v_codes || !v_sz || !k_res || !v_res || !ws)
+        return MINIKV_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || cap < MINIKV_GROUP || cap % MINIKV_GROUP) return MINIKV_ERR_SHAPE;
+    if (!supported_d(D)) return MINIKV_ERR_UNSUPPORTED;
+    const int R = Hq / Hkv;
+    if (R != 1 && R != 2 && R != 4) return MINIKV_ERR_UNSUPPORTED;
+    if (misaligned(q) || misaligned(out) || misaligned(ws) || misaligned(counts) || misaligned(k_codes) ||
+        misaligned(k_sz) || misaligned(v_codes) || misaligned(v_sz) || misaligned(k_res) || misaligned(v_res))
+        return MINIKV_ERR_ALIGN;
+    const minikv::DecodePlan plan = minikv::decode_plan(B, Hq, Hkv, cap, D);
+    if (ws_bytes < minikv::stream_decode_ws_bytes(B, Hq, D, cap, MINIKV_GROUP - 1, plan)) return MINIKV_ERR_WORKSPACE;
+    return status_of(minikv::launch_stream_decode_counted(q, k_codes, k_sz, v_codes, v_sz, B, Hq, Hkv, D, cap, counts,
+                                                          k_res, v_res, resolve_scale(sm_scale, D), out, ws, plan,
+                                                          as_stream(stream)));
+}
+
 }  // extern "C"

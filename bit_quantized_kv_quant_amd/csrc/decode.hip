@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes, const uint32_t* __restrict__ k_sz,
     const uint8_t* __restrict__ v_codes, const uint32_t* __restrict__ v_sz, int n, int tok_stride, int grp_stride,
     int chunk, int splits, int ws_splits, int n_items, float scale_log2, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml, __bf16* __restrict__ out) {
+    float* __restrict__ ws_ml, __bf16* __restrict__ out, const int32_t* __restrict__ counts) {
     constexpr int NG = D / 32;  // 32-channel groups: key K blocks and value scale groups
     constexpr int NT = D / 16;  // 16-channel value tiles
     constexpr int GPL = NG * R / 4 > 1 ? NG * R / 4 : 1;  // value groups per lane in the weight prep
@@ -213,6 +213,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const int nwaves = gridDim.x * 4;
     int item = blockIdx.x * 4 + wave;
     if (item >= n_items) return;  // wave-uniform; the kernel has no workgroup barrier
+    // a device-side streaming step: the packed token count is read here (the
+    // split plan covers the capacity n; ranges past the count are empty parts)
+    if (counts) n = max(0, min(n, counts[0]));
 
     // never-written LDS positions must read as zero: key K positions >= D, value piece 3
     {
@@ -313,9 +316,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
             qb[r][1] = qr[c0 + 2];
         }
     };
-    auto pos_of = [&](int it) {  // first step of an item
+    auto pos_of = [&](int it) {  // first step of an item (an empty range past n)
         const int t0 = (it % splits) * chunk;
-        return Pos{it / splits, t0 / kStep, min(n, t0 + chunk)};
+        return Pos{it / splits, t0 / kStep, max(t0, min(n, t0 + chunk))};
     };
 
     // online-softmax state of this lane's head (uniform within its 16-lane row)
@@ -573,8 +576,10 @@ template <int D>
 __global__ __launch_bounds__(64) void decode_residual_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_res, const uint16_t* __restrict__ v_res,
     int res_stride, int n_res, int Hq, int Hkv, float scale_log2, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml, int ws_splits, int slot, __bf16* __restrict__ out) {
+    float* __restrict__ ws_ml, int ws_splits, int slot, __bf16* __restrict__ out,
+    const int32_t* __restrict__ counts) {
     constexpr int C = D / kWave;  // channels per lane
+    if (counts) n_res = max(0, min(n_res, counts[1]));  // device-side step: an empty window is an empty part
     const int row = blockIdx.x;   // b * Hq + h
     const int b = row / Hq, h = row % Hq;
     const int g = h / (Hq / Hkv);
@@ -646,6 +651,8 @@ int resident_workgroups() {
 // Where a decode reads: the packed region (n tokens; strides of its layout)
 // and an optional exact residual (n_res tokens of res_stride slots).
 struct DecodeSrc {
+    // with counts (device int32 {n_packed, n_res, ...}), n and n_res are upper
+    // bounds and the kernels read the actual counts
     const uint8_t* k_codes;
     const uint32_t* k_sz;
     const uint8_t* v_codes;
@@ -654,6 +661,7 @@ struct DecodeSrc {
     const uint16_t* k_res;
     const uint16_t* v_res;
     int res_stride, n_res;
+    const int32_t* counts;
 };
 
 template <int D, int R>
@@ -669,14 +677,14 @@ hipError_t launch_dr(const void* q, const DecodeSrc& src, int B, int Hq, int Hkv
         hipLaunchKernelGGL((decode_partial_kernel<D, R>), dim3((unsigned)grid), dim3(256), 0, stream,
                            static_cast<const uint16_t*>(q), src.k_codes, src.k_sz, src.v_codes, src.v_sz, src.n,
                            src.tok_stride, src.grp_stride, plan.chunk, plan.splits, parts, (int)items, scale_log2,
-                           ws_acc, ws_ml, static_cast<__bf16*>(out));
+                           ws_acc, ws_ml, static_cast<__bf16*>(out), src.counts);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (src.n_res > 0) {
         hipLaunchKernelGGL((decode_residual_kernel<D>), dim3(B * Hq), dim3(kWave), 0, stream,
                            static_cast<const uint16_t*>(q), src.k_res, src.v_res, src.res_stride, src.n_res, Hq, Hkv,
-                           scale_log2, ws_acc, ws_ml, parts, parts - 1, static_cast<__bf16*>(out));
+                           scale_log2, ws_acc, ws_ml, parts, parts - 1, static_cast<__bf16*>(out), src.counts);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -726,7 +734,7 @@ hipError_t launch_decode(const void* q, const uint8_t* k_codes, const uint32_t* 
                          void* out, void* ws, const DecodePlan& plan, hipStream_t stream) {
     const float scale_log2 = sm_scale * kLog2e;
     const DecodeSrc src{k_codes, k_sz, v_codes, v_sz, n_keep, n_keep, (n_keep + kGroup - 1) / kGroup,
-                        nullptr, nullptr, 0, 0};
+                        nullptr, nullptr, 0, 0, nullptr};
     if (D == 128) return launch_d<128>(q, src, B, Hq, Hkv, scale_log2, out, ws, plan, stream);
     return launch_d<64>(q, src, B, Hq, Hkv, scale_log2, out, ws, plan, stream);
 }
@@ -737,7 +745,22 @@ hipError_t launch_stream_decode(const void* q, const uint8_t* k_codes, const uin
                                 void* ws, const DecodePlan& plan, hipStream_t stream) {
     const float scale_log2 = sm_scale * kLog2e;
     const DecodeSrc src{k_codes, k_sz, v_codes, v_sz, n_packed, cap, cap / kGroup,
-                        static_cast<const uint16_t*>(k_res), static_cast<const uint16_t*>(v_res), kGroup, n_res};
+                        static_cast<const uint16_t*>(k_res), static_cast<const uint16_t*>(v_res), kGroup, n_res,
+                        nullptr};
+    if (D == 128) return launch_d<128>(q, src, B, Hq, Hkv, scale_log2, out, ws, plan, stream);
+    return launch_d<64>(q, src, B, Hq, Hkv, scale_log2, out, ws, plan, stream);
+}
+
+hipError_t launch_stream_decode_counted(const void* q, const uint8_t* k_codes, const uint32_t* k_sz,
+                                        const uint8_t* v_codes, const uint32_t* v_sz, int B, int Hq, int Hkv, int D,
+                                        int cap, const int32_t* counts, const void* k_res, const void* v_res,
+                                        float sm_scale, void* out, void* ws, const DecodePlan& plan,
+                                        hipStream_t stream) {
+    const float scale_log2 = sm_scale * kLog2e;
+    // bounds: the whole capacity and a full window; the kernels read the counts
+    const DecodeSrc src{k_codes, k_sz, v_codes, v_sz, cap, cap, cap / kGroup,
+                        static_cast<const uint16_t*>(k_res), static_cast<const uint16_t*>(v_res), kGroup,
+                        kGroup - 1, counts};
     if (D == 128) return launch_d<128>(q, src, B, Hq, Hkv, scale_log2, out, ws, plan, stream);
     return launch_d<64>(q, src, B, Hq, Hkv, scale_log2, out, ws, plan, stream);
 }

@@ -22,6 +22,17 @@ hipError_t launch_stream_pack(const void* k, const void* v, bool bf16, const int
 hipError_t launch_stream_append(const void* k, const void* v, const int32_t* idx, int idx_stride, int B, int Hkv,
                                 int T_ctx, int D, int n, int slot, void* k_res, void* v_res, hipStream_t stream);
 
+// Device-side generation step (counts = device int32 {n_packed, n_res,
+// overflow, 0}): set the counts; append one token per (sequence, KV head) into
+// window slot n_res, pack a filled window at n_packed, advance the counts.
+hipError_t launch_stream_set_counts(int32_t* counts, int n_packed, int n_res, hipStream_t stream);
+hipError_t launch_stream_pack_counted(const void* k_res, const void* v_res, int B, int Hkv, int D, int cap,
+                                     const int32_t* counts, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes,
+                                     uint32_t* v_sz, hipStream_t stream);
+hipError_t launch_stream_step_append(const void* k_new, const void* v_new, int B, int Hkv, int D, int cap,
+                                     int32_t* counts, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes,
+                                     uint32_t* v_sz, void* k_res, void* v_res, hipStream_t stream);
+
 hipError_t launch_select_topk(const float* scores, int B, int Hkv, int T_ctx, int n_heavy,
                               int n_recent, int32_t* idx, hipStream_t stream);
 
@@ -49,6 +60,14 @@ hipError_t launch_stream_decode(const void* q, const uint8_t* k_codes, const uin
 // Pass 1; with window > 0 (only where prefill_fuses_scores) it also writes the
 // window scores of pass 2 in the same launch.
 bool prefill_fuses_scores(int B, int T_ctx, int Hq, int Hkv, int window);
+// Streaming decode with the counts read on the device: planned for the whole
+// capacity (plan of cap tokens), always a residual part.
+hipError_t launch_stream_decode_counted(const void* q, const uint8_t* k_codes, const uint32_t* k_sz,
+                                        const uint8_t* v_codes, const uint32_t* v_sz, int B, int Hq, int Hkv, int D,
+                                        int cap, const int32_t* counts, const void* k_res, const void* v_res,
+                                        float sm_scale, void* out, void* ws, const DecodePlan& plan,
+                                        hipStream_t stream);
+
 hipError_t launch_prefill(const void* q, const void* k, const void* v, int B, int T_ctx, int Hq,
                           int Hkv, int D, float sm_scale, void* o, float* lse, int window, float* scores,
                           hipStream_t stream);

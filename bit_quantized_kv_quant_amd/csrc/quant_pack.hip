@@ -296,7 +296,13 @@ template <typename T, int D>
 __global__ __launch_bounds__(128) void quant_pack_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, PackGeom pg,
     int Hkv, uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz, uint8_t* __restrict__ v_codes,
-    uint32_t* __restrict__ v_sz) {
+    uint32_t* __restrict__ v_sz, const int32_t* __restrict__ counts) {
+    if (counts) {  // window pack of a device-side step: only when the token just appended filled the window
+        if (counts[2] != 0 || counts[1] != kGroup - 1 || counts[0] < 0 || counts[0] % kGroup != 0 ||
+            counts[0] + kGroup > pg.tok_stride)
+            return;
+        pg.tok0 = counts[0];
+    }
     const bool full = (blockIdx.x + 1) * kGroup <= pg.n;
     if (threadIdx.x < kWave) {
         if (full) pack_keys_full<T, D>(k, idx, T_ctx, pg, Hkv, k_codes, k_sz);
@@ -310,10 +316,10 @@ __global__ __launch_bounds__(128) void quant_pack_kernel(
 template <typename T, int D>
 hipError_t launch_typed(const void* k, const void* v, const int32_t* idx, int B, int Hkv, int T_ctx,
                         const PackGeom& pg, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes, uint32_t* v_sz,
-                        hipStream_t stream) {
+                        hipStream_t stream, const int32_t* counts = nullptr) {
     const int G = (pg.n + kGroup - 1) / kGroup;
     hipLaunchKernelGGL((quant_pack_kernel<T, D>), dim3(G, Hkv, B), dim3(128), 0, stream, static_cast<const T*>(k),
-                       static_cast<const T*>(v), idx, T_ctx, pg, Hkv, k_codes, k_sz, v_codes, v_sz);
+                       static_cast<const T*>(v), idx, T_ctx, pg, Hkv, k_codes, k_sz, v_codes, v_sz, counts);
     return hipGetLastError();
 }
 
@@ -335,6 +341,17 @@ hipError_t launch_quant_pack(const void* k, const void* v, bool bf16, const int3
                              uint8_t* v_codes, uint32_t* v_sz, hipStream_t stream) {
     const PackGeom pg{n_keep, n_keep, n_keep, (n_keep + kGroup - 1) / kGroup, 0};
     return launch_geom(k, v, bf16, idx, B, Hkv, T_ctx, D, pg, k_codes, k_sz, v_codes, v_sz, stream);
+}
+
+hipError_t launch_stream_pack_counted(const void* k_res, const void* v_res, int B, int Hkv, int D, int cap,
+                                     const int32_t* counts, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes,
+                                     uint32_t* v_sz, hipStream_t stream) {
+    const PackGeom pg{kGroup, kGroup, cap, cap / kGroup, 0};  // tok0 comes from counts
+    if (D == 128)
+        return launch_typed<uint16_t, 128>(k_res, v_res, nullptr, B, Hkv, kGroup, pg, k_codes, k_sz, v_codes, v_sz,
+                                           stream, counts);
+    return launch_typed<uint16_t, 64>(k_res, v_res, nullptr, B, Hkv, kGroup, pg, k_codes, k_sz, v_codes, v_sz, stream,
+                                      counts);
 }
 
 hipError_t launch_stream_pack(const void* k, const void* v, bool bf16, const int32_t* idx, int idx_stride, int B,

@@ -232,6 +232,47 @@ int minikv_stream_decode(const void *q, int B, int Hq, int Hkv, int D, int cap, 
 /* Workspace bytes minikv_stream_decode needs (0 for invalid sizes). */
 size_t minikv_stream_decode_ws_bytes(int B, int Hq, int Hkv, int n_packed, int n_res, int D);
 
+/*
+ * A generation step with the counts in device memory, so that the step is a
+ * fixed sequence of launches a HIP graph can capture and replay (the host no
+ * longer passes n_packed / n_res).  counts: device int32[4], caller-owned,
+ * {n_packed, n_res, overflow flag, 0}; the same streaming layout as above.
+ *
+ * minikv_stream_set_counts writes {n_packed, n_res, 0, 0} with a kernel (no
+ * memset node).  Errors: NULL; SHAPE (cap not a positive multiple of 32,
+ * n_packed not a multiple of 32 or > cap, n_res outside 0..31); ALIGN; LAUNCH.
+ *
+ * minikv_stream_step_append appends k_new, v_new bf16 [B][Hkv][D] (one token
+ * per sequence and KV head) in three launches: the token into window slot
+ * n_res; the window packed at token n_packed when that token filled it (the
+ * same quantisation as minikv_stream_pack); counts advanced (n_res + 1, or
+ * n_packed + 32 and n_res = 0 after a pack).  When a full window cannot be
+ * packed (n_packed + 32 > cap) the overflow flag is set, the window is kept,
+ * and every later step writes nothing until the counts are set again: the
+ * caller reads the flag to detect it.  Errors: NULL; SHAPE (sizes, cap);
+ * UNSUPPORTED (D); ALIGN; LAUNCH.
+ *
+ * minikv_stream_step_decode is minikv_stream_decode with the counts read on
+ * the device: the split plan covers all cap tokens (token ranges past n_packed
+ * contribute empty parts) and the window is always a part (empty at n_res 0).
+ * Workspace: minikv_stream_step_decode_ws_bytes (0 for invalid sizes).
+ * Errors: NULL (any pointer, ws included); SHAPE; UNSUPPORTED (D, Hq/Hkv not
+ * 1, 2 or 4); ALIGN; WORKSPACE; LAUNCH.  Calls that overlap on one counts
+ * buffer race.
+ */
+int minikv_stream_set_counts(int32_t *counts, int n_packed, int n_res, int cap, void *stream);
+
+int minikv_stream_step_append(const void *k_new, const void *v_new, int B, int Hkv, int D, int cap,
+                              int32_t *counts, uint8_t *k_codes, uint32_t *k_sz, uint8_t *v_codes,
+                              uint32_t *v_sz, void *k_res, void *v_res, void *stream);
+
+size_t minikv_stream_step_decode_ws_bytes(int B, int Hq, int Hkv, int cap, int D);
+
+int minikv_stream_step_decode(const void *q, int B, int Hq, int Hkv, int D, int cap, const int32_t *counts,
+                              const uint8_t *k_codes, const uint32_t *k_sz, const uint8_t *v_codes,
+                              const uint32_t *v_sz, const void *k_res, const void *v_res, float sm_scale,
+                              void *out, void *ws, size_t ws_bytes, void *stream);
+
 /* ---- host helpers (no GPU work) ---- */
 
 /* Bytes of the packed cache: per (sequence, KV head), G = ceil(n/32):

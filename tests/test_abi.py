@@ -188,6 +188,50 @@ def test_stream_decode_validation(L):
     assert call(ws=None) == _lib.ERR_WORKSPACE
 
 
+def test_device_step_validation(L):
+    sc = L.minikv_stream_set_counts
+    assert sc(None, 0, 0, 64, None) == _lib.ERR_NULL
+    assert sc(A, 16, 0, 64, None) == _lib.ERR_SHAPE      # packed tokens not whole groups
+    assert sc(A, 96, 0, 64, None) == _lib.ERR_SHAPE      # beyond the capacity
+    assert sc(A, 0, 32, 64, None) == _lib.ERR_SHAPE      # the window holds at most 31
+    assert sc(A, 0, 0, 48, None) == _lib.ERR_SHAPE       # capacity not whole groups
+    assert sc(MIS, 0, 0, 64, None) == _lib.ERR_ALIGN
+
+    ap = L.minikv_stream_step_append
+
+    def app(k=A, B=2, D=128, cap=128, counts=A, k_res=A):
+        return ap(k, A, B, 4, D, cap, counts, A, A, A, A, k_res, A, None)
+
+    assert app(k=None) == _lib.ERR_NULL
+    assert app(counts=None) == _lib.ERR_NULL
+    assert app(k_res=None) == _lib.ERR_NULL
+    assert app(B=0) == _lib.ERR_SHAPE
+    assert app(cap=100) == _lib.ERR_SHAPE
+    assert app(D=96) == _lib.ERR_UNSUPPORTED
+    assert app(counts=MIS) == _lib.ERR_ALIGN
+
+    need = L.minikv_stream_step_decode_ws_bytes(2, 8, 4, 128, 128)
+    assert need > 0
+    assert L.minikv_stream_step_decode_ws_bytes(2, 8, 3, 128, 128) == 0
+    assert L.minikv_stream_step_decode_ws_bytes(2, 8, 4, 100, 128) == 0
+    # planned for the whole capacity, with a window part: at least the host-count workspace
+    assert need >= L.minikv_stream_decode_ws_bytes(2, 8, 4, 128, 31, 128)
+    f = L.minikv_stream_step_decode
+
+    def dec(q=A, Hq=8, cap=128, counts=A, ws=A, ws_bytes=need, D=128):
+        return f(q, 2, Hq, 4, D, cap, counts, A, A, A, A, A, A, 0.0, A, ws, ws_bytes, None)
+
+    assert dec(q=None) == _lib.ERR_NULL
+    assert dec(counts=None) == _lib.ERR_NULL
+    assert dec(ws=None) == _lib.ERR_NULL
+    assert dec(Hq=6) == _lib.ERR_SHAPE
+    assert dec(cap=100) == _lib.ERR_SHAPE
+    assert dec(Hq=32) == _lib.ERR_UNSUPPORTED
+    assert dec(D=96) == _lib.ERR_UNSUPPORTED
+    assert dec(counts=MIS) == _lib.ERR_ALIGN
+    assert dec(ws_bytes=need - 4) == _lib.ERR_WORKSPACE
+
+
 def test_host_budget_helpers_match_oracle(L):
     for T in (1, 7, 256, 4096, 8192, 16384, 44000, 65536):
         for pct in (5, 15, 30, 100):

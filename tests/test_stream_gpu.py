@@ -117,3 +117,118 @@ def test_stream_residual_only(dev):
     out = c.decode(torch.from_numpy(q).to(dev).to(torch.bfloat16))
     torch.cuda.synchronize()
     assert_attn_close(to_np(out), oracle.stream_decode_ref(q, oracle.stream_init_ref(k, v, idx)), "residual only")
+
+
+# ---------------------------------------------------------------------------
+# device-side generation step (counts in device memory) and its graph replays
+# ---------------------------------------------------------------------------
+
+def _start(dev, seed, B, Hkv, T, D, n_sel, cap):
+    rng, k, v = _inputs(seed, B, Hkv, T, D)
+    idx = np.sort(np.stack([[rng.choice(T, n_sel, replace=False) for _ in range(Hkv)] for _ in range(B)]), -1)
+    kd = torch.from_numpy(k).to(dev).to(torch.bfloat16)
+    vd = torch.from_numpy(v).to(dev).to(torch.bfloat16)
+    c = mk.StreamCache.alloc(B, Hkv, cap, D, dev).init(kd, vd, torch.from_numpy(idx.astype(np.int32)).to(dev))
+    return rng, c, oracle.stream_init_ref(k, v, idx)
+
+
+def _token(rng, B, H, D, scale=1.0):
+    return synth.bf16_round(rng.standard_normal((B, H, D)).astype(np.float32) * scale)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,n_sel,steps", [(8, 2, 128, 150, 70), (4, 4, 64, 20, 45), (2, 2, 128, 64, 33)])
+def test_device_step_matches_oracle(dev, Hq, Hkv, D, n_sel, steps):
+    """step_append / step_decode (counts read on the device) against the oracle at every step."""
+    say("device step Hq", Hq, "Hkv", Hkv, "D", D, "selection", n_sel, "steps", steps)
+    B, T = 2, 600
+    cap = 32 * ((n_sel + steps) // 32 + 2)
+    rng, c, st = _start(dev, n_sel + 1, B, Hkv, T, D, n_sel, cap)
+    c.to_device_counts()
+    ws = torch.empty(c.step_ws_bytes(Hq), dtype=torch.uint8, device=dev)
+    for step in range(steps):
+        kn, vn = _token(rng, B, Hkv, D), _token(rng, B, Hkv, D, 0.5)
+        c.step_append(torch.from_numpy(kn).to(dev).to(torch.bfloat16), torch.from_numpy(vn).to(dev).to(torch.bfloat16))
+        st = oracle.stream_append_ref(st, kn, vn)
+        q = _token(rng, B, Hq, D)
+        out = c.step_decode(torch.from_numpy(q).to(dev).to(torch.bfloat16), ws=ws)
+        torch.cuda.synchronize()
+        assert_attn_close(to_np(out), oracle.stream_decode_ref(q, st), f"device step {step}")
+        if step % 16 == 15 or step == steps - 1:
+            c.from_device_counts()
+            _check_state(c, st)
+
+
+def test_device_step_graph_replays(dev):
+    """One captured generation step over two layers (append + decode each), replayed 40 times with
+    new inputs copied in and eager work between replays; every replay against the oracle."""
+    say("device step in a HIP graph")
+    B, Hq, Hkv, T, D, n_sel = 2, 8, 2, 500, 128, 90
+    cap = 256
+    layers = []
+    for l in range(2):
+        rng, c, st = _start(dev, 50 + l, B, Hkv, T, D, n_sel, cap)
+        c.to_device_counts()
+        layers.append([rng, c, st, torch.empty(c.step_ws_bytes(Hq), dtype=torch.uint8, device=dev)])
+    # one eager step on a scratch cache of the same shapes (host-side launch set-up happens outside the capture)
+    _, scratch, _ = _start(dev, 99, B, Hkv, T, D, n_sel, cap)
+    scratch.to_device_counts()
+    scratch.step_append(torch.zeros((B, Hkv, D), dtype=torch.bfloat16, device=dev),
+                        torch.zeros((B, Hkv, D), dtype=torch.bfloat16, device=dev))
+    scratch.step_decode(torch.zeros((B, Hq, D), dtype=torch.bfloat16, device=dev))
+    k_in = torch.empty((B, Hkv, D), dtype=torch.bfloat16, device=dev)
+    v_in = torch.empty_like(k_in)
+    q_in = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    outs = [torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev) for _ in layers]
+    torch.cuda.synchronize()
+    # capture on a side stream; the capture itself runs nothing
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for (rng, c, st, ws), out in zip(layers, outs):
+                c.step_append(k_in, v_in)
+                c.step_decode(q_in, out=out, ws=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    for rep in range(40):
+        kn, vn, q = _token(rng, B, Hkv, D), _token(rng, B, Hkv, D, 0.5), _token(rng, B, Hq, D)
+        k_in.copy_(torch.from_numpy(kn).to(torch.bfloat16))
+        v_in.copy_(torch.from_numpy(vn).to(torch.bfloat16))
+        q_in.copy_(torch.from_numpy(q).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, layer in enumerate(layers):
+            layer[2] = oracle.stream_append_ref(layer[2], kn, vn)
+            assert_attn_close(to_np(outs[i]), oracle.stream_decode_ref(q, layer[2]), f"replay {rep} layer {i}")
+        _ = (q_in.float() * 2).sum().item()  # eager work between replays
+    for rng_, c, st, ws in layers:
+        c.from_device_counts()
+        _check_state(c, st)
+        assert c.n_packed == 32 * ((n_sel + 40) // 32) and c.n_res == (n_sel + 40) % 32
+
+
+def test_device_step_overflow_sets_flag(dev):
+    """A full window that does not fit the capacity sets the flag; nothing is written out of bounds."""
+    say("device step overflow")
+    B, Hq, Hkv, T, D = 1, 2, 2, 200, 128
+    rng, c, st = _start(dev, 7, B, Hkv, T, D, 63, 64)   # 32 packed + 31 in the window
+    c.to_device_counts()
+    kn, vn = _token(rng, B, Hkv, D), _token(rng, B, Hkv, D)   # fills the window: packed at 32 (cap 64 reached)
+    c.step_append(torch.from_numpy(kn).to(dev).to(torch.bfloat16), torch.from_numpy(vn).to(dev).to(torch.bfloat16))
+    st = oracle.stream_append_ref(st, kn, vn)
+    c.from_device_counts()
+    _check_state(c, st)
+    assert c.n_packed == 64 and c.n_res == 0
+    packed0 = [t.clone() for t in (c.k_codes, c.k_sz, c.v_codes, c.v_sz)]
+    for _ in range(32):  # 31 fill the window again, the 32nd cannot be packed
+        kn, vn = _token(rng, B, Hkv, D), _token(rng, B, Hkv, D)
+        c.step_append(torch.from_numpy(kn).to(dev).to(torch.bfloat16), torch.from_numpy(vn).to(dev).to(torch.bfloat16))
+    torch.cuda.synchronize()
+    counts = c.counts.cpu().tolist()
+    assert counts[:3] == [64, 31, 1]
+    with pytest.raises(ValueError):
+        c.from_device_counts()
+    # the packed region is untouched after the overflow
+    for a, b in zip((c.k_codes, c.k_sz, c.v_codes, c.v_sz), packed0):
+        assert torch.equal(a, b)
