@@ -189,7 +189,10 @@ def prefill_layer(torch, mk, synth, wl, reps):
 def decode_stream(torch, mk, synth, wl, steps):
     """Generation over a streaming cache per layer: each step appends one token per
     (sequence, KV head) to every layer (packing every 32nd) and decodes one query per
-    sequence through all layers.  Kept-token K/V of the prompt are drawn directly."""
+    sequence through all layers.  Kept-token K/V of the prompt are drawn directly.
+    Timed twice: with host-side counts (Python decides each pack), and with the
+    counts on the device, one step of all layers captured in a HIP graph and
+    replayed per token (graph_*)."""
     dev = torch.device("cuda:0")
     B, n = wl.B, mk.keep_count(wl.T, wl.budget_pct)
     cap = 32 * ((n + steps) // 32 + 1)
@@ -222,12 +225,52 @@ def decode_stream(torch, mk, synth, wl, steps):
     ms = e0.elapsed_time(e1) / steps
     packed_bytes = sum(mk.packed_bytes(B, wl.Hkv, c.n_packed, wl.D) for c in caches)
     flushes = (res0 + steps) // 32
-    del caches
+
+    # ---- the same generation with device-side counts: one step (all layers) is a
+    # fixed launch sequence, captured once in a HIP graph and replayed per token ----
+    for l, c in enumerate(caches):  # back to the prompt's state
+        k, v = synth.make_kept_kv(wl, n, dev, seed=wl.seed * 100000 + l * 1000 + 7, B=B)
+        idx = torch.arange(n, dtype=torch.int32, device=dev).expand(B, wl.Hkv, n).contiguous()
+        c.init(k, v, idx).to_device_counts()
+        del k, v, idx
+    k_in, v_in, q_in = kn[0].clone(), vn[0].clone(), qs[0].clone()
+    ws_g = torch.empty(max(16, caches[0].step_ws_bytes(wl.Hq)), dtype=torch.uint8, device=dev)
+    scratch = mk.StreamCache.alloc(B, wl.Hkv, cap, wl.D, dev)
+    scratch.n_packed, scratch.n_res = 0, 0
+    scratch.to_device_counts()
+    scratch.step_append(k_in, v_in)  # launch set-up outside the capture
+    scratch.step_decode(q_in, out=out, ws=ws_g)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for c in caches:
+                c.step_append(k_in, v_in)
+                c.step_decode(q_in, out=out, ws=ws_g)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    g0.record()
+    for s in range(steps):
+        k_in.copy_(kn[s % pool])  # the step's new token and query
+        v_in.copy_(vn[s % pool])
+        q_in.copy_(qs[s % pool])
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    gwall = time.perf_counter() - wall0
+    gms = g0.elapsed_time(g1) / steps
+    caches[0].from_device_counts()  # raises if a window could not be packed
+    g_packed = caches[0].n_packed
+    del caches, graph, scratch
     torch.cuda.empty_cache()
     return {"workload": wl.name, "batch": B, "layers": wl.layers, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
             "prompt_kept_tokens": n, "steps": steps, "packs_per_layer": flushes,
             "packed_GB_at_end": packed_bytes / 1e9, "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3),
-            "host_ms_per_step": wall * 1e3 / steps}
+            "host_ms_per_step": wall * 1e3 / steps,
+            "graph_ms_per_step": gms, "graph_tokens_per_s": B / (gms * 1e-3),
+            "graph_host_ms_per_step": gwall * 1e3 / steps, "graph_packed_tokens_at_end": g_packed}
 
 
 

@@ -203,7 +203,7 @@ class StreamCache:
     D: int
     n_packed: int = 0
     n_res: int = 0
-    counts: torch.Tensor = None  # int32 [4] {n_packed, n_res, overflow, 0}: the device-side step's counts
+    counts: torch.Tensor = None  # int32 [4] {n_packed, n_res, overflow, ticket}: the device-side step's counts
 
     @staticmethod
     def alloc(B, Hkv, cap, D, device="cuda"):

@@ -197,7 +197,7 @@ template <int D, int R>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes, const uint32_t* __restrict__ k_sz,
     const uint8_t* __restrict__ v_codes, const uint32_t* __restrict__ v_sz, int n, int tok_stride, int grp_stride,
-    int chunk, int splits, int ws_splits, int n_items, float scale_log2, float* __restrict__ ws_acc,
+    int chunk, int splits, int ws_splits, int direct, int n_items, float scale_log2, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, __bf16* __restrict__ out, const int32_t* __restrict__ counts) {
     constexpr int NG = D / 32;  // 32-channel groups: key K blocks and value scale groups
     constexpr int NT = D / 16;  // 16-channel value tiles
@@ -503,12 +503,12 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 #pragma unroll
             for (int T = 0; T < NT; ++T) {
                 const float x = acc[T] + s_z[wave][blk][T / 2];
-                if (ws_splits == 1)
+                if (direct)
                     out[row * D + 16 * T + col] = (__bf16)(x / lsum);
                 else
                     ws_acc[(row * ws_splits + split) * D + 16 * T + col] = x;
             }
-            if (ws_splits > 1 && col == 0) {
+            if (!direct && col == 0) {
                 ws_ml[(row * ws_splits + split) * 2 + 0] = m_run;
                 ws_ml[(row * ws_splits + split) * 2 + 1] = lsum;
             }
@@ -520,19 +520,84 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     }
 }
 
+// Exact part of a streaming decode for one (sequence, query head) row, by one
+// wave: the residual tokens (bf16 K / V, at most 31, slots [B][Hkv][res_stride][D]).
+// Returns m and the sum of 2^(l - m) (l = q.k in log2 units) and leaves
+// x[c] = sum of 2^(l - m) v[lane + 64 c].
+template <int D>
+__device__ __forceinline__ void residual_part(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_res,
+                                              const uint16_t* __restrict__ v_res, int res_stride, int n_res, int Hq,
+                                              int Hkv, float scale_log2, int row, int lane, float& m_out,
+                                              float& l_out, float (&x)[D / kWave]) {
+    constexpr int C = D / kWave;  // channels per lane
+    const int b = row / Hq, h = row % Hq;
+    const int g = h / (Hq / Hkv);
+    const uint16_t* kr = k_res + ((size_t)b * Hkv + g) * res_stride * D;
+    const uint16_t* vr = v_res + ((size_t)b * Hkv + g) * res_stride * D;
+    float qc[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) qc[c] = bf16_bits_to_f32(q[(size_t)row * D + lane + kWave * c]);
+    float l[kGroup];
+    float m = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kGroup - 1; ++t) {
+        l[t] = -INFINITY;
+        if (t < n_res) {
+            float d = 0.0f;
+#pragma unroll
+            for (int c = 0; c < C; ++c) d = fmaf(qc[c], bf16_bits_to_f32(kr[(size_t)t * D + lane + kWave * c]), d);
+            l[t] = dpp_sum<kWave>(d) * scale_log2;
+            m = fmaxf(m, l[t]);
+        }
+    }
+    float lsum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) x[c] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kGroup - 1; ++t) {
+        if (t < n_res) {
+            const float p = exp2f(l[t] - m);
+            lsum += p;
+#pragma unroll
+            for (int c = 0; c < C; ++c) x[c] = fmaf(p, bf16_bits_to_f32(vr[(size_t)t * D + lane + kWave * c]), x[c]);
+        }
+    }
+    m_out = m;
+    l_out = lsum;
+}
+
 // Merge the token ranges of one (sequence, query head): the range maxima and
 // weights 2^(m_s - M) are computed cooperatively and kept in LDS, then every
-// thread (one channel) sums its partials with several loads in flight.
+// thread (one channel) sums its partials with several loads in flight.  With
+// k_res, wave 0 first computes the exact window part (residual_part) and it is
+// merged as one more range.
 constexpr int kMaxSplits = 256;
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ ws_acc,
                                                            const float* __restrict__ ws_ml, int splits,
-                                                           __bf16* __restrict__ out) {
+                                                           __bf16* __restrict__ out, const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ k_res,
+                                                           const uint16_t* __restrict__ v_res, int res_stride,
+                                                           int n_res, int Hq, int Hkv, float scale_log2,
+                                                           const int32_t* __restrict__ counts) {
     constexpr int NW = D / kWave;
     __shared__ float s_w[kMaxSplits];
     __shared__ float s_part[2][NW];
+    __shared__ float s_res[D + 2];  // window part: sum 2^(l - m) v per channel, then m, sum 2^(l - m)
     const int bh = blockIdx.x;
     const int t = threadIdx.x;
+    const bool res = k_res != nullptr;
+    if (res && t < kWave) {
+        if (counts) n_res = max(0, min(n_res, counts[1]));
+        float m_r, l_r, x[D / kWave];
+        residual_part<D>(q, k_res, v_res, res_stride, n_res, Hq, Hkv, scale_log2, bh, t, m_r, l_r, x);
+#pragma unroll
+        for (int c = 0; c < D / kWave; ++c) s_res[t + kWave * c] = x[c];
+        if (t == 0) {
+            s_res[D] = m_r;
+            s_res[D + 1] = l_r;
+        }
+    }
     const float* ml = ws_ml + (size_t)bh * splits * 2;
     float m = -INFINITY;
     for (int s = t; s < splits; s += D) m = fmaxf(m, ml[2 * s]);
@@ -542,6 +607,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     float M = s_part[0][0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) M = fmaxf(M, s_part[0][w]);
+    if (res) M = fmaxf(M, s_res[D]);
     float l = 0.0f;
     for (int s = t; s < splits; s += D) {
         const float w = exp2f(ml[2 * s] - M);
@@ -564,7 +630,13 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
         o3 = fmaf(a[(size_t)(s + 3) * D], s_w[s + 3], o3);
     }
     for (; s < splits; ++s) o0 = fmaf(a[(size_t)s * D], s_w[s], o0);
-    out[(size_t)bh * D + t] = (__bf16)(((o0 + o1) + (o2 + o3)) / L);
+    float o = (o0 + o1) + (o2 + o3);
+    if (res) {
+        const float w = exp2f(s_res[D] - M);  // 0 for an empty window (m = -inf)
+        L = fmaf(s_res[D + 1], w, L);
+        o = fmaf(s_res[t], w, o);
+    }
+    out[(size_t)bh * D + t] = (__bf16)(o / L);
 }
 
 // Exact part of a streaming decode: the residual tokens (bf16 K / V, at most
@@ -581,39 +653,9 @@ __global__ __launch_bounds__(64) void decode_residual_kernel(
     constexpr int C = D / kWave;  // channels per lane
     if (counts) n_res = max(0, min(n_res, counts[1]));  // device-side step: an empty window is an empty part
     const int row = blockIdx.x;   // b * Hq + h
-    const int b = row / Hq, h = row % Hq;
-    const int g = h / (Hq / Hkv);
     const int lane = threadIdx.x;
-    const uint16_t* kr = k_res + ((size_t)b * Hkv + g) * res_stride * D;
-    const uint16_t* vr = v_res + ((size_t)b * Hkv + g) * res_stride * D;
-    float qc[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) qc[c] = bf16_bits_to_f32(q[(size_t)row * D + lane + kWave * c]);
-    float l[kGroup];
-    float m = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < kGroup - 1; ++t) {
-        l[t] = -INFINITY;
-        if (t < n_res) {
-            float d = 0.0f;
-#pragma unroll
-            for (int c = 0; c < C; ++c) d = fmaf(qc[c], bf16_bits_to_f32(kr[(size_t)t * D + lane + kWave * c]), d);
-            l[t] = dpp_sum<kWave>(d) * scale_log2;
-            m = fmaxf(m, l[t]);
-        }
-    }
-    float lsum = 0.0f, x[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) x[c] = 0.0f;
-#pragma unroll
-    for (int t = 0; t < kGroup - 1; ++t) {
-        if (t < n_res) {
-            const float p = exp2f(l[t] - m);
-            lsum += p;
-#pragma unroll
-            for (int c = 0; c < C; ++c) x[c] = fmaf(p, bf16_bits_to_f32(vr[(size_t)t * D + lane + kWave * c]), x[c]);
-        }
-    }
+    float m, lsum, x[C];
+    residual_part<D>(q, k_res, v_res, res_stride, n_res, Hq, Hkv, scale_log2, row, lane, m, lsum, x);
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         if (ws_splits == 1)
@@ -667,30 +709,32 @@ struct DecodeSrc {
 template <int D, int R>
 hipError_t launch_dr(const void* q, const DecodeSrc& src, int B, int Hq, int Hkv, float scale_log2, void* out,
                      void* ws, const DecodePlan& plan, hipStream_t stream) {
-    const int packed_parts = src.n > 0 ? plan.splits : 0;
-    const int parts = packed_parts + (src.n_res > 0 ? 1 : 0);
+    const auto qq = static_cast<const uint16_t*>(q);
+    const auto o = static_cast<__bf16*>(out);
+    const bool res = src.n_res > 0;
+    if (src.n <= 0) {  // the window alone: one part, written as the output
+        hipLaunchKernelGGL((decode_residual_kernel<D>), dim3(B * Hq), dim3(kWave), 0, stream, qq, src.k_res,
+                           src.v_res, src.res_stride, src.n_res, Hq, Hkv, scale_log2, static_cast<float*>(ws),
+                           static_cast<float*>(ws), 1, 0, o, src.counts);
+        return hipGetLastError();
+    }
+    // packed ranges: plan.splits parts in the workspace (the output itself when
+    // it is the only part); the window, if any, is computed and merged by the
+    // merge kernel
+    const int parts = plan.splits;
+    const bool direct = parts == 1 && !res;
     float* ws_acc = static_cast<float*>(ws);
     float* ws_ml = ws_acc + (size_t)B * Hq * parts * D;
-    if (packed_parts) {
-        const long items = (long)B * Hkv * plan.splits;
-        const long grid = std::min<long>((items + 3) / 4, resident_workgroups<D, R>());
-        hipLaunchKernelGGL((decode_partial_kernel<D, R>), dim3((unsigned)grid), dim3(256), 0, stream,
-                           static_cast<const uint16_t*>(q), src.k_codes, src.k_sz, src.v_codes, src.v_sz, src.n,
-                           src.tok_stride, src.grp_stride, plan.chunk, plan.splits, parts, (int)items, scale_log2,
-                           ws_acc, ws_ml, static_cast<__bf16*>(out), src.counts);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (src.n_res > 0) {
-        hipLaunchKernelGGL((decode_residual_kernel<D>), dim3(B * Hq), dim3(kWave), 0, stream,
-                           static_cast<const uint16_t*>(q), src.k_res, src.v_res, src.res_stride, src.n_res, Hq, Hkv,
-                           scale_log2, ws_acc, ws_ml, parts, parts - 1, static_cast<__bf16*>(out), src.counts);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (parts == 1) return hipSuccess;  // a single part wrote out itself
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(B * Hq), dim3(D), 0, stream, ws_acc, ws_ml, parts,
-                       static_cast<__bf16*>(out));
+    const long items = (long)B * Hkv * plan.splits;
+    const long grid = std::min<long>((items + 3) / 4, resident_workgroups<D, R>());
+    hipLaunchKernelGGL((decode_partial_kernel<D, R>), dim3((unsigned)grid), dim3(256), 0, stream, qq, src.k_codes,
+                       src.k_sz, src.v_codes, src.v_sz, src.n, src.tok_stride, src.grp_stride, plan.chunk, plan.splits,
+                       parts, direct ? 1 : 0, (int)items, scale_log2, ws_acc, ws_ml, o, src.counts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || direct) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(B * Hq), dim3(D), 0, stream, ws_acc, ws_ml, parts, o, qq,
+                       res ? src.k_res : nullptr, src.v_res, src.res_stride, src.n_res, Hq, Hkv, scale_log2,
+                       src.counts);
     return hipGetLastError();
 }
 

@@ -23,12 +23,10 @@ hipError_t launch_stream_append(const void* k, const void* v, const int32_t* idx
                                 int T_ctx, int D, int n, int slot, void* k_res, void* v_res, hipStream_t stream);
 
 // Device-side generation step (counts = device int32 {n_packed, n_res,
-// overflow, 0}): set the counts; append one token per (sequence, KV head) into
-// window slot n_res, pack a filled window at n_packed, advance the counts.
+// overflow, ticket}): set the counts; in one launch, append one token per
+// (sequence, KV head) into window slot n_res, pack a filled window at n_packed
+// and advance the counts.
 hipError_t launch_stream_set_counts(int32_t* counts, int n_packed, int n_res, hipStream_t stream);
-hipError_t launch_stream_pack_counted(const void* k_res, const void* v_res, int B, int Hkv, int D, int cap,
-                                     const int32_t* counts, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes,
-                                     uint32_t* v_sz, hipStream_t stream);
 hipError_t launch_stream_step_append(const void* k_new, const void* v_new, int B, int Hkv, int D, int cap,
                                      int32_t* counts, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes,
                                      uint32_t* v_sz, void* k_res, void* v_res, hipStream_t stream);

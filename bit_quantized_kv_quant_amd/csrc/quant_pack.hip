@@ -296,13 +296,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(128) void quant_pack_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, PackGeom pg,
     int Hkv, uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz, uint8_t* __restrict__ v_codes,
-    uint32_t* __restrict__ v_sz, const int32_t* __restrict__ counts) {
-    if (counts) {  // window pack of a device-side step: only when the token just appended filled the window
-        if (counts[2] != 0 || counts[1] != kGroup - 1 || counts[0] < 0 || counts[0] % kGroup != 0 ||
-            counts[0] + kGroup > pg.tok_stride)
-            return;
-        pg.tok0 = counts[0];
-    }
+    uint32_t* __restrict__ v_sz) {
     const bool full = (blockIdx.x + 1) * kGroup <= pg.n;
     if (threadIdx.x < kWave) {
         if (full) pack_keys_full<T, D>(k, idx, T_ctx, pg, Hkv, k_codes, k_sz);
@@ -313,13 +307,67 @@ __global__ __launch_bounds__(128) void quant_pack_kernel(
     }
 }
 
+// One generation step's append with the counts in device memory
+// (counts = {n_packed, n_res, overflow, ticket}): workgroup (g, b) of grid
+// (1, Hkv, B) copies the new K row (wave 0) and V row (wave 1) into window slot
+// n_res; when that slot was the window's last, the same waves pack the window
+// as group n_packed / 32 (the rule of quant_pack_kernel) or, with no capacity
+// left, the overflow flag is raised.  Every workgroup reads the counts before
+// it takes a ticket, so the workgroup that takes the last ticket can advance
+// them: no other launch, no spinning.
+template <int D>
+__global__ __launch_bounds__(128) void stream_step_append_kernel(
+    const uint32_t* __restrict__ k_new, const uint32_t* __restrict__ v_new, int Hkv, int cap,
+    int32_t* __restrict__ counts, uint16_t* __restrict__ k_res, uint16_t* __restrict__ v_res,
+    uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz, uint8_t* __restrict__ v_codes,
+    uint32_t* __restrict__ v_sz) {
+    constexpr int W = D / 2;  // dwords per bf16 row
+    const int unit = blockIdx.z * Hkv + blockIdx.y;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int n_packed = counts[0], n_res = counts[1], flag = counts[2];
+    const bool ok = flag == 0 && n_res >= 0 && n_res < kGroup && n_packed >= 0 && n_packed % kGroup == 0 &&
+                    n_packed <= cap;
+    const bool full = ok && n_res == kGroup - 1;
+    const bool pack = full && n_packed + kGroup <= cap;
+    if (ok && lane < W) {
+        const uint32_t* src = (wave == 0 ? k_new : v_new) + (size_t)unit * W;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(wave == 0 ? k_res : v_res) + ((size_t)unit * kGroup + n_res) * W;
+        dst[lane] = src[lane];
+    }
+    __syncthreads();  // the new row is visible to both waves
+    if (pack) {
+        const PackGeom pg{kGroup, kGroup, cap, cap / kGroup, n_packed};
+        if (wave == 0) pack_keys_full<uint16_t, D>(k_res, nullptr, kGroup, pg, Hkv, k_codes, k_sz);
+        else pack_values_full<uint16_t, D>(v_res, nullptr, kGroup, pg, Hkv, v_codes, v_sz);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        const int nwg = (int)(gridDim.y * gridDim.z);
+        if (atomicAdd(&counts[3], 1) == nwg - 1) {  // every workgroup has read the counts
+            if (ok) {
+                if (!full) {
+                    counts[1] = n_res + 1;
+                } else if (pack) {
+                    counts[0] = n_packed + kGroup;
+                    counts[1] = 0;
+                } else {
+                    counts[2] = 1;
+                }
+            }
+            counts[3] = 0;
+            __threadfence();
+        }
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const void* k, const void* v, const int32_t* idx, int B, int Hkv, int T_ctx,
                         const PackGeom& pg, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes, uint32_t* v_sz,
-                        hipStream_t stream, const int32_t* counts = nullptr) {
+                        hipStream_t stream) {
     const int G = (pg.n + kGroup - 1) / kGroup;
     hipLaunchKernelGGL((quant_pack_kernel<T, D>), dim3(G, Hkv, B), dim3(128), 0, stream, static_cast<const T*>(k),
-                       static_cast<const T*>(v), idx, T_ctx, pg, Hkv, k_codes, k_sz, v_codes, v_sz, counts);
+                       static_cast<const T*>(v), idx, T_ctx, pg, Hkv, k_codes, k_sz, v_codes, v_sz);
     return hipGetLastError();
 }
 
@@ -343,15 +391,19 @@ hipError_t launch_quant_pack(const void* k, const void* v, bool bf16, const int3
     return launch_geom(k, v, bf16, idx, B, Hkv, T_ctx, D, pg, k_codes, k_sz, v_codes, v_sz, stream);
 }
 
-hipError_t launch_stream_pack_counted(const void* k_res, const void* v_res, int B, int Hkv, int D, int cap,
-                                     const int32_t* counts, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes,
-                                     uint32_t* v_sz, hipStream_t stream) {
-    const PackGeom pg{kGroup, kGroup, cap, cap / kGroup, 0};  // tok0 comes from counts
+hipError_t launch_stream_step_append(const void* k_new, const void* v_new, int B, int Hkv, int D, int cap,
+                                     int32_t* counts, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes,
+                                     uint32_t* v_sz, void* k_res, void* v_res, hipStream_t stream) {
+    const dim3 grid(1, Hkv, B);
     if (D == 128)
-        return launch_typed<uint16_t, 128>(k_res, v_res, nullptr, B, Hkv, kGroup, pg, k_codes, k_sz, v_codes, v_sz,
-                                           stream, counts);
-    return launch_typed<uint16_t, 64>(k_res, v_res, nullptr, B, Hkv, kGroup, pg, k_codes, k_sz, v_codes, v_sz, stream,
-                                      counts);
+        hipLaunchKernelGGL((stream_step_append_kernel<128>), grid, dim3(128), 0, stream,
+                           static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new), Hkv, cap, counts,
+                           static_cast<uint16_t*>(k_res), static_cast<uint16_t*>(v_res), k_codes, k_sz, v_codes, v_sz);
+    else
+        hipLaunchKernelGGL((stream_step_append_kernel<64>), grid, dim3(128), 0, stream,
+                           static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new), Hkv, cap, counts,
+                           static_cast<uint16_t*>(k_res), static_cast<uint16_t*>(v_res), k_codes, k_sz, v_codes, v_sz);
+    return hipGetLastError();
 }
 
 hipError_t launch_stream_pack(const void* k, const void* v, bool bf16, const int32_t* idx, int idx_stride, int B,

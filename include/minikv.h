@@ -236,17 +236,18 @@ size_t minikv_stream_decode_ws_bytes(int B, int Hq, int Hkv, int n_packed, int n
  * A generation step with the counts in device memory, so that the step is a
  * fixed sequence of launches a HIP graph can capture and replay (the host no
  * longer passes n_packed / n_res).  counts: device int32[4], caller-owned,
- * {n_packed, n_res, overflow flag, 0}; the same streaming layout as above.
+ * {n_packed, n_res, overflow flag, ticket}; the same streaming layout as above.
  *
  * minikv_stream_set_counts writes {n_packed, n_res, 0, 0} with a kernel (no
  * memset node).  Errors: NULL; SHAPE (cap not a positive multiple of 32,
  * n_packed not a multiple of 32 or > cap, n_res outside 0..31); ALIGN; LAUNCH.
  *
  * minikv_stream_step_append appends k_new, v_new bf16 [B][Hkv][D] (one token
- * per sequence and KV head) in three launches: the token into window slot
- * n_res; the window packed at token n_packed when that token filled it (the
- * same quantisation as minikv_stream_pack); counts advanced (n_res + 1, or
- * n_packed + 32 and n_res = 0 after a pack).  When a full window cannot be
+ * per sequence and KV head) in one launch: the token into window slot n_res;
+ * the window packed at token n_packed when that token filled it (the same
+ * quantisation as minikv_stream_pack); counts advanced (n_res + 1, or
+ * n_packed + 32 and n_res = 0 after a pack) by the workgroup that finishes
+ * last (counts[3] is its ticket and is back at 0 after every call).  When a full window cannot be
  * packed (n_packed + 32 > cap) the overflow flag is set, the window is kept,
  * and every later step writes nothing until the counts are set again: the
  * caller reads the flag to detect it.  Errors: NULL; SHAPE (sizes, cap);
