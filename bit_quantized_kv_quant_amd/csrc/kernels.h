@@ -8,6 +8,9 @@
 
 namespace minikv {
 
+// Compute units of the current device (cached on first use; 256 without a device).
+int device_cu_count();
+
 hipError_t launch_quant_pack(const void* k, const void* v, bool bf16, const int32_t* idx, int B,
                              int Hkv, int T_ctx, int D, int n_keep, uint8_t* k_codes, uint32_t* k_sz,
                              uint8_t* v_codes, uint32_t* v_sz, hipStream_t stream);

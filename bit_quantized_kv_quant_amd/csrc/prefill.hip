@@ -463,18 +463,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd_kernel(
     }
 }
 
-int cu_count() {
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, c = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
-            n = c;
-        else
-            n = 256;
-    }
-    return n;
-}
+int cu_count() { return device_cu_count(); }
 
 template <int D, bool kWithO>
 hipError_t launch_fa(const void* q, const void* k, const void* v, int B, int T_ctx, int Hq, int Hkv,
@@ -490,6 +479,19 @@ hipError_t launch_fa(const void* q, const void* k, const void* v, int B, int T_c
 }
 
 }  // namespace
+
+int device_cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, c = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+            n = c;
+        else
+            n = 256;
+    }
+    return n;
+}
 
 // One score pass per head runs on the workgroup that finishes the head's last
 // query block, its 8 waves walking the head's keys; with fewer heads than

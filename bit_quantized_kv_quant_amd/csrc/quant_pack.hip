@@ -99,10 +99,8 @@ __device__ __forceinline__ uint32_t or8(uint32_t x) {
 // Lane l owns channels 2l, 2l+1 (D/2 active lanes).
 template <typename T, int D>
 __device__ __forceinline__ void pack_keys(
-    const T* __restrict__ k, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int Hkv,
+    const T* __restrict__ k, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int gi, int unit,
     uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz) {
-    const int gi = blockIdx.x;
-    const int unit = blockIdx.z * Hkv + blockIdx.y;
     const int lane = threadIdx.x % kWave;
     const bool active = lane < D / 2;
     const int c = 2 * (active ? lane : 0);
@@ -150,10 +148,8 @@ __device__ __forceinline__ void pack_keys(
 // both in one 16-byte write; tokens past the call's count stay code 0.
 template <typename T, int D>
 __device__ __forceinline__ void pack_values(
-    const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int Hkv,
+    const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int gi, int unit,
     uint8_t* __restrict__ v_codes, uint32_t* __restrict__ v_sz) {
-    const int gi = blockIdx.x;
-    const int unit = blockIdx.z * Hkv + blockIdx.y;
     const int lane = threadIdx.x % kWave;
     const bool active = lane < D / 2;
     const int c = 2 * (active ? lane : 0);
@@ -224,10 +220,8 @@ __device__ __forceinline__ void gather_full(const T* __restrict__ x, const int32
 
 template <typename T, int D>
 __device__ __forceinline__ void pack_keys_full(
-    const T* __restrict__ k, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int Hkv,
+    const T* __restrict__ k, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int gi, int unit,
     uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz) {
-    const int gi = blockIdx.x;
-    const int unit = blockIdx.z * Hkv + blockIdx.y;
     const int lane = threadIdx.x % kWave;
     const bool active = lane < D / 2;
     const int c = 2 * (active ? lane : 0);
@@ -261,10 +255,8 @@ __device__ __forceinline__ void pack_keys_full(
 
 template <typename T, int D>
 __device__ __forceinline__ void pack_values_full(
-    const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int Hkv,
+    const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int gi, int unit,
     uint8_t* __restrict__ v_codes, uint32_t* __restrict__ v_sz) {
-    const int gi = blockIdx.x;
-    const int unit = blockIdx.z * Hkv + blockIdx.y;
     const int lane = threadIdx.x % kWave;
     const bool active = lane < D / 2;
     const int c = 2 * (active ? lane : 0);
@@ -298,12 +290,14 @@ __global__ __launch_bounds__(128) void quant_pack_kernel(
     int Hkv, uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz, uint8_t* __restrict__ v_codes,
     uint32_t* __restrict__ v_sz) {
     const bool full = (blockIdx.x + 1) * kGroup <= pg.n;
+    const int gi = blockIdx.x;
+    const int unit = blockIdx.z * Hkv + blockIdx.y;
     if (threadIdx.x < kWave) {
-        if (full) pack_keys_full<T, D>(k, idx, T_ctx, pg, Hkv, k_codes, k_sz);
-        else pack_keys<T, D>(k, idx, T_ctx, pg, Hkv, k_codes, k_sz);
+        if (full) pack_keys_full<T, D>(k, idx, T_ctx, pg, gi, unit, k_codes, k_sz);
+        else pack_keys<T, D>(k, idx, T_ctx, pg, gi, unit, k_codes, k_sz);
     } else {
-        if (full) pack_values_full<T, D>(v, idx, T_ctx, pg, Hkv, v_codes, v_sz);
-        else pack_values<T, D>(v, idx, T_ctx, pg, Hkv, v_codes, v_sz);
+        if (full) pack_values_full<T, D>(v, idx, T_ctx, pg, gi, unit, v_codes, v_sz);
+        else pack_values<T, D>(v, idx, T_ctx, pg, gi, unit, v_codes, v_sz);
     }
 }
 
@@ -337,8 +331,8 @@ __global__ __launch_bounds__(128) void stream_step_append_kernel(
     __syncthreads();  // the new row is visible to both waves
     if (pack) {
         const PackGeom pg{kGroup, kGroup, cap, cap / kGroup, n_packed};
-        if (wave == 0) pack_keys_full<uint16_t, D>(k_res, nullptr, kGroup, pg, Hkv, k_codes, k_sz);
-        else pack_values_full<uint16_t, D>(v_res, nullptr, kGroup, pg, Hkv, v_codes, v_sz);
+        if (wave == 0) pack_keys_full<uint16_t, D>(k_res, nullptr, kGroup, pg, 0, unit, k_codes, k_sz);
+        else pack_values_full<uint16_t, D>(v_res, nullptr, kGroup, pg, 0, unit, v_codes, v_sz);
     }
     __syncthreads();
     if (threadIdx.x == 0) {
