@@ -8,13 +8,16 @@
 //   code = s == 0 ? 0 : clamp(rint(fl32(x - z) / s), 0, 3)
 // The file is compiled with -ffp-contract=off so no multiply-add is fused and
 // the divide by 3 stays correctly rounded; the codes come from exact threshold
-// tests (code_of) and match a plain IEEE evaluation of the rule bit for bit.
+// tests (code_of: three comparisons with exact multiples of s) and match a
+// plain IEEE evaluation of the rule bit for bit.
 // Inputs are finite (-fno-honor-nans: min / max need no NaN handling).
 //
 // HBM-bound gather: each kept row is read once (coalesced 4-byte lane loads of
 // two channels), each packed byte written once (key codes: dword stores
 // assembled with DPP ORs; value codes: one 16-byte store per lane).  Keys and
 // values of a token group are packed by the two waves of one workgroup.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -39,7 +42,7 @@ template <> __device__ __forceinline__ Pair load_pair<uint16_t>(const uint16_t* 
 struct GroupParams {
     float s, z;
     uint32_t word;     // fp16 s in bits 0..15, fp16 z in bits 16..31
-    float e1, e2, e3;  // decision thresholds of code_of (infinite when s == 0)
+    float h1, h2, h3;  // decision thresholds of code_of: s/2, 3s/2, 5s/2 (infinite when s == 0)
 };
 
 // fl32(r / 3) for r >= 0 without the divide sequence: q0 = fl(r c) with
@@ -60,7 +63,7 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
     const float s = half_bits_to_f32(sb);
     const bool zero = s == 0.0f;
     return {s, half_bits_to_f32(zb), sb | (zb << 16),
-            zero ? INFINITY : s * 0x1p-25f, zero ? INFINITY : -s * 0x1p-24f, zero ? INFINITY : s * 0x1p-23f};
+            zero ? INFINITY : 0.5f * s, zero ? INFINITY : 1.5f * s, zero ? INFINITY : 2.5f * s};
 }
 
 // code = s == 0 ? 0 : clamp(rint(u), 0, 3) with u = fl32(d / s), d = fl32(x - z), decided
@@ -68,15 +71,14 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
 //   rint(u) >= 1  <=>  u > 0.5  <=>  d / s > 0.5 + 2^-25   (the rounding midpoint above 0.5 ties to 0.5)
 //   rint(u) >= 2  <=>  u >= 1.5 <=>  d / s >= 1.5 - 2^-24  (the midpoint below 1.5 ties to 1.5)
 //   rint(u) >= 3  <=>  u > 2.5  <=>  d / s > 2.5 + 2^-23
-// and, with s > 0, d / s > c + t  <=>  d - c s > t s.  c s is exact (s is an fp16 value, c in
-// {0.5, 1.5, 2.5}); fma(-c, s, d) rounds d - c s once, and wherever d is within [c s / 2, 2 c s] that
-// difference is exact (Sterbenz), so the comparison with the exact t s is exact; outside that range
-// |d - c s| >= c s / 2 dwarfs both the rounding and t s, so the sign decides alone.  With s == 0 all
+// With s > 0 an fp16 value (11 significant bits), s/2, 3s/2 and 5s/2 are exact in fp32 and each
+// bound s (c + t) lies less than one fp32 ulp from c s, on the side that makes the fp32 decision
+// d > s/2, d >= 3s/2, d > 5s/2 (no fp32 value falls between c s and the bound).  Checked for every
+// positive fp16 s against the division (tests/test_code_thresholds_exhaustive.py).  With s == 0 the
 // thresholds are infinite and the code is 0.
 __device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
     const float d = x - p.z;
-    return (uint32_t)(fmaf(-0.5f, p.s, d) > p.e1) + (uint32_t)(fmaf(-1.5f, p.s, d) >= p.e2) +
-           (uint32_t)(fmaf(-2.5f, p.s, d) > p.e3);
+    return (uint32_t)(d > p.h1) + (uint32_t)(d >= p.h2) + (uint32_t)(d > p.h3);
 }
 
 // Where one call packs: tokens 0..n-1 of its selection (index row stride
@@ -86,6 +88,21 @@ __device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
 struct PackGeom {
     int n, idx_stride, tok_stride, grp_stride, tok0;
 };
+
+// Lane S of each 16-lane row, to the whole row (DPP row_newbcast).
+template <int S>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + S, 0xF, 0xF, false));
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 // OR over aligned groups of 8 lanes: quad swaps, then the mirrored half row.
 __device__ __forceinline__ uint32_t or8(uint32_t x) {
@@ -263,17 +280,33 @@ __device__ __forceinline__ void pack_values_full(
     const int t0 = gi * kGroup;
     Pair x[kGroup];
     gather_full<T, D>(v, idx, T_ctx, pg.idx_stride, unit, t0, c, x);
-    // Token t's parameter word of row lane / 16 is kept by the lane with lane % 16 == t % 16.
-    uint32_t wa[2] = {0u, 0u}, wb[2] = {0u, 0u}, vw[2] = {0u, 0u};
-#pragma unroll
-    for (int t = 0; t < kGroup; ++t) {
+    // Every 16-lane row (32 channels) reduces each token's min / max; the lane
+    // with lane % 16 == j keeps those of tokens j and j + 16, derives their
+    // parameters once, and the row reads them back by DPP broadcast, instead of
+    // all 16 lanes deriving every token's parameters.
+    float own_mn[2], own_mx[2];
+    static_for<0, kGroup>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
         const float mn = dpp_min<16>(fminf(x[t].a, x[t].b));
         const float mx = dpp_max<16>(fmaxf(x[t].a, x[t].b));
-        const GroupParams p = group_params(mn, mx);
+        if ((lane & 15) == (t & 15)) {
+            own_mn[t / 16] = mn;
+            own_mx[t / 16] = mx;
+        }
+    });
+    const GroupParams own[2] = {group_params(own_mn[0], own_mx[0]), group_params(own_mn[1], own_mx[1])};
+    uint32_t wa[2] = {0u, 0u}, wb[2] = {0u, 0u};
+    const uint32_t vw[2] = {own[0].word, own[1].word};  // token 16 h + lane % 16 of row lane / 16
+    static_for<0, kGroup>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        GroupParams p;
+        p.z = row_bcast<t & 15>(own[t / 16].z);
+        p.h1 = row_bcast<t & 15>(own[t / 16].h1);
+        p.h2 = row_bcast<t & 15>(own[t / 16].h2);
+        p.h3 = row_bcast<t & 15>(own[t / 16].h3);
         wa[t / 16] |= code_of(x[t].a, p) << (2 * (t % 16));
         wb[t / 16] |= code_of(x[t].b, p) << (2 * (t % 16));
-        vw[t / 16] = (lane & 15) == (t & 15) ? p.word : vw[t / 16];
-    }
+    });
     if (active) {
         *reinterpret_cast<uint4*>(v_codes + (((size_t)unit * pg.grp_stride + pg.tok0 / kGroup + gi) * D + c) * 8) = make_uint4(wa[0], wa[1], wb[0], wb[1]);
 #pragma unroll
