@@ -43,7 +43,7 @@ constexpr int kMaxStaged = 4;  // (query head, row block) operand sets a workgro
 // from (blockIdx.x * 4 + w) * nbw (nbw even).  kMode 0: one query head per KV
 // head and a window of at most 32 rows (Q operand and row lse in registers);
 // 1: at most kMaxStaged (query head, row block) pairs, staged once per
-// workgroup in LDS in the operand layout; 2: anything else (operands from L2).
+// workgroup in LDS in the operand layout.  More sets: window_scores_rows_kernel.
 template <int D, int kMode>
 __global__ __launch_bounds__(256, 3) void window_scores_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
@@ -104,8 +104,7 @@ __global__ __launch_bounds__(256, 3) void window_scores_kernel(const uint16_t* _
             if (i + 1 < nb) emit(i + 1, block_mass<D>(qa, kb, l2, scale_log2, w0, (kb0 + i + 1) * 32, lane));
         }
     } else {
-        // Per key block, every (query head, row block) set: operands from LDS
-        // (mode 1) or from L2 (mode 2).
+        // Per key block, every staged (query head, row block) set, operands from LDS.
         auto mass = [&](int i, const bf16x8 (&kr)[KS]) {
             const int kt0 = (kb0 + i) * 32;
             float a = 0.0f;
@@ -115,18 +114,14 @@ __global__ __launch_bounds__(256, 3) void window_scores_kernel(const uint16_t* _
                     if (row0 + 31 < kt0) continue;  // rows entirely before this key block
                     bf16x8 qa[KS];
                     float l2[16];
-                    if constexpr (kMode == 1) {
-                        const int set = r * nrb + rb;
+                    const int set = r * nrb + rb;
 #pragma unroll
-                        for (int kk = 0; kk < KS; ++kk) qa[kk] = s_q[(set * KS + kk) * kWave + lane];
+                    for (int kk = 0; kk < KS; ++kk) qa[kk] = s_q[(set * KS + kk) * kWave + lane];
 #pragma unroll
-                        for (int g4 = 0; g4 < 4; ++g4) {
-                            const f32x4 t = *reinterpret_cast<const f32x4*>(s_l2 + set * 32 + 8 * g4 + 4 * half);
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const f32x4 t = *reinterpret_cast<const f32x4*>(s_l2 + set * 32 + 8 * g4 + 4 * half);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) l2[4 * g4 + e] = t[e];
-                        }
-                    } else {
-                        load_qblock<D>(q, lse, ((size_t)b * Hq + g * R + r) * T_ctx, w0, W, rb, lane, qa, l2);
+                        for (int e = 0; e < 4; ++e) l2[4 * g4 + e] = t[e];
                     }
                     a += block_mass<D>(qa, kr, l2, scale_log2, row0, kt0, lane);
                 }
@@ -138,6 +133,89 @@ __global__ __launch_bounds__(256, 3) void window_scores_kernel(const uint16_t* _
             emit(i, mass(i, ka));
             if (i + 2 < nb) load_kblock<D>(rk, (kb0 + i + 2) * 32, lane, ka);
             if (i + 1 < nb) emit(i + 1, mass(i + 1, kb));
+        }
+    }
+}
+
+// Many window rows (more (query head, row block) sets than a workgroup can
+// keep, e.g. every prompt row for cumulative scores): the keys stay and the
+// rows stream.  A workgroup owns a range of 8 key blocks (wave w: blocks 2w,
+// 2w + 1, their K operands in registers) and walks the sets (query head
+// outer, row block inner), staging each set's Q operand and row lse in LDS
+// once for all four waves; a wave adds a set's mass for each of its blocks
+// that the set's rows can see.  The summation order per key is the same as
+// mode 1's, and ranges are paired (x, last - x) so every workgroup does about
+// the same causal work.  grid (ceil(ranges / 2), Hkv, B).
+template <int D>
+__global__ __launch_bounds__(256) void window_scores_rows_kernel(const uint16_t* __restrict__ q,
+                                                                 const uint16_t* __restrict__ k,
+                                                                 const float* __restrict__ lse, int T_ctx, int Hq,
+                                                                 int Hkv, int W, int n_ranges, float scale_log2,
+                                                                 float* __restrict__ scores) {
+    constexpr int KS = D / 16;
+    constexpr int KBW = 2;            // key blocks per wave
+    constexpr int KR = 4 * KBW;       // key blocks per range
+    constexpr int CPR = D / 8;        // 16-byte chunks per Q row
+    __shared__ bf16x8 s_q[KS * kWave];
+    __shared__ float s_l[32];
+    const int g = blockIdx.y;
+    const int b = blockIdx.z;
+    const int R = Hq / Hkv;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int half = lane >> 5;
+    const size_t kvbase = ((size_t)b * Hkv + g) * T_ctx;
+    const int w0 = T_ctx - W;
+    const int nrb = (W + 31) / 32;
+    const int nkb = (T_ctx + 31) / 32;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k + kvbase * D), 0, T_ctx * D * 2, 0x00020000);
+    for (int pass = 0; pass < 2; ++pass) {
+        const int range = pass == 0 ? (int)blockIdx.x : n_ranges - 1 - (int)blockIdx.x;
+        if (pass == 1 && range <= (int)blockIdx.x) break;  // workgroup-uniform
+        const int kb_first = range * KR;
+        bf16x8 kr[KBW][KS];
+        float acc[KBW];
+#pragma unroll
+        for (int i = 0; i < KBW; ++i) {
+            wmass::load_kblock<D>(rk, (kb_first + wave * KBW + i) * 32, lane, kr[i]);
+            acc[i] = 0.0f;
+        }
+        for (int r = 0; r < R; ++r) {
+            const size_t qbase = ((size_t)b * Hq + g * R + r) * T_ctx;
+            for (int rb = 0; rb < nrb; ++rb) {
+                const int row0 = w0 + 32 * rb;
+                if (row0 + 31 < kb_first * 32) continue;  // rows before every key of the range
+                __syncthreads();                          // the previous set is consumed
+                for (int c = threadIdx.x; c < 32 * CPR; c += 256) {
+                    const int m = c / CPR, cr = c % CPR;
+                    const int row = 32 * rb + m;
+                    s_q[(cr >> 1) * kWave + ((cr & 1) << 5 | m)] =
+                        row < W ? *reinterpret_cast<const bf16x8*>(q + (qbase + w0 + row) * D + 8 * cr) : bf16x8{};
+                }
+                if (threadIdx.x < 32) {
+                    const int row = 32 * rb + threadIdx.x;
+                    s_l[threadIdx.x] = row < W ? lse[qbase + w0 + row] * kLog2e : INFINITY;
+                }
+                __syncthreads();
+                bf16x8 qa[KS];
+                float l2[16];
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) qa[kk] = s_q[kk * kWave + lane];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) l2[e] = s_l[wmass::acc_row(e, lane)];
+#pragma unroll
+                for (int i = 0; i < KBW; ++i) {
+                    const int kb = kb_first + wave * KBW + i;
+                    if (kb < nkb && row0 + 31 >= kb * 32)  // wave-uniform
+                        acc[i] += block_mass<D>(qa, kr[i], l2, scale_log2, row0, kb * 32, lane);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < KBW; ++i) {
+            const float a = acc[i] + swap_halves(acc[i]);
+            const int j = (kb_first + wave * KBW + i) * 32 + (lane & 31);
+            if (half == 0 && j < T_ctx) scores[kvbase + j] = a;
         }
     }
 }
@@ -160,8 +238,11 @@ hipError_t launch_ws(const void* q, const void* k, const float* lse, int B, int 
         hipLaunchKernelGGL((window_scores_kernel<D, 0>), grid, dim3(256), 0, stream, qq, kk, lse, T_ctx, Hq, Hkv, W, nbw, sl, scores);
     else if (sets <= kMaxStaged)
         hipLaunchKernelGGL((window_scores_kernel<D, 1>), grid, dim3(256), 0, stream, qq, kk, lse, T_ctx, Hq, Hkv, W, nbw, sl, scores);
-    else
-        hipLaunchKernelGGL((window_scores_kernel<D, 2>), grid, dim3(256), 0, stream, qq, kk, lse, T_ctx, Hq, Hkv, W, nbw, sl, scores);
+    else {
+        const int n_ranges = ((T_ctx + 31) / 32 + 7) / 8;
+        hipLaunchKernelGGL((window_scores_rows_kernel<D>), dim3((n_ranges + 1) / 2, Hkv, B), dim3(256), 0, stream, qq,
+                           kk, lse, T_ctx, Hq, Hkv, W, n_ranges, sl, scores);
+    }
     return hipGetLastError();
 }
 
