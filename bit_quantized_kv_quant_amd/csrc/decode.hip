@@ -639,34 +639,21 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     out[(size_t)bh * D + t] = (__bf16)(o / L);
 }
 
-// Exact part of a streaming decode: the residual tokens (bf16 K / V, at most
-// 31, slots [B][Hkv][res_stride][D]) of one (sequence, query head) per wave.
-// Writes partial `slot` in the merge format (sum of 2^(l - m) v, m, sum of
-// 2^(l - m); l in log2 units), or the normalised output when it is the only
-// part (ws_splits == 1).  Lane l holds channels l, l + 64 (D = 128) or l.
+// A streaming cache with nothing packed: the window's tokens are the whole
+// attention set, one (sequence, query head) per wave, written as the output.
 template <int D>
-__global__ __launch_bounds__(64) void decode_residual_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_res, const uint16_t* __restrict__ v_res,
-    int res_stride, int n_res, int Hq, int Hkv, float scale_log2, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml, int ws_splits, int slot, __bf16* __restrict__ out,
-    const int32_t* __restrict__ counts) {
+__global__ __launch_bounds__(64) void decode_residual_kernel(const uint16_t* __restrict__ q,
+                                                             const uint16_t* __restrict__ k_res,
+                                                             const uint16_t* __restrict__ v_res, int res_stride,
+                                                             int n_res, int Hq, int Hkv, float scale_log2,
+                                                             __bf16* __restrict__ out) {
     constexpr int C = D / kWave;  // channels per lane
-    if (counts) n_res = max(0, min(n_res, counts[1]));  // device-side step: an empty window is an empty part
     const int row = blockIdx.x;   // b * Hq + h
     const int lane = threadIdx.x;
     float m, lsum, x[C];
     residual_part<D>(q, k_res, v_res, res_stride, n_res, Hq, Hkv, scale_log2, row, lane, m, lsum, x);
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-        if (ws_splits == 1)
-            out[(size_t)row * D + lane + kWave * c] = (__bf16)(x[c] / lsum);
-        else
-            ws_acc[((size_t)row * ws_splits + slot) * D + lane + kWave * c] = x[c];
-    }
-    if (ws_splits > 1 && lane == 0) {
-        ws_ml[((size_t)row * ws_splits + slot) * 2 + 0] = m;
-        ws_ml[((size_t)row * ws_splits + slot) * 2 + 1] = lsum;
-    }
+    for (int c = 0; c < C; ++c) out[(size_t)row * D + lane + kWave * c] = (__bf16)(x[c] / lsum);
 }
 
 // Resident workgroups of a decode instantiation on the current device: the
@@ -714,8 +701,7 @@ hipError_t launch_dr(const void* q, const DecodeSrc& src, int B, int Hq, int Hkv
     const bool res = src.n_res > 0;
     if (src.n <= 0) {  // the window alone: one part, written as the output
         hipLaunchKernelGGL((decode_residual_kernel<D>), dim3(B * Hq), dim3(kWave), 0, stream, qq, src.k_res,
-                           src.v_res, src.res_stride, src.n_res, Hq, Hkv, scale_log2, static_cast<float*>(ws),
-                           static_cast<float*>(ws), 1, 0, o, src.counts);
+                           src.v_res, src.res_stride, src.n_res, Hq, Hkv, scale_log2, o);
         return hipGetLastError();
     }
     // packed ranges: plan.splits parts in the workspace (the output itself when
