@@ -13,7 +13,8 @@
 // read from HBM once, the next block's K loaded while the current one is
 // reduced; for one query head and a window of up to 32 rows the Q operand and
 // the row lse stay in registers, for up to four (query head, row block) sets
-// they are staged once per workgroup in LDS, otherwise they come from L2.
+// they are staged once per workgroup in LDS; with more sets the keys stay in
+// registers and the sets stream through LDS (window_scores_rows_kernel).
 // Summation order is fixed, so the scores are deterministic.
 #include "common.h"
 #include "kernels.h"
