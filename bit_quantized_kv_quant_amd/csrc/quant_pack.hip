@@ -104,6 +104,37 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
+// One stage of the row reduce-scatter: lanes paired by DPP pattern P (which
+// flips bit B of lane % 16, among others already resolved) exchange the
+// tokens whose bit B differs from their own and keep the min / max of the
+// rest; slot t (bit B of t clear) ends with the kept token's value.
+template <int P, int B>
+__device__ __forceinline__ void rs_stage(float (&mn)[kGroup], float (&mx)[kGroup], int lane) {
+    const bool hi = (lane >> B) & 1;
+    static_for<0, kGroup>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        if constexpr ((t & (1 << B)) == 0) {
+            constexpr int u = t | (1 << B);
+            const float kmn = hi ? mn[u] : mn[t], smn = hi ? mn[t] : mn[u];
+            const float kmx = hi ? mx[u] : mx[t], smx = hi ? mx[t] : mx[u];
+            mn[t] = fminf(kmn, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, smn), P, 0xF, 0xF, false)));
+            mx[t] = fmaxf(kmx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, smx), P, 0xF, 0xF, false)));
+        }
+    });
+}
+
+// Per-token min / max over each 16-lane row, scattered: afterwards mn[0],
+// mx[0] hold token lane % 16 and mn[16], mx[16] token 16 + lane % 16.  The
+// partners are row_mirror (lane ^ 15), row_half_mirror (^ 7), quad_perm
+// [3,2,1,0] (^ 3) and [1,0,3,2] (^ 1); each flips the bit it resolves and, besides
+// it, only bits still unresolved, so partners always hold the same tokens.
+__device__ __forceinline__ void row_reduce_scatter(float (&mn)[kGroup], float (&mx)[kGroup], int lane) {
+    rs_stage<0x140, 3>(mn, mx, lane);
+    rs_stage<0x141, 2>(mn, mx, lane);
+    rs_stage<0x1B, 1>(mn, mx, lane);
+    rs_stage<0xB1, 0>(mn, mx, lane);
+}
+
 // OR over aligned groups of 8 lanes: quad swaps, then the mirrored half row.
 __device__ __forceinline__ uint32_t or8(uint32_t x) {
     x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
@@ -280,20 +311,18 @@ __device__ __forceinline__ void pack_values_full(
     const int t0 = gi * kGroup;
     Pair x[kGroup];
     gather_full<T, D>(v, idx, T_ctx, pg.idx_stride, unit, t0, c, x);
-    // Every 16-lane row (32 channels) reduces each token's min / max; the lane
-    // with lane % 16 == j keeps those of tokens j and j + 16, derives their
-    // parameters once, and the row reads them back by DPP broadcast, instead of
-    // all 16 lanes deriving every token's parameters.
-    float own_mn[2], own_mx[2];
-    static_for<0, kGroup>([&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        const float mn = dpp_min<16>(fminf(x[t].a, x[t].b));
-        const float mx = dpp_max<16>(fmaxf(x[t].a, x[t].b));
-        if ((lane & 15) == (t & 15)) {
-            own_mn[t / 16] = mn;
-            own_mx[t / 16] = mx;
-        }
-    });
+    // Every 16-lane row (32 channels) reduces each token's min / max so that
+    // the lane with lane % 16 == j ends with those of tokens j and j + 16
+    // (a reduce-scatter), derives their parameters once, and the row reads them
+    // back by DPP broadcast, instead of all 16 lanes deriving every token's.
+    float mn[kGroup], mx[kGroup];
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) {
+        mn[t] = fminf(x[t].a, x[t].b);
+        mx[t] = fmaxf(x[t].a, x[t].b);
+    }
+    row_reduce_scatter(mn, mx, lane);
+    const float own_mn[2] = {mn[0], mn[16]}, own_mx[2] = {mx[0], mx[16]};
     const GroupParams own[2] = {group_params(own_mn[0], own_mx[0]), group_params(own_mn[1], own_mx[1])};
     uint32_t wa[2] = {0u, 0u}, wb[2] = {0u, 0u};
     const uint32_t vw[2] = {own[0].word, own[1].word};  // token 16 h + lane % 16 of row lane / 16
