@@ -21,8 +21,11 @@ LLaMA2-13B-shaped pyramid cache (40 layers x 40 heads, context 8192, per-layer
 budget 30 % -> 5 %) at a batch that fills about 227 GB of HBM, and the
 Mistral-7B-shaped GQA cache (32 layers, 32 / 8 heads, 6600 kept tokens of a
 44000-token prompt, batch 4).  A decode step there is one query per sequence
-through every layer; kept-token K/V are drawn directly from the workload's
-distributions and packed by the library.  The Mistral-shaped cache is also run
+through every layer (the Mistral-shaped sweep: 256 steps, each with fresh
+seeded queries); kept-token K/V are drawn directly from the workload's
+distributions and packed by the library.  `--pyramid-sweep` adds the
+pyramid decode's batch sweep up to the batch that fills about 250 GB (the
+maximum over the sweep is the maximum throughput).  The Mistral-shaped cache is also run
 as generation (decode_stream): 256 steps, each appending one new token per
 layer to a streaming cache (every 32nd packs the residual window) and decoding
 through all 32 layers.  Then two single-layer prefill lines
@@ -63,6 +66,9 @@ def parse():
                     help="after the timed region, run one device copy of this size (counter calibration)")
     ap.add_argument("--pyramid-batch", type=int, default=1024,
                     help="batch of the 40-layer pyramid decode sweep (1024 fills about 227 GB; 0 skips it)")
+    ap.add_argument("--pyramid-sweep", default="",
+                    help="comma-separated batches for a max-throughput sweep of the 40-layer pyramid decode "
+                         "(e.g. 1,64,256,512,1024,1133; 1133 fills about 250 GB); off by default")
     ap.add_argument("--no-gqa-sweep", action="store_true", help="skip the 32-layer GQA decode sweep")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the comparison of cache policies (KIVI-like, H2O-like, MiniKV, Pyramid)")
@@ -71,9 +77,11 @@ def parse():
     return ap.parse_args()
 
 
-def decode_layers(torch, mk, synth, wl, B, budgets, reps=3, chunk=64):
-    """Pack one cache per layer (kept-token K/V drawn directly), then time decode
-    steps through all layers: one query per sequence per step."""
+def decode_layers(torch, mk, synth, wl, B, budgets, reps=3, chunk=64, n_queries=1):
+    """Pack one cache per layer (kept-token K/V drawn directly), then time `reps`
+    decode steps through all layers: one query per sequence per step, step i
+    using seeded query set i % n_queries (fresh queries each step when
+    n_queries >= reps)."""
     dev = torch.device("cuda:0")
     caches = []
     for l, n in enumerate(budgets):
@@ -86,7 +94,8 @@ def decode_layers(torch, mk, synth, wl, B, budgets, reps=3, chunk=64):
             mk.quant_pack(k, v, out=sub)
             del k, v
         caches.append(c)
-    q = synth.make_decode_q(wl, dev, B=B)
+    qs = [synth.make_decode_q(wl, dev, B=B, step=i) for i in range(max(1, n_queries))]
+    q = qs[0]
     out = torch.empty_like(q)
     ws = torch.empty(max(16, max(mk.decode_ws_bytes(B, wl.Hq, wl.Hkv, c.n_keep, wl.D) for c in caches)),
                      dtype=torch.uint8, device=dev)
@@ -96,28 +105,33 @@ def decode_layers(torch, mk, synth, wl, B, budgets, reps=3, chunk=64):
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record()
-    for _ in range(reps):
+    for i in range(reps):
+        qi = qs[i % len(qs)]
         for c in caches:
-            mk.decode_attn(q, c, out=out, ws=ws)
+            mk.decode_attn(qi, c, out=out, ws=ws)
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / reps
-    # The same step replayed as one HIP graph (how a serving loop issues it): no
-    # per-call host work between the layers' launches.
+    # The same steps replayed as one HIP graph (how a serving loop issues it): no
+    # per-call host work between the layers' launches; each step's queries are
+    # copied into the captured query buffer first.
+    q_buf = q.clone()
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         for c in caches:
-            mk.decode_attn(q, c, out=out, ws=ws)
+            mk.decode_attn(q_buf, c, out=out, ws=ws)
     torch.cuda.current_stream().wait_stream(side)
     with torch.cuda.graph(graph):
         for c in caches:
-            mk.decode_attn(q, c, out=out, ws=ws)
+            mk.decode_attn(q_buf, c, out=out, ws=ws)
     graph.replay()
     torch.cuda.synchronize()
     ev0.record()
-    for _ in range(reps):
+    for i in range(reps):
+        if len(qs) > 1:
+            q_buf.copy_(qs[i % len(qs)])
         graph.replay()
     ev1.record()
     torch.cuda.synchronize()
@@ -134,7 +148,7 @@ def decode_layers(torch, mk, synth, wl, B, budgets, reps=3, chunk=64):
             "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3), "achieved_GBs": gbs,
             "hbm_frac": gbs / PEAK_HBM_GBS,
             "graph_ms_per_step": gms, "graph_tokens_per_s": B / (gms * 1e-3), "graph_achieved_GBs": ggbs,
-            "graph_hbm_frac": ggbs / PEAK_HBM_GBS}
+            "graph_hbm_frac": ggbs / PEAK_HBM_GBS, "steps": reps, "distinct_queries": len(qs)}
 
 
 def prefill_layer(torch, mk, synth, wl, reps):
@@ -623,10 +637,22 @@ def main():
         budgets = [mk.pyramid_keep(pw.T, pw.layers, l, *pw.pyramid) for l in range(pw.layers)]
         res["decode_pyramid"] = decode_layers(torch, mk, synth, pw, args.pyramid_batch, budgets)
         print(f"# pyramid decode: {json.dumps(res['decode_pyramid'])}", file=sys.stderr, flush=True)
+    if args.pyramid_sweep:
+        pw = synth.WORKLOADS["llama13b_pyramid"]
+        budgets = [mk.pyramid_keep(pw.T, pw.layers, l, *pw.pyramid) for l in range(pw.layers)]
+        sweep = []
+        for bs in (int(x) for x in args.pyramid_sweep.split(",") if x.strip()):
+            r = decode_layers(torch, mk, synth, pw, bs, budgets, reps=20 if bs <= 256 else 3)
+            sweep.append(r)
+            print(f"# pyramid sweep B={bs}: {json.dumps(r)}", file=sys.stderr, flush=True)
+        best = max(sweep, key=lambda r: r["tokens_per_s"])
+        res["decode_pyramid_sweep"] = {"points": sweep, "max_tokens_per_s": best["tokens_per_s"],
+                                       "at_batch": best["batch"]}
     if not args.no_gqa_sweep:
         gw = synth.WORKLOADS["mistral_44k"]
         budgets = [mk.keep_count(gw.T, gw.budget_pct)] * gw.layers
-        res["decode_gqa"] = decode_layers(torch, mk, synth, gw, gw.B, budgets, reps=20)
+        res["decode_gqa"] = decode_layers(torch, mk, synth, gw, gw.B, budgets, reps=gw.decode_steps,
+                                          n_queries=gw.decode_steps)
         print(f"# gqa decode: {json.dumps(res['decode_gqa'])}", file=sys.stderr, flush=True)
     if not args.no_gqa_sweep:
         gw = synth.WORKLOADS["mistral_44k"]

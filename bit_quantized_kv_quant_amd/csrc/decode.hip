@@ -217,12 +217,16 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     // split plan covers the capacity n; ranges past the count are empty parts)
     if (counts) n = max(0, min(n, counts[0]));
 
-    // never-written LDS positions must read as zero: key K positions >= D, value piece 3
-    {
+    // never-written LDS positions must read as zero: key K positions >= D
+    // (D < 128 only) and value piece 3 (every other byte is rewritten each step)
+    if constexpr (D < 128) {
         uint32_t* za = reinterpret_cast<uint32_t*>(&s_qa[wave][0][0][0][0]);
         for (int i = lane; i < 4 * R * 4 * 128 / 4; i += kWave) za[i] = 0u;
-        uint32_t* zw = reinterpret_cast<uint32_t*>(&s_wa[wave][0][0][0][0]);
-        for (int i = lane; i < R * NG * 4 * 128 / 4; i += kWave) zw[i] = 0u;
+    }
+#pragma unroll
+    for (int i = lane; i < R * NG * 32; i += kWave) {  // dword i % 32 of (head, group) row i / 32
+        const int hg = i / 32;
+        reinterpret_cast<uint32_t*>(&s_wa[wave][hg / NG][hg % NG][3][0])[i % 32] = 0u;
     }
 
     // Query channels c0, c0 + 2 of this lane sit at key K positions 2 lane,
