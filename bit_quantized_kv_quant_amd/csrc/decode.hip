@@ -526,44 +526,55 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 
 // Exact part of a streaming decode for one (sequence, query head) row, by one
 // wave: the residual tokens (bf16 K / V, at most 31, slots [B][Hkv][res_stride][D]).
-// Returns m and the sum of 2^(l - m) (l = q.k in log2 units) and leaves
-// x[c] = sum of 2^(l - m) v[lane + 64 c].
+// Lane l holds channels 2l and 2l + 1 (lanes >= D / 2 carry zeros).  Every
+// window row is requested at once, one dword per lane and row, through buffer
+// resources sized to the n_res valid slots (slots past it read as zeros, no
+// branch); then one wave-wide sum per token.  Returns m and the sum of
+// 2^(l - m) (l = q.k in log2 units) and leaves x[c] = sum of 2^(l - m) v[2 lane + c].
 template <int D>
 __device__ __forceinline__ void residual_part(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_res,
                                               const uint16_t* __restrict__ v_res, int res_stride, int n_res, int Hq,
                                               int Hkv, float scale_log2, int row, int lane, float& m_out,
-                                              float& l_out, float (&x)[D / kWave]) {
-    constexpr int C = D / kWave;  // channels per lane
+                                              float& l_out, float (&x)[2]) {
+    constexpr int S = kGroup - 1;  // window slots that can hold a token
     const int b = row / Hq, h = row % Hq;
     const int g = h / (Hq / Hkv);
-    const uint16_t* kr = k_res + ((size_t)b * Hkv + g) * res_stride * D;
-    const uint16_t* vr = v_res + ((size_t)b * Hkv + g) * res_stride * D;
-    float qc[C];
+    const size_t unit = (size_t)b * Hkv + g;
+    const bool act = 2 * lane < D;
+    const int off = act ? 4 * lane : 0;  // byte offset of the lane's channel pair within a row
+    const int bytes = n_res * D * 2;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k_res + unit * res_stride * D), 0, bytes,
+                                                      0x00020000);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(v_res + unit * res_stride * D), 0, bytes,
+                                                      0x00020000);
+    uint32_t kw[S], vw[S];
 #pragma unroll
-    for (int c = 0; c < C; ++c) qc[c] = bf16_bits_to_f32(q[(size_t)row * D + lane + kWave * c]);
-    float l[kGroup];
+    for (int t = 0; t < S; ++t) kw[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, off + t * D * 2, 0, 0);
+#pragma unroll
+    for (int t = 0; t < S; ++t) vw[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, off + t * D * 2, 0, 0);
+    const uint32_t qw = act ? *reinterpret_cast<const uint32_t*>(q + (size_t)row * D + 2 * lane) : 0u;
+    const float q0 = bf16_bits_to_f32(qw & 0xFFFFu), q1 = bf16_bits_to_f32(qw >> 16);
+    float l[S];
     float m = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < kGroup - 1; ++t) {
+    for (int t = 0; t < S; ++t) {
         l[t] = -INFINITY;
-        if (t < n_res) {
-            float d = 0.0f;
-#pragma unroll
-            for (int c = 0; c < C; ++c) d = fmaf(qc[c], bf16_bits_to_f32(kr[(size_t)t * D + lane + kWave * c]), d);
+        if (t < n_res) {  // wave-uniform
+            const float d = fmaf(q0, bf16_bits_to_f32(kw[t] & 0xFFFFu), q1 * bf16_bits_to_f32(kw[t] >> 16));
             l[t] = dpp_sum<kWave>(d) * scale_log2;
             m = fmaxf(m, l[t]);
         }
     }
     float lsum = 0.0f;
+    x[0] = 0.0f;
+    x[1] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < C; ++c) x[c] = 0.0f;
-#pragma unroll
-    for (int t = 0; t < kGroup - 1; ++t) {
+    for (int t = 0; t < S; ++t) {
         if (t < n_res) {
             const float p = exp2f(l[t] - m);
             lsum += p;
-#pragma unroll
-            for (int c = 0; c < C; ++c) x[c] = fmaf(p, bf16_bits_to_f32(vr[(size_t)t * D + lane + kWave * c]), x[c]);
+            x[0] = fmaf(p, bf16_bits_to_f32(vw[t] & 0xFFFFu), x[0]);
+            x[1] = fmaf(p, bf16_bits_to_f32(vw[t] >> 16), x[1]);
         }
     }
     m_out = m;
@@ -593,10 +604,12 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     const bool res = k_res != nullptr;
     if (res && t < kWave) {
         if (counts) n_res = max(0, min(n_res, counts[1]));
-        float m_r, l_r, x[D / kWave];
+        float m_r, l_r, x[2];
         residual_part<D>(q, k_res, v_res, res_stride, n_res, Hq, Hkv, scale_log2, bh, t, m_r, l_r, x);
-#pragma unroll
-        for (int c = 0; c < D / kWave; ++c) s_res[t + kWave * c] = x[c];
+        if (2 * t < D) {
+            s_res[2 * t] = x[0];
+            s_res[2 * t + 1] = x[1];
+        }
         if (t == 0) {
             s_res[D] = m_r;
             s_res[D + 1] = l_r;
@@ -651,13 +664,14 @@ __global__ __launch_bounds__(64) void decode_residual_kernel(const uint16_t* __r
                                                              const uint16_t* __restrict__ v_res, int res_stride,
                                                              int n_res, int Hq, int Hkv, float scale_log2,
                                                              __bf16* __restrict__ out) {
-    constexpr int C = D / kWave;  // channels per lane
-    const int row = blockIdx.x;   // b * Hq + h
+    const int row = blockIdx.x;  // b * Hq + h
     const int lane = threadIdx.x;
-    float m, lsum, x[C];
+    float m, lsum, x[2];
     residual_part<D>(q, k_res, v_res, res_stride, n_res, Hq, Hkv, scale_log2, row, lane, m, lsum, x);
-#pragma unroll
-    for (int c = 0; c < C; ++c) out[(size_t)row * D + lane + kWave * c] = (__bf16)(x[c] / lsum);
+    if (2 * lane < D) {
+        out[(size_t)row * D + 2 * lane] = (__bf16)(x[0] / lsum);
+        out[(size_t)row * D + 2 * lane + 1] = (__bf16)(x[1] / lsum);
+    }
 }
 
 // Resident workgroups of a decode instantiation on the current device: the
