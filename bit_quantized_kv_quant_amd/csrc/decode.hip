@@ -529,14 +529,17 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 // Lane l holds channels 2l and 2l + 1 (lanes >= D / 2 carry zeros).  Every
 // window row is requested at once, one dword per lane and row, through buffer
 // resources sized to the n_res valid slots (slots past it read as zeros, no
-// branch); then one wave-wide sum per token.  Returns m and the sum of
-// 2^(l - m) (l = q.k in log2 units) and leaves x[c] = sum of 2^(l - m) v[2 lane + c].
+// branch); then one wave-wide sum per token.  The result: m, the sum of
+// 2^(l - m) (l = q.k in log2 units) and x[c] = sum of 2^(l - m) v[2 lane + c].
+constexpr int kResSlots = kGroup - 1;  // window slots that can hold a token
+struct ResRows {
+    uint32_t k[kResSlots], v[kResSlots];  // the lane's channel pair of every window row
+    uint32_t q;                           // the lane's channel pair of the query
+};
 template <int D>
-__device__ __forceinline__ void residual_part(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_res,
+__device__ __forceinline__ void residual_load(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_res,
                                               const uint16_t* __restrict__ v_res, int res_stride, int n_res, int Hq,
-                                              int Hkv, float scale_log2, int row, int lane, float& m_out,
-                                              float& l_out, float (&x)[2]) {
-    constexpr int S = kGroup - 1;  // window slots that can hold a token
+                                              int Hkv, int row, int lane, ResRows& rr) {
     const int b = row / Hq, h = row % Hq;
     const int g = h / (Hq / Hkv);
     const size_t unit = (size_t)b * Hkv + g;
@@ -547,20 +550,22 @@ __device__ __forceinline__ void residual_part(const uint16_t* __restrict__ q, co
                                                       0x00020000);
     const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(v_res + unit * res_stride * D), 0, bytes,
                                                       0x00020000);
-    uint32_t kw[S], vw[S];
 #pragma unroll
-    for (int t = 0; t < S; ++t) kw[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, off + t * D * 2, 0, 0);
+    for (int t = 0; t < kResSlots; ++t) rr.k[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, off + t * D * 2, 0, 0);
 #pragma unroll
-    for (int t = 0; t < S; ++t) vw[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, off + t * D * 2, 0, 0);
-    const uint32_t qw = act ? *reinterpret_cast<const uint32_t*>(q + (size_t)row * D + 2 * lane) : 0u;
-    const float q0 = bf16_bits_to_f32(qw & 0xFFFFu), q1 = bf16_bits_to_f32(qw >> 16);
-    float l[S];
+    for (int t = 0; t < kResSlots; ++t) rr.v[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, off + t * D * 2, 0, 0);
+    rr.q = act ? *reinterpret_cast<const uint32_t*>(q + (size_t)row * D + 2 * lane) : 0u;
+}
+__device__ __forceinline__ void residual_reduce(const ResRows& rr, int n_res, float scale_log2, float& m_out,
+                                                float& l_out, float (&x)[2]) {
+    const float q0 = bf16_bits_to_f32(rr.q & 0xFFFFu), q1 = bf16_bits_to_f32(rr.q >> 16);
+    float l[kResSlots];
     float m = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < S; ++t) {
+    for (int t = 0; t < kResSlots; ++t) {
         l[t] = -INFINITY;
         if (t < n_res) {  // wave-uniform
-            const float d = fmaf(q0, bf16_bits_to_f32(kw[t] & 0xFFFFu), q1 * bf16_bits_to_f32(kw[t] >> 16));
+            const float d = fmaf(q0, bf16_bits_to_f32(rr.k[t] & 0xFFFFu), q1 * bf16_bits_to_f32(rr.k[t] >> 16));
             l[t] = dpp_sum<kWave>(d) * scale_log2;
             m = fmaxf(m, l[t]);
         }
@@ -569,91 +574,122 @@ __device__ __forceinline__ void residual_part(const uint16_t* __restrict__ q, co
     x[0] = 0.0f;
     x[1] = 0.0f;
 #pragma unroll
-    for (int t = 0; t < S; ++t) {
+    for (int t = 0; t < kResSlots; ++t) {
         if (t < n_res) {
             const float p = exp2f(l[t] - m);
             lsum += p;
-            x[0] = fmaf(p, bf16_bits_to_f32(vw[t] & 0xFFFFu), x[0]);
-            x[1] = fmaf(p, bf16_bits_to_f32(vw[t] >> 16), x[1]);
+            x[0] = fmaf(p, bf16_bits_to_f32(rr.v[t] & 0xFFFFu), x[0]);
+            x[1] = fmaf(p, bf16_bits_to_f32(rr.v[t] >> 16), x[1]);
         }
     }
     m_out = m;
     l_out = lsum;
 }
 
+template <int D>
+__device__ __forceinline__ void residual_part(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_res,
+                                              const uint16_t* __restrict__ v_res, int res_stride, int n_res, int Hq,
+                                              int Hkv, float scale_log2, int row, int lane, float& m_out,
+                                              float& l_out, float (&x)[2]) {
+    ResRows rr;
+    residual_load<D>(q, k_res, v_res, res_stride, n_res, Hq, Hkv, row, lane, rr);
+    residual_reduce(rr, n_res, scale_log2, m_out, l_out, x);
+}
+
 // Merge the token ranges of one (sequence, query head): the range maxima and
 // weights 2^(m_s - M) are computed cooperatively and kept in LDS, then every
 // thread (one channel) sums its partials with several loads in flight.  With
-// k_res, wave 0 first computes the exact window part (residual_part) and it is
-// merged as one more range.
+// k_res the workgroup has one more wave, which requests the window rows at the
+// start and reduces them (residual_reduce) while the other waves sum the
+// ranges; its part is merged last, as one more range.
 constexpr int kMaxSplits = 256;
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ ws_acc,
-                                                           const float* __restrict__ ws_ml, int splits,
-                                                           __bf16* __restrict__ out, const uint16_t* __restrict__ q,
-                                                           const uint16_t* __restrict__ k_res,
-                                                           const uint16_t* __restrict__ v_res, int res_stride,
-                                                           int n_res, int Hq, int Hkv, float scale_log2,
-                                                           const int32_t* __restrict__ counts) {
+__global__ __launch_bounds__(D + kWave) void decode_combine_kernel(const float* __restrict__ ws_acc,
+                                                                   const float* __restrict__ ws_ml, int splits,
+                                                                   __bf16* __restrict__ out,
+                                                                   const uint16_t* __restrict__ q,
+                                                                   const uint16_t* __restrict__ k_res,
+                                                                   const uint16_t* __restrict__ v_res, int res_stride,
+                                                                   int n_res, int Hq, int Hkv, float scale_log2,
+                                                                   const int32_t* __restrict__ counts) {
     constexpr int NW = D / kWave;
     __shared__ float s_w[kMaxSplits];
     __shared__ float s_part[2][NW];
     __shared__ float s_res[D + 2];  // window part: sum 2^(l - m) v per channel, then m, sum 2^(l - m)
     const int bh = blockIdx.x;
     const int t = threadIdx.x;
-    const bool res = k_res != nullptr;
-    if (res && t < kWave) {
+    const bool res = k_res != nullptr;  // then blockDim.x = D + kWave
+    const bool win = t >= D;            // the window wave
+    ResRows rr;
+    if (win) {
         if (counts) n_res = max(0, min(n_res, counts[1]));
-        float m_r, l_r, x[2];
-        residual_part<D>(q, k_res, v_res, res_stride, n_res, Hq, Hkv, scale_log2, bh, t, m_r, l_r, x);
-        if (2 * t < D) {
-            s_res[2 * t] = x[0];
-            s_res[2 * t + 1] = x[1];
-        }
-        if (t == 0) {
-            s_res[D] = m_r;
-            s_res[D + 1] = l_r;
-        }
+        residual_load<D>(q, k_res, v_res, res_stride, n_res, Hq, Hkv, bh, t - D, rr);
     }
     const float* ml = ws_ml + (size_t)bh * splits * 2;
     float m = -INFINITY;
-    for (int s = t; s < splits; s += D) m = fmaxf(m, ml[2 * s]);
-    m = dpp_max<kWave>(m);
-    if (t % kWave == 0) s_part[0][t / kWave] = m;
+    if (!win) {
+        for (int s = t; s < splits; s += D) m = fmaxf(m, ml[2 * s]);
+        m = dpp_max<kWave>(m);
+        if (t % kWave == 0) s_part[0][t / kWave] = m;
+    }
     __syncthreads();
     float M = s_part[0][0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) M = fmaxf(M, s_part[0][w]);
-    if (res) M = fmaxf(M, s_res[D]);
+    // weights are taken against Ms: with every range empty (M = -inf, a
+    // streaming step with nothing packed yet) they are all 0, not NaN
+    const float Ms = M == -INFINITY ? 0.0f : M;
     float l = 0.0f;
-    for (int s = t; s < splits; s += D) {
-        const float w = exp2f(ml[2 * s] - M);
-        s_w[s] = w;
-        l = fmaf(ml[2 * s + 1], w, l);
+    if (!win) {
+        for (int s = t; s < splits; s += D) {
+            const float w = exp2f(ml[2 * s] - Ms);
+            s_w[s] = w;
+            l = fmaf(ml[2 * s + 1], w, l);
+        }
+        l = dpp_sum<kWave>(l);
+        if (t % kWave == 0) s_part[1][t / kWave] = l;
     }
-    l = dpp_sum<kWave>(l);
-    if (t % kWave == 0) s_part[1][t / kWave] = l;
     __syncthreads();
-    float L = 0.0f;
+    float o = 0.0f, L = 0.0f;
+    if (!win) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) L += s_part[1][w];
-    const float* a = ws_acc + (size_t)bh * splits * D + t;
-    float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
-    int s = 0;
-    for (; s + 4 <= splits; s += 4) {
-        o0 = fmaf(a[(size_t)s * D], s_w[s], o0);
-        o1 = fmaf(a[(size_t)(s + 1) * D], s_w[s + 1], o1);
-        o2 = fmaf(a[(size_t)(s + 2) * D], s_w[s + 2], o2);
-        o3 = fmaf(a[(size_t)(s + 3) * D], s_w[s + 3], o3);
+        for (int w = 0; w < NW; ++w) L += s_part[1][w];
+        const float* a = ws_acc + (size_t)bh * splits * D + t;
+        float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
+        int s = 0;
+        for (; s + 4 <= splits; s += 4) {
+            o0 = fmaf(a[(size_t)s * D], s_w[s], o0);
+            o1 = fmaf(a[(size_t)(s + 1) * D], s_w[s + 1], o1);
+            o2 = fmaf(a[(size_t)(s + 2) * D], s_w[s + 2], o2);
+            o3 = fmaf(a[(size_t)(s + 3) * D], s_w[s + 3], o3);
+        }
+        for (; s < splits; ++s) o0 = fmaf(a[(size_t)s * D], s_w[s], o0);
+        o = (o0 + o1) + (o2 + o3);
+    } else {
+        float m_r, l_r, x[2];
+        residual_reduce(rr, n_res, scale_log2, m_r, l_r, x);
+        const int lane = t - D;
+        if (2 * lane < D) {
+            s_res[2 * lane] = x[0];
+            s_res[2 * lane + 1] = x[1];
+        }
+        if (lane == 0) {
+            s_res[D] = m_r;
+            s_res[D + 1] = l_r;
+        }
     }
-    for (; s < splits; ++s) o0 = fmaf(a[(size_t)s * D], s_w[s], o0);
-    float o = (o0 + o1) + (o2 + o3);
     if (res) {
-        const float w = exp2f(s_res[D] - M);  // 0 for an empty window (m = -inf)
-        L = fmaf(s_res[D + 1], w, L);
-        o = fmaf(s_res[t], w, o);
+        __syncthreads();  // the window part is in s_res
+        if (!win) {
+            // one more range: rescale both sides to the larger maximum (a factor
+            // of 0 for an empty window, m = -inf)
+            const float Mt = fmaxf(M, s_res[D]);
+            const float a = M == -INFINITY ? 0.0f : exp2f(Ms - Mt), c = exp2f(s_res[D] - Mt);
+            L = fmaf(L, a, s_res[D + 1] * c);
+            o = fmaf(o, a, s_res[t] * c);
+        }
     }
-    out[(size_t)bh * D + t] = (__bf16)(o / L);
+    if (!win) out[(size_t)bh * D + t] = (__bf16)(o / L);
 }
 
 // A streaming cache with nothing packed: the window's tokens are the whole
@@ -736,7 +772,8 @@ hipError_t launch_dr(const void* q, const DecodeSrc& src, int B, int Hq, int Hkv
                        parts, direct ? 1 : 0, (int)items, scale_log2, ws_acc, ws_ml, o, src.counts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(B * Hq), dim3(D), 0, stream, ws_acc, ws_ml, parts, o, qq,
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(B * Hq), dim3(D + (res ? kWave : 0)), 0, stream, ws_acc,
+                       ws_ml, parts, o, qq,
                        res ? src.k_res : nullptr, src.v_res, src.res_stride, src.n_res, Hq, Hkv, scale_log2,
                        src.counts);
     return hipGetLastError();
