@@ -148,6 +148,8 @@ def _decode_case(dev, B, Hq, Hkv, n, D, seed, kmul=3.0, vstd=1.0):
 @pytest.mark.parametrize("B,Hq,Hkv,n,D", [
     (1, 2, 2, 64, 64), (1, 1, 1, 1, 128), (2, 4, 4, 45, 128), (3, 8, 4, 300, 128), (2, 8, 2, 1000, 128),
     (1, 4, 1, 6600, 128), (4, 2, 1, 129, 64), (8, 32, 32, 614, 128),
+    # more token ranges than merge threads: 157 ranges at D = 64, 129 at D = 128
+    (1, 2, 1, 20000, 64), (1, 2, 1, 33000, 128),
 ])
 def test_decode_matches_oracle(dev, B, Hq, Hkv, n, D):
     say("decode B", B, "Hq", Hq, "Hkv", Hkv, "n", n, "D", D)

@@ -119,6 +119,22 @@ def test_stream_residual_only(dev):
     assert_attn_close(to_np(out), oracle.stream_decode_ref(q, oracle.stream_init_ref(k, v, idx)), "residual only")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_stream_decode_many_ranges(dev, D):
+    """A long packed region (more token ranges than merge threads) plus a window: host-side
+    and device-side counts against the oracle."""
+    say("stream decode, many ranges and a window, D", D)
+    B, Hq, Hkv, T, n_sel = 1, 2, 1, 33100, 33013
+    rng, c, st = _start(dev, 5 + D, B, Hkv, T, D, n_sel, 32 * (n_sel // 32 + 2))
+    assert c.n_packed == 32 * (n_sel // 32) and c.n_res == n_sel % 32  # 32992 packed, 21 in the window
+    q = synth.bf16_round(rng.standard_normal((B, Hq, D)).astype(np.float32))
+    qd = torch.from_numpy(q).to(dev).to(torch.bfloat16)
+    ref = oracle.stream_decode_ref(q, st)
+    assert_attn_close(to_np(c.decode(qd)), ref, "host counts")
+    c.to_device_counts()
+    assert_attn_close(to_np(c.step_decode(qd)), ref, "device counts")
+
+
 # ---------------------------------------------------------------------------
 # device-side generation step (counts in device memory) and its graph replays
 # ---------------------------------------------------------------------------
