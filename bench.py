@@ -1,44 +1,37 @@
 """Benchmark of the 2-bit layer-discriminative KV-cache hot path on one MI355X.
 
-A step is one pass of the whole path over one batch of the LLaMA2-7B-shaped
-workload (8 sequences x 32 heads x 4096 tokens, head dim 128, 15 % budget):
+Headline (the JSON line's value): decode attention over the LLaMA2-13B-shaped
+layer-discriminative cache - 40 layers x 40 heads, head dim 128, context 8192,
+per-layer budget falling linearly from 30 % (2457 kept tokens) to 5 % (409),
+2-bit packed - at the batch that fills about 250 GB of HBM (1133 sequences,
+249.8 GB packed).  A step is one decode query per sequence through all 40
+layers (40 launches of the decode kernel); value = batch / step time in
+tokens/s, beside the achieved HBM GB/s and its fraction of 8 TB/s.  Kept-token
+K/V are drawn directly from the workload's distributions (bf16, 4 outlier key
+channels per head x 8, V ~ N(0, 0.5)) and packed by the library before the
+timed region, so the cache is resident in HBM when timing starts.  Each
+launch is bracketed by HIP events on the stream it runs on; the roofline
+object reports the decode kernel's algorithmic bytes per launch over its
+average launch time.  cpu_baseline times the oracle's decode of the same
+cache on a bounded sample of sequences.
 
-  selective flash attention pass 1 (o, lse)  ->  pass 2 (window scores, W = 32)
-  ->  heavy-hitter + recent selection (492 + 122 tokens)
-  ->  2-bit quantise-and-pack of the kept K / V
-  ->  decode attention of one new query per sequence over the packed cache
+Extra objects in the same line:
+  chain            the whole path on the LLaMA2-7B-shaped workload (8 x 32 heads x
+                   4096 tokens, 15 % budget): selective flash attention with the
+                   window scores, selection, quantise-and-pack, decode; per-stage
+                   HIP-event times and the prefill kernel's bf16 MFMA roofline
+                   (prefill_roofline)
+  decode           the chain's single-layer decode alone, rotating over >= 1 GB of
+                   distinct packed caches (Infinity Cache excluded)
+  decode_gqa       the Mistral-7B-shaped 32-layer GQA cache (32 / 8 heads, 6600
+                   kept of 44000, batch 4), 256 steps of fresh queries, eager and
+                   as a HIP graph replay
+  decode_stream    the same cache as generation (append + decode per layer)
+  prefill_16k, prefill_gqa_44k   single-layer prefill lines
+  variants         the comparison tables' cache policies on the chain's prompt
+  decode_pyramid_sweep (--pyramid-sweep) the pyramid decode over a batch sweep
 
-Inputs are seeded synthetic tensors already resident in HBM.  `value` is the
-whole job's token throughput: B * (T + 1) tokens (prompt plus the decoded
-token) per step.  Per-kernel durations come from HIP events recorded on the
-stream the kernels run on, over the timed steps.  Decode is additionally timed
-alone while rotating over >= 1 GB of distinct packed caches, so its HBM figure
-is not served from the 256 MB Infinity Cache.  The CPU oracle is timed on a
-bounded sample of the same work (cpu_baseline).
-
-Two multi-layer decode sweeps follow (extra objects in the JSON line): the
-LLaMA2-13B-shaped pyramid cache (40 layers x 40 heads, context 8192, per-layer
-budget 30 % -> 5 %) at a batch that fills about 227 GB of HBM, and the
-Mistral-7B-shaped GQA cache (32 layers, 32 / 8 heads, 6600 kept tokens of a
-44000-token prompt, batch 4).  A decode step there is one query per sequence
-through every layer (the Mistral-shaped sweep: 256 steps, each with fresh
-seeded queries); kept-token K/V are drawn directly from the workload's
-distributions and packed by the library.  `--pyramid-sweep` adds the
-pyramid decode's batch sweep up to the batch that fills about 250 GB (the
-maximum over the sweep is the maximum throughput).  The Mistral-shaped cache is also run
-as generation (decode_stream): 256 steps, each appending one new token per
-layer to a streaming cache (every 32nd packs the residual window) and decoding
-through all 32 layers.  Then two single-layer prefill lines
-(1 x 32 heads x 16384 tokens, and one layer of the Mistral-7B-shaped GQA
-prompt, 4 x 32 / 8 heads x 44000 tokens): passes 1 and 2, selection and
-packing, each timed alone.  Before the sweeps, the cache policies of the
-pages' comparison tables run on the chain's prompt (variants): KIVI-like
-(every token at 2 bits), H2O-like (scores from every prompt row), MiniKV
-(32-row window, 15 %) and MiniKV Pyramid (30 % -> 5 % over 32 layers), each
-with its compression, compress / decode time and decode error against exact
-attention over the full 16-bit cache.
-
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
 
 import argparse
@@ -64,8 +57,12 @@ def parse():
     ap.add_argument("--decode-rotation-gb", type=float, default=1.2)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after the timed region, run one device copy of this size (counter calibration)")
-    ap.add_argument("--pyramid-batch", type=int, default=1024,
-                    help="batch of the 40-layer pyramid decode sweep (1024 fills about 227 GB; 0 skips it)")
+    ap.add_argument("--pyramid-batch", type=int, default=1133,
+                    help="batch of the headline 40-layer pyramid decode (1133 fills about 250 GB)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="run the headline decode only (e.g. under a counter profiler)")
+    ap.add_argument("--chain-warmup", type=int, default=25,
+                    help="warm-up steps of the chain extra (a fresh process runs its first chain steps slow)")
     ap.add_argument("--pyramid-sweep", default="",
                     help="comma-separated batches for a max-throughput sweep of the 40-layer pyramid decode "
                          "(e.g. 1,64,256,512,1024,1133; 1133 fills about 250 GB); off by default")
@@ -83,17 +80,7 @@ def decode_layers(torch, mk, synth, wl, B, budgets, reps=3, chunk=64, n_queries=
     using seeded query set i % n_queries (fresh queries each step when
     n_queries >= reps)."""
     dev = torch.device("cuda:0")
-    caches = []
-    for l, n in enumerate(budgets):
-        c = mk.PackedCache.alloc(B, wl.Hkv, n, wl.D, dev)
-        for b0 in range(0, B, chunk):
-            b1 = min(B, b0 + chunk)
-            k, v = synth.make_kept_kv(wl, n, dev, seed=wl.seed * 100000 + l * 1000 + b0, B=b1 - b0)
-            sub = mk.PackedCache(c.k_codes[b0:b1], c.k_sz[b0:b1], c.v_codes[b0:b1], c.v_sz[b0:b1],
-                                 b1 - b0, wl.Hkv, n, wl.D)
-            mk.quant_pack(k, v, out=sub)
-            del k, v
-        caches.append(c)
+    caches = build_layer_caches(torch, mk, synth, wl, B, budgets, chunk)
     qs = [synth.make_decode_q(wl, dev, B=B, step=i) for i in range(max(1, n_queries))]
     q = qs[0]
     out = torch.empty_like(q)
@@ -149,6 +136,107 @@ def decode_layers(torch, mk, synth, wl, B, budgets, reps=3, chunk=64, n_queries=
             "hbm_frac": gbs / PEAK_HBM_GBS,
             "graph_ms_per_step": gms, "graph_tokens_per_s": B / (gms * 1e-3), "graph_achieved_GBs": ggbs,
             "graph_hbm_frac": ggbs / PEAK_HBM_GBS, "steps": reps, "distinct_queries": len(qs)}
+
+
+def build_layer_caches(torch, mk, synth, wl, B, budgets, chunk=64):
+    """One packed cache per layer, kept-token K/V drawn directly per chunk of
+    sequences and packed by the library into the layer's cache."""
+    dev = torch.device("cuda:0")
+    caches = []
+    t0 = time.perf_counter()
+    for l, n in enumerate(budgets):
+        if l and l % 8 == 0:
+            torch.cuda.synchronize()
+            print(f"# building {wl.name} caches: {l} of {len(budgets)} layers, {time.perf_counter() - t0:.1f} s",
+                  file=sys.stderr, flush=True)
+        c = mk.PackedCache.alloc(B, wl.Hkv, n, wl.D, dev)
+        for b0 in range(0, B, chunk):
+            b1 = min(B, b0 + chunk)
+            k, v = synth.make_kept_kv(wl, n, dev, seed=wl.seed * 100000 + l * 1000 + b0, B=b1 - b0)
+            sub = mk.PackedCache(c.k_codes[b0:b1], c.k_sz[b0:b1], c.v_codes[b0:b1], c.v_sz[b0:b1],
+                                 b1 - b0, wl.Hkv, n, wl.D)
+            mk.quant_pack(k, v, out=sub)
+            del k, v
+        caches.append(c)
+    return caches
+
+
+def pyramid_headline(torch, mk, synth, B, steps, warmup, sample_seqs=0):
+    """The headline: decode over the 40-layer pyramid cache at batch B.
+
+    Returns the step time (HIP events around the K timed steps, bracketed by
+    device synchronisation), the per-launch durations of the decode kernel
+    (one launch per layer; events on the launch stream) and the algorithmic
+    bytes: each layer's packed cache plus the bf16 query read and output
+    written."""
+    dev = torch.device("cuda:0")
+    pw = synth.WORKLOADS["llama13b_pyramid"]
+    budgets = [mk.pyramid_keep(pw.T, pw.layers, l, *pw.pyramid) for l in range(pw.layers)]
+    t0 = time.perf_counter()
+    caches = build_layer_caches(torch, mk, synth, pw, B, budgets)
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
+    n_q = 4  # distinct seeded query sets, cycled step by step
+    qs = [synth.make_decode_q(pw, dev, B=B, step=i) for i in range(n_q)]
+    out = torch.empty_like(qs[0])
+    ws = torch.empty(max(16, max(mk.decode_ws_bytes(B, pw.Hq, pw.Hkv, c.n_keep, pw.D) for c in caches)),
+                     dtype=torch.uint8, device=dev)
+    cache_bytes = [c.nbytes() for c in caches]
+    print(f"# pyramid cache: batch {B}, {sum(cache_bytes) / 1e9:.1f} GB packed, built in {build_s:.1f} s",
+          file=sys.stderr, flush=True)
+    for i in range(warmup):
+        for c in caches:
+            mk.decode_attn(qs[i % n_q], c, out=out, ws=ws)
+    torch.cuda.synchronize()
+    L = len(caches)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(L + 1)] for _ in range(steps)]
+    e_all = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    wall0 = time.perf_counter()
+    e_all[0].record()
+    for s_ in range(steps):
+        q = qs[s_ % n_q]
+        for l, c in enumerate(caches):
+            ev[s_][l].record()
+            mk.decode_attn(q, c, out=out, ws=ws)
+        ev[s_][L].record()
+    e_all[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = e_all[0].elapsed_time(e_all[1]) / steps
+    launch_ms = [[ev[s_][l].elapsed_time(ev[s_][l + 1]) for l in range(L)] for s_ in range(steps)]
+    layer_ms = [sum(launch_ms[s_][l] for s_ in range(steps)) / steps for l in range(L)]
+    qo_bytes = 2 * B * pw.Hq * pw.D * 2
+    alg_bytes = [cb + qo_bytes for cb in cache_bytes]
+    step_bytes = sum(alg_bytes)
+    kernel_ms = sum(layer_ms)
+    # the kernel plan: one token range per KV head at this batch, so the decode
+    # call is exactly one decode_partial_kernel launch per layer (no merge)
+    splits = [mk.decode_ws_bytes(B, pw.Hq, pw.Hkv, c.n_keep, pw.D) for c in caches]
+    # host copies of a bounded sample of the same cache and queries, for the
+    # oracle's timing (cpu_baseline)
+    sample = None
+    if sample_seqs:
+        sel = torch.arange(sample_seqs, device=dev)
+        sample = {"q": qs[0][sel].float().cpu().numpy(), "layers": [], "seqs": sample_seqs}
+        for c in caches:
+            ksz = c.k_sz[sel].cpu().numpy().view("uint32")
+            vsz = c.v_sz[sel].cpu().numpy().view("uint32")
+            sample["layers"].append({"k_codes": c.k_codes[sel].cpu().numpy(), "v_codes": c.v_codes[sel].cpu().numpy(),
+                                     "k_sz": ksz, "v_sz": vsz})
+    del caches, ws, out, qs
+    torch.cuda.empty_cache()
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    return {
+        "workload": "llama13b_pyramid", "batch": B, "layers": L, "q_heads": pw.Hq, "kv_heads": pw.Hkv,
+        "head_dim": pw.D, "context": pw.T, "kept_tokens_first_last": [int(budgets[0]), int(budgets[-1])],
+        "kept_tokens_per_seq_head": int(sum(budgets)), "packed_GB": sum(cache_bytes) / 1e9,
+        "cache_build_s": build_s, "ms_per_step": ms_per_step, "host_ms_per_step": wall * 1e3 / steps,
+        "tokens_per_s": B / (ms_per_step * 1e-3), "achieved_GBs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+        "step_bytes": step_bytes, "kernel_ms_per_step": kernel_ms,
+        "launch_ms_avg": kernel_ms / L, "bytes_per_launch_avg": step_bytes / L,
+        "single_range_per_head": all(x == splits[0] for x in splits),
+        "layer_ms_first_last": [layer_ms[0], layer_ms[-1]], "distinct_queries": n_q,
+    }, sample
 
 
 def prefill_layer(torch, mk, synth, wl, reps):
@@ -390,6 +478,32 @@ class StageTimer:
         return {k: v / steps for k, v in tot.items()}
 
 
+def cpu_baseline_pyramid(sample):
+    """Time the oracle's decode (dequantise, softmax attention in fp64) of the
+    sampled sequences' packed caches through all 40 layers; tokens/s."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    half = lambda w: (w & 0xFFFF).astype(np.uint16).view(np.float16)  # noqa: E731
+    packed = [{"k_codes": ly["k_codes"], "k_scale": half(ly["k_sz"]), "k_zero": half(ly["k_sz"] >> 16),
+               "v_codes": ly["v_codes"], "v_scale": half(ly["v_sz"]), "v_zero": half(ly["v_sz"] >> 16)}
+              for ly in sample["layers"]]
+    t0 = time.perf_counter()
+    for p_ in packed:
+        oracle.decode_ref(sample["q"], p_)
+    dt = time.perf_counter() - t0
+    n = sample["seqs"]
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} of the batch's sequences (all 40 heads, all 40 layers) of the same packed cache and "
+                      f"queries: the oracle's decode_ref per layer; {dt:.1f} s; BLAS threads = cores"}
+
+
 def cpu_baseline(wl, n_seq=2):
     """Time the oracle on n_seq sequences (all heads) of the same chain; report tokens/s."""
     import torch
@@ -447,19 +561,21 @@ def load_traffic(path, kernel_src):
         return None
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards per "
-              "(sequence, KV head) with no exchange, but this build measures a single GPU.",
-              file=sys.stderr)
-        sys.exit(2)
+def calibration_copy(torch, mb):
+    """One device-to-device copy of a known size, for scaling HBM counters."""
+    src = torch.empty(mb * (1 << 20), dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"# calibration copy: {src.numel()} bytes read, {dst.numel()} written", file=sys.stderr, flush=True)
+    del src, dst
+    torch.cuda.empty_cache()
 
-    import torch
 
-    import bit_quantized_kv_quant_amd as mk
-    import synth
-
+def chain(torch, mk, synth, args):
+    """The whole path on the LLaMA2-7B-shaped workload; returns (chain, prefill
+    roofline, single-layer decode) objects."""
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS["llama7b_decode"]
     B, Hq, Hkv, T, D, W = wl.B, wl.Hq, wl.Hkv, wl.T, wl.D, wl.window
@@ -507,29 +623,24 @@ def main():
         if t:
             t.mark()
 
-    for _ in range(args.warmup):
+    for _ in range(args.chain_warmup):
         step()
     torch.cuda.synchronize()
-    # timed region: whole steps, bracketed by device synchronisation
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
     t_all0.record()
     for _ in range(args.steps):
         step(timer)
     t_all1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     ms_per_step = t_all0.elapsed_time(t_all1) / args.steps
     per_stage = timer.totals(args.steps)
-    print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
-          file=sys.stderr, flush=True)
 
-    # ---- the same chain with the two passes as separate launches, for comparison ----
-    two_pass = {}
+    # the same chain with the two passes as separate launches, for comparison
+    two_pass = None
     if fused:
         timer2 = StageTimer(torch, stage_names(False))
-        for _ in range(args.warmup):
+        for _ in range(args.chain_warmup):
             step(single=False)
         torch.cuda.synchronize()
         e2 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -539,104 +650,144 @@ def main():
         e2[1].record()
         torch.cuda.synchronize()
         two_pass = {"ms_per_step": e2[0].elapsed_time(e2[1]) / args.steps, "stages_ms": timer2.totals(args.steps)}
-        step()  # leave the single-pass outputs in place
+        step()
         torch.cuda.synchronize()
 
-    # ---- decode alone, rotating over >= 1 GB of distinct packed caches ----
+    # decode alone, rotating over >= 1 GB of distinct packed caches
     cache_bytes = cache.nbytes()
-    n_rot = max(2, int(args.decode_rotation_gb * 1e9 / cache_bytes) + 1)
-    g = torch.Generator(device=dev).manual_seed(77)
-    rot = []
-    for i in range(n_rot):
-        perm = torch.rand((B, Hkv, T), generator=g, device=dev).argsort(-1)[..., :n_keep]
-        ridx = torch.sort(perm, -1).values.to(torch.int32).contiguous()
-        rot.append(mk.quant_pack(k, v, ridx))
-    torch.cuda.synchronize()
-    dec_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for c in rot[:2]:
-        mk.decode_attn(qdec, c, out=out, ws=ws)
-    reps = 3
-    dec_ev[0].record()
-    for _ in range(reps):
-        for c in rot:
+    dec = None
+    if args.decode_rotation_gb > 0:
+        n_rot = max(2, int(args.decode_rotation_gb * 1e9 / cache_bytes) + 1)
+        g = torch.Generator(device=dev).manual_seed(77)
+        rot = []
+        for i in range(n_rot):
+            perm = torch.rand((B, Hkv, T), generator=g, device=dev).argsort(-1)[..., :n_keep]
+            ridx = torch.sort(perm, -1).values.to(torch.int32).contiguous()
+            rot.append(mk.quant_pack(k, v, ridx))
+        torch.cuda.synchronize()
+        dec_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for c in rot[:2]:
             mk.decode_attn(qdec, c, out=out, ws=ws)
-    dec_ev[1].record()
-    torch.cuda.synchronize()
-    dec_ms = dec_ev[0].elapsed_time(dec_ev[1]) / (reps * n_rot)
-    q_out_bytes = 2 * B * Hq * D * 2
-    dec_bytes = cache_bytes + q_out_bytes
-    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
-    del rot
-
-    if args.calibrate_copy_mb:
-        src = torch.empty(args.calibrate_copy_mb * (1 << 20), dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
+        reps = 3
+        dec_ev[0].record()
+        for _ in range(reps):
+            for c in rot:
+                mk.decode_attn(qdec, c, out=out, ws=ws)
+        dec_ev[1].record()
         torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"# calibration copy: {src.numel()} bytes read, {dst.numel()} written", file=sys.stderr)
+        dec_ms = dec_ev[0].elapsed_time(dec_ev[1]) / (reps * n_rot)
+        dec_bytes = cache_bytes + 2 * B * Hq * D * 2
+        dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+        dec = {"workload": "llama7b_decode", "tokens_per_s": B / (dec_ms * 1e-3), "ms": dec_ms, "bytes": dec_bytes,
+               "achieved_GBs": dec_gbs, "hbm_frac": dec_gbs / PEAK_HBM_GBS, "rotated_caches": n_rot,
+               "rotation_bytes": n_rot * cache_bytes}
+        del rot
 
-    # ---- roofline of the dominant kernel (prefill pass 1, MFMA-bound) ----
+    if args.calibrate_copy_mb and not args.headline_only:
+        calibration_copy(torch, args.calibrate_copy_mb)
+
+    # roofline of the prefill kernel (bf16 / fp16 MFMA-bound)
     flops = 2.0 * D * T * (T + 1) * Hq * B   # causal pairs only: QK^T and PV
     if fused:  # plus the window rows' QK^T of the score pass (causal pairs)
         flops += 2.0 * D * (W * T - W * (W - 1) / 2) * Hq * B
     k1_ms = per_stage["prefill_attn_scores" if fused else "prefill_attn"]
-    achieved = flops / (k1_ms * 1e-3) / 1e12
-    tokens_per_step = B * (T + 1)
-    value = tokens_per_step / (ms_per_step * 1e-3)
+    tflops = flops / (k1_ms * 1e-3) / 1e12
+    prefill_roof = {"bound": "mfma", "kernel": "fa_fwd_kernel (pass 1" + (" with the window scores)" if fused else ")"),
+                    "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tflops / PEAK_BF16_TFLOPS,
+                    "traffic": load_traffic(os.path.join(ROOT, "profiles", "fa_fwd_llama7b_hbm_traffic.md"),
+                                            os.path.join(ROOT, "bit_quantized_kv_quant_amd", "csrc", "prefill.hip")),
+                    "flops_per_launch": flops, "launch_ms": k1_ms}
+    res = {"workload": "llama7b_decode chain: prefill + window scores + select + 2-bit pack + decode",
+           "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "context": T, "window": W,
+           "n_keep": n_keep, "n_heavy": n_heavy, "n_recent": n_recent, "steps": args.steps,
+           "warmup": args.chain_warmup, "ms_per_step": ms_per_step,
+           "prompt_tokens_per_s": B * (T + 1) / (ms_per_step * 1e-3),
+           "output_tokens_per_s": B / (ms_per_step * 1e-3), "stages_ms": per_stage,
+           "single_pass_scores": fused, "two_pass_chain": two_pass}
+    del q, k, v, qdec, o, lse, scores, idx, cache, out, ws
+    torch.cuda.empty_cache()
+    return res, prefill_roof, dec
 
+
+def variants(torch, mk, synth):
+    """The comparison tables' cache policies on the chain's prompt and on a
+    heavy-hitter prompt of the same shape (32-layer plans)."""
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS["llama7b_decode"]
+    q, k, v, _ = synth.make_qkv(wl, dev)
+    qdec = synth.make_decode_q(wl, dev)
+    res = {"iid": variants_compare(
+        torch, mk, q, k, v, qdec, 32, "llama7b_decode prompt (iid Gaussian, outlier key channels), "
+        "one decode query per sequence")}
+    del q, k, v, qdec
+    qh, kh, vh, qdh = synth.make_heavy_qkv(wl, dev)
+    res["heavy_hitters"] = variants_compare(
+        torch, mk, qh, kh, vh, qdh, 32, "llama7b_decode shape, 5 % of keys and every query share a "
+        "direction (strength 7): attention concentrated on heavy hitters")
+    del qh, kh, vh, qdh
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards per "
+              "(sequence, KV head) with no exchange, but this build measures a single GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_quantized_kv_quant_amd as mk
+    import synth
+
+    print(f"# libminikv build {mk.build_id()} ({mk.lib_path()})", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+
+    # ---- headline: 40-layer pyramid decode at the ~250 GB batch ----
+    head, sample = pyramid_headline(torch, mk, synth, args.pyramid_batch, args.steps, args.warmup,
+                                    sample_seqs=0 if args.no_cpu_baseline else 4)
+    print(f"# headline: {json.dumps(head)}", file=sys.stderr, flush=True)
+    traffic = load_traffic(os.path.join(ROOT, "profiles", "decode_pyramid_hbm_traffic.md"),
+                           os.path.join(ROOT, "bit_quantized_kv_quant_amd", "csrc", "decode.hip"))
+    achieved = head["bytes_per_launch_avg"] / (head["launch_ms_avg"] * 1e-3) / 1e9
     res = {
         "metric": METRIC,
-        "value": value,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "e2m1 x e4m3 MFMA on 2-bit codes, fp32 softmax; bf16 q / out",
         "data": "synthetic",
-        "config": {"workload": "llama7b_decode chain: prefill + window scores + select + 2-bit pack + decode",
-                   "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "context": T, "window": W,
-                   "n_keep": n_keep, "n_heavy": n_heavy, "n_recent": n_recent, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "fa_fwd_kernel (pass 1" + (" with the window scores)" if fused else ")"),
-                     "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": load_traffic(os.path.join(ROOT, "profiles", "fa_fwd_llama7b_hbm_traffic.md"),
-                                             os.path.join(ROOT, "bit_quantized_kv_quant_amd", "csrc",
-                                                          "prefill.hip")),
-                     "flops_per_launch": flops},
-        "stages_ms": per_stage,
-        "single_pass_scores": fused,
-        "two_pass_chain": two_pass or None,
-        "decode": {"tokens_per_s": B / (dec_ms * 1e-3), "ms": dec_ms, "bytes": dec_bytes,
-                   "achieved_GBs": dec_gbs, "hbm_frac": dec_gbs / PEAK_HBM_GBS, "rotated_caches": n_rot,
-                   "rotation_bytes": n_rot * cache_bytes},
-        "output_tokens_per_s": B / (ms_per_step * 1e-3),
+        "config": {"workload": "llama13b_pyramid decode: 40 layers x 40 heads, head dim 128, context 8192, "
+                               "budget 30 % -> 5 % (2457 -> 409 kept tokens), one query per sequence per step",
+                   "batch": head["batch"], "packed_GB": head["packed_GB"], "layers": head["layers"],
+                   "q_heads": head["q_heads"], "kv_heads": head["kv_heads"], "head_dim": head["head_dim"],
+                   "context": head["context"], "parallelism": "single GPU"},
+        "achieved_GBs": head["achieved_GBs"],
+        "hbm_frac": head["hbm_frac"],
+        "roofline": {"bound": "hbm", "kernel": "decode_partial_kernel<128, 1> (one launch per layer)",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic, "bytes_per_launch": head["bytes_per_launch_avg"],
+                     "launch_ms": head["launch_ms_avg"]},
+        "decode_pyramid": head,
     }
-    # ---- cache policies of the comparison tables on this prompt (32-layer plans) ----
-    del o, lse, scores, idx, cache, out, ws
-    torch.cuda.empty_cache()
-    if not args.no_variants:
-        res["variants"] = {"iid": variants_compare(
-            torch, mk, q, k, v, qdec, 32, "llama7b_decode prompt (iid Gaussian, outlier key channels), "
-            "one decode query per sequence")}
-        qh, kh, vh, qdh = synth.make_heavy_qkv(wl, dev)
-        res["variants"]["heavy_hitters"] = variants_compare(
-            torch, mk, qh, kh, vh, qdh, 32, "llama7b_decode shape, 5 % of keys and every query share a "
-            "direction (strength 7): attention concentrated on heavy hitters")
-        del qh, kh, vh, qdh
-        print(f"# variants: {json.dumps(res['variants'])}", file=sys.stderr, flush=True)
-    # ---- multi-layer decode sweeps (the chain's buffers are released first) ----
-    del q, k, v, qdec
-    torch.cuda.empty_cache()
-    if args.pyramid_batch > 0:
-        pw = synth.WORKLOADS["llama13b_pyramid"]
-        budgets = [mk.pyramid_keep(pw.T, pw.layers, l, *pw.pyramid) for l in range(pw.layers)]
-        res["decode_pyramid"] = decode_layers(torch, mk, synth, pw, args.pyramid_batch, budgets)
-        print(f"# pyramid decode: {json.dumps(res['decode_pyramid'])}", file=sys.stderr, flush=True)
+    if args.headline_only:
+        if args.calibrate_copy_mb:
+            calibration_copy(torch, args.calibrate_copy_mb)
+        if sample is not None:
+            res["cpu_baseline"] = cpu_baseline_pyramid(sample)
+        print(json.dumps(res), flush=True)
+        return
+    res["chain"], res["prefill_roofline"], res["decode"] = chain(torch, mk, synth, args)
+    print(f"# chain: {json.dumps(res['chain'])}", file=sys.stderr, flush=True)
     if args.pyramid_sweep:
         pw = synth.WORKLOADS["llama13b_pyramid"]
         budgets = [mk.pyramid_keep(pw.T, pw.layers, l, *pw.pyramid) for l in range(pw.layers)]
@@ -654,8 +805,6 @@ def main():
         res["decode_gqa"] = decode_layers(torch, mk, synth, gw, gw.B, budgets, reps=gw.decode_steps,
                                           n_queries=gw.decode_steps)
         print(f"# gqa decode: {json.dumps(res['decode_gqa'])}", file=sys.stderr, flush=True)
-    if not args.no_gqa_sweep:
-        gw = synth.WORKLOADS["mistral_44k"]
         res["decode_stream"] = decode_stream(torch, mk, synth, gw, gw.decode_steps)
         print(f"# streaming decode: {json.dumps(res['decode_stream'])}", file=sys.stderr, flush=True)
     if not args.no_prefill_sweep:
@@ -663,8 +812,12 @@ def main():
         print(f"# prefill 16k: {json.dumps(res['prefill_16k'])}", file=sys.stderr, flush=True)
         res["prefill_gqa_44k"] = prefill_layer(torch, mk, synth, synth.WORKLOADS["mistral_44k"], reps=3)
         print(f"# prefill gqa 44k (one layer): {json.dumps(res['prefill_gqa_44k'])}", file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl)
+    if not args.no_variants:
+        res["variants"] = variants(torch, mk, synth)
+        print(f"# variants: {json.dumps(res['variants'])}", file=sys.stderr, flush=True)
+    if sample is not None:
+        res["cpu_baseline"] = cpu_baseline_pyramid(sample)
+        res["chain"]["cpu_baseline"] = cpu_baseline(synth.WORKLOADS["llama7b_decode"])
     print(json.dumps(res), flush=True)
 
 

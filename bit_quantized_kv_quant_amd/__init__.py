@@ -6,7 +6,7 @@ over the packed cache - runs in the HIP kernels of libminikv.so (C ABI in
 include/minikv.h).  This package is the thin Python binding.
 """
 
-from ._lib import MinikvError, lib, status_string  # noqa: F401
+from ._lib import MinikvError, build_id, lib, lib_path, status_string  # noqa: F401
 from .api import (  # noqa: F401
     PackedCache,
     StreamCache,
@@ -21,6 +21,7 @@ from .api import (  # noqa: F401
     pyramid_keep,
     quant_pack,
     select_topk,
+    select_ws_bytes,
     split_heavy_recent,
 )
 from .variants import POLICIES, Policy, compress, layer_plan  # noqa: F401

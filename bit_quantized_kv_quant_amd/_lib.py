@@ -7,9 +7,10 @@ missing this module raises; there is no fallback path.
 import ctypes
 import os
 
+from . import build as _build
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# MINIKV_LIB may name another build of the same library (e.g. a tuning variant).
-LIB_PATH = os.environ.get("MINIKV_LIB") or os.path.join(_HERE, "libminikv.so")
+LIB_PATH = os.path.join(_HERE, "libminikv.so")
 
 OK = 0
 ERR_NULL = -1
@@ -24,6 +25,7 @@ GROUP = 32
 
 # Every function the header declares, with its ctypes signature.
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_ip = ctypes.POINTER(ctypes.c_int)
 
 
 class PackedT(ctypes.Structure):
@@ -47,7 +49,8 @@ SIGNATURES = {
     "minikv_window_scores": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _vp]),
     "minikv_prefill_attn_scores": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp]),
     "minikv_prefill_fuses_scores": (_i, [_i, _i, _i, _i, _i]),
-    "minikv_select_topk": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp]),
+    "minikv_select_topk": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "minikv_select_ws_bytes": (_sz, [_i, _i, _i]),
     "minikv_quant_pack": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(PackedT), _vp]),
     "minikv_decode_attn": (_i, [_vp, ctypes.POINTER(PackedT), _i, _f, _vp, _vp, _sz, _vp]),
     "minikv_stream_pack": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
@@ -55,6 +58,8 @@ SIGNATURES = {
     "minikv_stream_decode": (_i, [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _f, _vp, _vp,
                                   _sz, _vp]),
     "minikv_stream_decode_ws_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "minikv_stream_init": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _ip, _ip, _vp]),
+    "minikv_stream_append_token": (_i, [_vp, _vp, _i, _i, _i, _i, _ip, _ip, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "minikv_stream_set_counts": (_i, [_vp, _i, _i, _i, _vp]),
     "minikv_stream_step_append": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "minikv_stream_step_decode_ws_bytes": (_sz, [_i, _i, _i, _i, _i]),
@@ -66,6 +71,7 @@ SIGNATURES = {
     "minikv_pyramid_keep": (_i, [_i, _i, _i, _i, _i]),
     "minikv_split_heavy_recent": (_i, [_i, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]),
     "minikv_status_string": (ctypes.c_char_p, [_i]),
+    "minikv_build_id": (ctypes.c_char_p, []),
 }
 
 _lib = None
@@ -78,7 +84,12 @@ class MinikvError(RuntimeError):
 
 
 def lib():
-    """Load libminikv.so once; raise if it has not been built."""
+    """Load the in-tree libminikv.so once.
+
+    Raises if it has not been built, or if its build id (a hash of the sources
+    it was compiled from) is not that of the sources beside it: a stale binary
+    is never used.
+    """
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
@@ -89,8 +100,21 @@ def lib():
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args
+        built, want = handle.minikv_build_id().decode(), _build.source_hash()
+        if built != want:
+            raise RuntimeError(f"{LIB_PATH} was built from other sources ({built}, sources are {want}): "
+                               "rebuild it with `python -m bit_quantized_kv_quant_amd.build`")
         _lib = handle
     return _lib
+
+
+def build_id():
+    """Source hash the loaded library was built from."""
+    return lib().minikv_build_id().decode()
+
+
+def lib_path():
+    return LIB_PATH
 
 
 def status_string(status):

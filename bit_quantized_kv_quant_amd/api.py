@@ -128,14 +128,24 @@ def prefill_fuses_scores(B, T, Hq, Hkv, window):
     return bool(_lib.lib().minikv_prefill_fuses_scores(int(B), int(T), int(Hq), int(Hkv), int(window)))
 
 
-def select_topk(scores, n_heavy, n_recent, idx=None):
+def select_ws_bytes(B, Hkv, T):
+    return int(_lib.lib().minikv_select_ws_bytes(int(B), int(Hkv), int(T)))
+
+
+def select_topk(scores, n_heavy, n_recent, idx=None, ws=None):
+    """Heavy-hitter + recent selection: scores fp32 [B, Hkv, T] -> idx int32 [B, Hkv, n], ascending."""
     B, Hkv, T = scores.shape
     _need(scores, torch.float32, (B, Hkv, T), "scores")
     n = n_heavy + n_recent
     if idx is None:
         idx = torch.empty((B, Hkv, n), dtype=torch.int32, device=scores.device)
     _need(idx, torch.int32, (B, Hkv, n), "idx")
-    st = _lib.lib().minikv_select_topk(_ptr(scores), B, Hkv, T, int(n_heavy), int(n_recent), _ptr(idx), _stream())
+    need = select_ws_bytes(B, Hkv, T)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = _lib.lib().minikv_select_topk(_ptr(scores), B, Hkv, T, int(n_heavy), int(n_recent), _ptr(idx), _ptr(ws),
+                                       ws_bytes, _stream())
     _lib.check("minikv_select_topk", st)
     return idx
 
@@ -219,51 +229,40 @@ class StreamCache:
             torch.empty((B, Hkv, _lib.GROUP, D), dtype=torch.bfloat16, device=device),
             B, Hkv, cap, D)
 
-    def _pack(self, k, v, idx, idx_stride, n, T):
-        dt = _lib.BF16 if k.dtype == torch.bfloat16 else _lib.F32
-        idx_ptr = None if idx is None else idx
-        st = _lib.lib().minikv_stream_pack(_ptr(k), _ptr(v), dt, idx_ptr, int(idx_stride), self.B, self.Hkv, int(T),
-                                           self.D, int(n), self.cap, self.n_packed, _ptr(self.k_codes),
-                                           _ptr(self.k_sz), _ptr(self.v_codes), _ptr(self.v_sz), _stream())
-        _lib.check("minikv_stream_pack", st)
-        self.n_packed += n
+    def _bufs(self):
+        return (_ptr(self.k_codes), _ptr(self.k_sz), _ptr(self.v_codes), _ptr(self.v_sz), _ptr(self.k_res),
+                _ptr(self.v_res))
 
     def init(self, k, v, idx):
         """Start from a selection idx int32 [B, Hkv, n] of bf16 k, v [B, Hkv, T, D]:
-        its first whole groups are packed, the rest go to the window."""
+        the library packs its whole groups and puts the rest in the window."""
         B, Hkv, T, D = k.shape
         _need(k, torch.bfloat16, (self.B, self.Hkv, T, self.D), "k")
         _need(v, torch.bfloat16, (self.B, self.Hkv, T, self.D), "v")
         n = idx.shape[-1]
         _need(idx, torch.int32, (self.B, self.Hkv, n), "idx")
-        n_pk = _lib.GROUP * (n // _lib.GROUP)
-        self.n_packed, self.n_res = 0, 0
-        if n_pk > self.cap:
-            raise ValueError("selection larger than the cache capacity")
-        if n_pk:
-            self._pack(k, v, idx.data_ptr(), n, n_pk, T)
-        if n > n_pk:
-            st = _lib.lib().minikv_stream_append(_ptr(k), _ptr(v), idx.data_ptr() + 4 * n_pk, n, self.B, self.Hkv,
-                                                 T, self.D, n - n_pk, 0, _ptr(self.k_res), _ptr(self.v_res),
-                                                 _stream())
-            _lib.check("minikv_stream_append", st)
-            self.n_res = n - n_pk
+        n_packed, n_res = ctypes.c_int(self.n_packed), ctypes.c_int(self.n_res)
+        kc, ks, vc, vs, kr, vr = self._bufs()
+        st = _lib.lib().minikv_stream_init(_ptr(k), _ptr(v), _ptr(idx), self.B, self.Hkv, int(T), self.D, int(n),
+                                           self.cap, kc, ks, vc, vs, kr, vr, ctypes.byref(n_packed),
+                                           ctypes.byref(n_res), _stream())
+        _lib.check("minikv_stream_init", st)
+        self.n_packed, self.n_res = n_packed.value, n_res.value
         return self
 
     def append(self, k_new, v_new):
         """One generated token per (sequence, KV head): k_new, v_new bf16 [B, Hkv, D].
-        Packs the window as the next group when it fills."""
+        The library packs the window as the next group when the token fills it
+        (a full cache raises MinikvError with the shape status)."""
         _need(k_new, torch.bfloat16, (self.B, self.Hkv, self.D), "k_new")
         _need(v_new, torch.bfloat16, (self.B, self.Hkv, self.D), "v_new")
-        st = _lib.lib().minikv_stream_append(_ptr(k_new), _ptr(v_new), None, 1, self.B, self.Hkv, 1, self.D, 1,
-                                             self.n_res, _ptr(self.k_res), _ptr(self.v_res), _stream())
-        _lib.check("minikv_stream_append", st)
-        self.n_res += 1
-        if self.n_res == _lib.GROUP:
-            if self.n_packed + _lib.GROUP > self.cap:
-                raise ValueError("streaming cache is full")
-            self._pack(self.k_res, self.v_res, None, _lib.GROUP, _lib.GROUP, _lib.GROUP)
-            self.n_res = 0
+        n_packed, n_res = ctypes.c_int(self.n_packed), ctypes.c_int(self.n_res)
+        kc, ks, vc, vs, kr, vr = self._bufs()
+        st = _lib.lib().minikv_stream_append_token(_ptr(k_new), _ptr(v_new), self.B, self.Hkv, self.D, self.cap,
+                                                   ctypes.byref(n_packed), ctypes.byref(n_res), kc, ks, vc, vs, kr,
+                                                   vr, _stream())
+        _lib.check("minikv_stream_append_token", st)
+        self.n_packed, self.n_res = n_packed.value, n_res.value
         return self
 
     def ws_bytes(self, Hq):

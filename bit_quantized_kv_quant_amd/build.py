@@ -9,6 +9,7 @@ quantiser is compiled without multiply-add contraction so its codes match an
 IEEE evaluation bit for bit.
 """
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -50,6 +51,19 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+def source_hash():
+    """Build id of the library: the first 16 hex digits of a sha256 over every
+    kernel, header and public-header source (name and bytes, in name order)."""
+    h = hashlib.sha256()
+    files = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".h"))]
+    files += [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
+    for path in sorted(files, key=os.path.basename):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return "sha256:" + h.hexdigest()[:16]
+
+
 def build(verbose=False, extra_flags=(), out=None):
     """Compile every source and link the shared library; returns its path."""
     cc = hipcc()
@@ -57,9 +71,11 @@ def build(verbose=False, extra_flags=(), out=None):
     tmp = tempfile.mkdtemp(prefix="minikv_build_")
     try:
         procs, objs = [], []
+        build_id = f'-DMINIKV_BUILD_ID="{source_hash()}"'
         for src in sources():
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
-            cmd = [cc, *COMMON, *extra_flags, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *COMMON, build_id, *extra_flags, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src),
+                   "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

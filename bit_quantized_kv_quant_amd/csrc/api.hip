@@ -20,6 +20,11 @@ bool supported_d(int D) { return D == 64 || D == 128; }
 
 extern "C" {
 
+#ifndef MINIKV_BUILD_ID
+#define MINIKV_BUILD_ID "sha256:unknown"
+#endif
+const char* minikv_build_id(void) { return MINIKV_BUILD_ID; }
+
 const char* minikv_status_string(int status) {
     switch (status) {
         case MINIKV_OK: return "ok";
@@ -126,14 +131,25 @@ int minikv_prefill_fuses_scores(int B, int T, int Hq, int Hkv, int window) {
     return minikv::prefill_fuses_scores(B, T, Hq, Hkv, window) ? 1 : 0;
 }
 
+size_t minikv_select_ws_bytes(int B, int Hkv, int T) {
+    // one workgroup per row keeps the row's keys (registers, or L2 re-reads past
+    // 32 per thread) and its radix histograms (LDS) on chip: nothing in HBM
+    (void)B;
+    (void)Hkv;
+    (void)T;
+    return 0;
+}
+
 int minikv_select_topk(const float* scores, int B, int Hkv, int T, int n_heavy, int n_recent, int32_t* idx,
-                       void* stream) {
+                       void* ws, size_t ws_bytes, void* stream) {
     if (!scores || !idx) return MINIKV_ERR_NULL;
     if (B < 1 || Hkv < 1 || T < 1 || n_heavy < 0 || n_recent < 0 || n_heavy + n_recent < 1 ||
         n_heavy + n_recent > T)
         return MINIKV_ERR_SHAPE;
     if (T - n_recent > 65536) return MINIKV_ERR_UNSUPPORTED;
-    if (misaligned(scores) || misaligned(idx)) return MINIKV_ERR_ALIGN;
+    if (misaligned(scores) || misaligned(idx) || (ws && misaligned(ws))) return MINIKV_ERR_ALIGN;
+    const size_t need = minikv_select_ws_bytes(B, Hkv, T);
+    if (need > 0 && (!ws || ws_bytes < need)) return MINIKV_ERR_WORKSPACE;
     return status_of(minikv::launch_select_topk(scores, B, Hkv, T, n_heavy, n_recent, idx, as_stream(stream)));
 }
 
@@ -197,6 +213,66 @@ int minikv_stream_append(const void* k, const void* v, const int32_t* idx, int i
     if (misaligned(k) || misaligned(v) || misaligned(k_res) || misaligned(v_res)) return MINIKV_ERR_ALIGN;
     return status_of(minikv::launch_stream_append(k, v, idx, idx ? idx_stride : n, B, Hkv, T, D, n, slot, k_res,
                                                   v_res, as_stream(stream)));
+}
+
+int minikv_stream_init(const void* k, const void* v, const int32_t* idx, int B, int Hkv, int T, int D, int n_keep,
+                       int cap, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes, uint32_t* v_sz, void* k_res,
+                       void* v_res, int* n_packed, int* n_res, void* stream) {
+    if (!k || !v || !idx || !k_codes || !k_sz || !v_codes || !v_sz || !k_res || !v_res || !n_packed || !n_res)
+        return MINIKV_ERR_NULL;
+    if (B < 1 || Hkv < 1 || T < 1 || n_keep < 1 || n_keep > T || cap < MINIKV_GROUP || cap % MINIKV_GROUP)
+        return MINIKV_ERR_SHAPE;
+    // whole 32-token groups are packed; the rest (at most 31) wait in the window
+    const int pk = MINIKV_GROUP * (n_keep / MINIKV_GROUP), rest = n_keep - pk;
+    if (pk > cap) return MINIKV_ERR_SHAPE;
+    if (!supported_d(D)) return MINIKV_ERR_UNSUPPORTED;
+    if (misaligned(k) || misaligned(v) || misaligned(idx) || misaligned(k_codes) || misaligned(k_sz) ||
+        misaligned(v_codes) || misaligned(v_sz) || misaligned(k_res) || misaligned(v_res))
+        return MINIKV_ERR_ALIGN;
+    const hipStream_t st = as_stream(stream);
+    if (pk > 0) {
+        const int e = status_of(minikv::launch_stream_pack(k, v, true, idx, n_keep, B, Hkv, T, D, pk, cap, 0,
+                                                           k_codes, k_sz, v_codes, v_sz, st));
+        if (e != MINIKV_OK) return e;
+    }
+    if (rest > 0) {
+        const int e = status_of(minikv::launch_stream_append(k, v, idx + pk, n_keep, B, Hkv, T, D, rest, 0, k_res,
+                                                             v_res, st));
+        if (e != MINIKV_OK) return e;
+    }
+    *n_packed = pk;
+    *n_res = rest;
+    return MINIKV_OK;
+}
+
+int minikv_stream_append_token(const void* k_new, const void* v_new, int B, int Hkv, int D, int cap, int* n_packed,
+                               int* n_res, uint8_t* k_codes, uint32_t* k_sz, uint8_t* v_codes, uint32_t* v_sz,
+                               void* k_res, void* v_res, void* stream) {
+    if (!k_new || !v_new || !n_packed || !n_res || !k_codes || !k_sz || !v_codes || !v_sz || !k_res || !v_res)
+        return MINIKV_ERR_NULL;
+    if (B < 1 || Hkv < 1 || cap < MINIKV_GROUP || cap % MINIKV_GROUP) return MINIKV_ERR_SHAPE;
+    const int np = *n_packed, nr = *n_res;
+    if (np < 0 || np % MINIKV_GROUP || np > cap || nr < 0 || nr >= MINIKV_GROUP) return MINIKV_ERR_SHAPE;
+    // this token fills the window: it is packed as the next group, which must fit
+    const bool flush = nr + 1 == MINIKV_GROUP;
+    if (flush && np + MINIKV_GROUP > cap) return MINIKV_ERR_SHAPE;
+    if (!supported_d(D)) return MINIKV_ERR_UNSUPPORTED;
+    if (misaligned(k_new) || misaligned(v_new) || misaligned(k_codes) || misaligned(k_sz) || misaligned(v_codes) ||
+        misaligned(v_sz) || misaligned(k_res) || misaligned(v_res))
+        return MINIKV_ERR_ALIGN;
+    const hipStream_t st = as_stream(stream);
+    int e = status_of(minikv::launch_stream_append(k_new, v_new, nullptr, 1, B, Hkv, 1, D, 1, nr, k_res, v_res, st));
+    if (e != MINIKV_OK) return e;
+    if (flush) {
+        e = status_of(minikv::launch_stream_pack(k_res, v_res, true, nullptr, MINIKV_GROUP, B, Hkv, MINIKV_GROUP, D,
+                                                 MINIKV_GROUP, cap, np, k_codes, k_sz, v_codes, v_sz, st));
+        if (e != MINIKV_OK) return e;
+        *n_packed = np + MINIKV_GROUP;
+        *n_res = 0;
+    } else {
+        *n_res = nr + 1;
+    }
+    return MINIKV_OK;
 }
 
 size_t minikv_stream_decode_ws_bytes(int B, int Hq, int Hkv, int n_packed, int n_res, int D) {

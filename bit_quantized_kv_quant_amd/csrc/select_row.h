@@ -1,6 +1,6 @@
 // Heavy-hitter + recent-window selection of one (sequence, KV head) row by
-// one workgroup: the device code shared by the selection kernel (select.hip)
-// and the fused selection + quantise-and-pack kernel (quant_pack.hip).
+// one workgroup: the device code of the selection kernel (select.hip), kept
+// as a header so that another kernel can run a row's selection in place.
 //
 // Method: gptget.net summary of arXiv 2411.18077, 术语表 "adaptive KV" (keep
 // the KV states chosen by importance) and 方法论 (2-bit quantisation combined

@@ -130,11 +130,20 @@ int minikv_prefill_fuses_scores(int B, int T, int Hq, int Hkv, int window);
  * scores fp32 [B][Hkv][T] (non-negative) -> idx int32 [B][Hkv][n_heavy+n_recent]:
  * positions T-n_recent..T-1 plus the n_heavy largest scores among positions
  * < T-n_recent (equal scores: the lower position first), ascending.
- * Errors: NULL; SHAPE if n_heavy<0, n_recent<0, n_heavy+n_recent<1 or > T;
- * UNSUPPORTED if T - n_recent > 65536; ALIGN; LAUNCH.
+ * ws: device workspace of at least minikv_select_ws_bytes(B, Hkv, T) bytes,
+ * caller-owned; when that size is 0 (every supported shape today: one
+ * workgroup per row keeps its keys and histograms on chip) ws may be NULL and
+ * ws_bytes 0.
+ * Errors: NULL (scores, idx); SHAPE if n_heavy<0, n_recent<0,
+ * n_heavy+n_recent<1 or > T; UNSUPPORTED if T - n_recent > 65536; ALIGN;
+ * WORKSPACE; LAUNCH.
  */
 int minikv_select_topk(const float *scores, int B, int Hkv, int T,
-                       int n_heavy, int n_recent, int32_t *idx, void *stream);
+                       int n_heavy, int n_recent, int32_t *idx,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes minikv_select_topk needs (0 also for invalid sizes). */
+size_t minikv_select_ws_bytes(int B, int Hkv, int T);
 
 /*
  * 2-bit asymmetric min/max quantise-and-pack of the kept tokens (method
@@ -233,6 +242,35 @@ int minikv_stream_decode(const void *q, int B, int Hq, int Hkv, int D, int cap, 
 size_t minikv_stream_decode_ws_bytes(int B, int Hq, int Hkv, int n_packed, int n_res, int D);
 
 /*
+ * The same two operations with the decisions taken here and the host-side
+ * counts kept in caller-owned ints (bf16 K/V; streaming layout as above).
+ *
+ * minikv_stream_init starts a cache from a selection idx int32 [B][Hkv][n_keep]
+ * (ascending, row stride n_keep) of k, v bf16 [B][Hkv][T][D]: the first
+ * 32*floor(n_keep/32) selected tokens are packed at token 0, the remaining
+ * n_keep mod 32 are copied into window slots 0.., and *n_packed, *n_res are
+ * set to those two counts.  Errors: NULL (any pointer); SHAPE (sizes < 1,
+ * n_keep > T, cap not a positive multiple of 32, the packed part > cap);
+ * UNSUPPORTED (D); ALIGN; LAUNCH.  On an error nothing is enqueued (LAUNCH
+ * aside) and the counts are unchanged.
+ *
+ * minikv_stream_append_token appends k_new, v_new bf16 [B][Hkv][D] into window
+ * slot *n_res; when that token fills the window the window is packed at token
+ * *n_packed (the minikv_stream_pack rule) and emptied.  The counts advance
+ * (*n_res + 1, or *n_packed + 32 and *n_res = 0).  Errors: NULL; SHAPE (sizes,
+ * counts out of range, or the window would have to be packed past cap: then
+ * nothing is enqueued and the counts are unchanged); UNSUPPORTED (D); ALIGN;
+ * LAUNCH.
+ */
+int minikv_stream_init(const void *k, const void *v, const int32_t *idx, int B, int Hkv, int T, int D,
+                       int n_keep, int cap, uint8_t *k_codes, uint32_t *k_sz, uint8_t *v_codes,
+                       uint32_t *v_sz, void *k_res, void *v_res, int *n_packed, int *n_res, void *stream);
+
+int minikv_stream_append_token(const void *k_new, const void *v_new, int B, int Hkv, int D, int cap,
+                               int *n_packed, int *n_res, uint8_t *k_codes, uint32_t *k_sz,
+                               uint8_t *v_codes, uint32_t *v_sz, void *k_res, void *v_res, void *stream);
+
+/*
  * A generation step with the counts in device memory, so that the step is a
  * fixed sequence of launches a HIP graph can capture and replay (the host no
  * longer passes n_packed / n_res).  counts: device int32[4], caller-owned,
@@ -298,6 +336,10 @@ int minikv_split_heavy_recent(int n_keep, int *n_heavy, int *n_recent);
 
 /* Static description of a status code. */
 const char *minikv_status_string(int status);
+
+/* Identity of this build: "sha256:" and the first 16 hex digits of a hash of
+ * every kernel and header source it was compiled from (static string). */
+const char *minikv_build_id(void);
 
 #ifdef __cplusplus
 }

@@ -40,9 +40,11 @@ from .minikv_ref import (  # noqa: F401
     window_scores_ref,
     select_ref,
     index_near_ties,
+    group_min_max,
     quant_group_ref,
     quant_pack_ref,
     code_near_ties,
+    code_parity,
     pack_codes_ref,
     unpack_codes_ref,
     pack_value_codes_ref,
@@ -50,6 +52,7 @@ from .minikv_ref import (  # noqa: F401
     sz_words_ref,
     dequant_ref,
     decode_ref,
+    attn_tolerance,
     stream_split_ref,
     concat_packed_ref,
     stream_init_ref,

@@ -217,11 +217,32 @@ def index_near_ties(scores, n_heavy, n_recent, tol=1e-6):
 # values per token, compact layout.
 # ---------------------------------------------------------------------------
 
-def _quant_groups(x):
-    """Quantise groups laid along the last axis of fp32 ``x`` (see quant_group_ref)."""
+def group_min_max(x):
+    """Minimum and maximum along the last axis, with -0 ordered below +0.
+
+    Reading (the pages do not say which zero a group's minimum is): the IEEE
+    754-2019 minimum / maximum operations, which rank -0 below +0, so the
+    result does not depend on the order of the elements.  A group whose
+    smallest value is zero has minimum -0 if it holds a -0, else +0; a group
+    whose largest value is zero has maximum +0 if it holds a +0, else -0.
+    Only the sign of the stored zero point z = fp16(min) can change; codes and
+    the scale cannot (x - z and max - min are the same for either zero).
+    """
     x = np.asarray(x, dtype=np.float32)
     mn = x.min(axis=-1, keepdims=True)
     mx = x.max(axis=-1, keepdims=True)
+    zero = x == 0
+    has_neg0 = (zero & np.signbit(x)).any(axis=-1, keepdims=True)
+    has_pos0 = (zero & ~np.signbit(x)).any(axis=-1, keepdims=True)
+    mn = np.where(mn == 0, np.where(has_neg0, np.float32(-0.0), np.float32(0.0)), mn).astype(np.float32)
+    mx = np.where(mx == 0, np.where(has_pos0, np.float32(0.0), np.float32(-0.0)), mx).astype(np.float32)
+    return mn, mx
+
+
+def _quant_groups(x):
+    """Quantise groups laid along the last axis of fp32 ``x`` (see quant_group_ref)."""
+    x = np.asarray(x, dtype=np.float32)
+    mn, mx = group_min_max(x)
     s32 = (mx - mn) / np.float32(3.0)          # fp32 subtract, fp32 divide
     s16 = s32.astype(np.float16)               # round-half-even to fp16
     z16 = mn.astype(np.float16)
@@ -239,7 +260,7 @@ def quant_group_ref(x):
     """Quantise one group (1-D fp32 values) to 2-bit codes with fp16 scale / zero.
 
     Readings (pages give only "2-bit, asymmetric, per-channel K / per-token V"):
-      mn, mx = min, max of the group (exact)
+      mn, mx = min, max of the group (exact; -0 below +0, see group_min_max)
       s = fp16( fl32( fl32(mx - mn) / 3 ) )      four levels 0..3
       z = fp16( mn )                             a float offset, not an integer zero point
       u = fl32( fl32(x - z) / s )                with the *stored* fp16 s, z
@@ -353,12 +374,33 @@ def quant_pack_ref(k, v, idx=None, return_u=False):
 
 
 def code_near_ties(u, tol=1e-6):
-    """Elements whose fp32 ratio u sits within tol of a rounding boundary m + 1/2."""
+    """Elements whose fp32 ratio u sits within tol of a rounding boundary m + 1/2.
+
+    The code of an element is rint(u) clamped to 0..3, so it changes only at
+    u = 0.5, 1.5 and 2.5; an element with |u - (m + 1/2)| < tol for m in
+    {0, 1, 2} is a near-tie, whose code a differently rounded evaluation of u
+    could flip.  u is NaN for groups with s == 0 (never a near-tie); values past
+    the clamp (u near 3.5 or -0.5) are not boundaries.  Returns a bool array.
+    """
     u = np.asarray(u, dtype=np.float64)
     near = np.zeros(u.shape, dtype=bool)
     for m in (0, 1, 2):
         near |= np.abs(u - (m + 0.5)) < tol
     return near
+
+
+def code_parity(got_codes, ref_codes, u, tol=1e-6):
+    """Compare 2-bit codes with near-ties excluded and counted.
+
+    got_codes, ref_codes: unpacked codes of the same shape; u: the oracle's fp32
+    ratios.  Returns (mismatches outside near-ties, near-ties, mismatches among
+    near-ties).
+    """
+    got = np.asarray(got_codes)
+    ref = np.asarray(ref_codes)
+    near = code_near_ties(u, tol)
+    diff = got != ref
+    return int(np.count_nonzero(diff & ~near)), int(np.count_nonzero(near)), int(np.count_nonzero(diff & near))
 
 
 def dequant_ref(packed, D=None):
@@ -404,6 +446,19 @@ def decode_ref(q, packed, sm_scale=None):
             p /= p.sum()
             out[b, h] = p @ v_hat[b, g]
     return out
+
+
+def attn_tolerance(ref):
+    """Elementwise bound for a bf16 attention output against the fp64 oracle.
+
+    The target is a max-abs error of 2e-3 with bf16 outputs and fp32
+    accumulation; a bf16 output alone is off by up to half an ulp, which
+    exceeds 2e-3 once |o| >= 0.5.  Reading: pass where
+    |o - o_ref| <= max(2e-3, 1 bf16 ulp of o_ref).
+    """
+    ax = np.abs(np.asarray(ref, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
+    return np.maximum(2e-3, 2.0 ** (e - 7))
 
 
 # ---------------------------------------------------------------------------

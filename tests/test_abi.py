@@ -72,13 +72,79 @@ def test_prefill_validation(L):
 
 def test_select_validation(L):
     f = L.minikv_select_topk
-    assert f(None, 1, 1, 100, 10, 5, A, None) == _lib.ERR_NULL
-    assert f(A, 1, 1, 100, 10, 5, None, None) == _lib.ERR_NULL
-    assert f(A, 1, 1, 100, 90, 11, A, None) == _lib.ERR_SHAPE
-    assert f(A, 1, 1, 100, -1, 5, A, None) == _lib.ERR_SHAPE
-    assert f(A, 1, 1, 100, 0, 0, A, None) == _lib.ERR_SHAPE
-    assert f(A, 1, 1, 70000, 10, 10, A, None) == _lib.ERR_UNSUPPORTED
-    assert f(MIS, 1, 1, 100, 10, 5, A, None) == _lib.ERR_ALIGN
+    assert f(None, 1, 1, 100, 10, 5, A, None, 0, None) == _lib.ERR_NULL
+    assert f(A, 1, 1, 100, 10, 5, None, None, 0, None) == _lib.ERR_NULL
+    assert f(A, 1, 1, 100, 90, 11, A, None, 0, None) == _lib.ERR_SHAPE
+    assert f(A, 1, 1, 100, -1, 5, A, None, 0, None) == _lib.ERR_SHAPE
+    assert f(A, 1, 1, 100, 0, 0, A, None, 0, None) == _lib.ERR_SHAPE
+    assert f(A, 1, 1, 70000, 10, 10, A, None, 0, None) == _lib.ERR_UNSUPPORTED
+    assert f(MIS, 1, 1, 100, 10, 5, A, None, 0, None) == _lib.ERR_ALIGN
+    assert f(A, 1, 1, 100, 10, 5, A, MIS, 64, None) == _lib.ERR_ALIGN     # a workspace, if given, is aligned
+
+
+def test_select_workspace_size(L):
+    """The selection keeps each row on chip: no workspace for any supported row
+    length, so NULL / 0 is accepted (the validation above reaches the launch
+    stage with ws NULL only on a device)."""
+    for B, Hkv, T in [(1, 1, 1), (8, 32, 4096), (1, 32, 16384), (4, 8, 44000), (2, 2, 65536 + 10)]:
+        assert L.minikv_select_ws_bytes(B, Hkv, T) == 0
+    assert L.minikv_select_ws_bytes(0, 1, 1) == 0
+
+
+def test_build_id_matches_sources(L):
+    """The loaded library reports the hash of the sources it was built from,
+    and the loader has checked it against the sources in the tree."""
+    from bit_quantized_kv_quant_amd import build
+
+    bid = L.minikv_build_id().decode()
+    assert re.fullmatch(r"sha256:[0-9a-f]{16}", bid)
+    assert bid == build.source_hash()
+
+
+def test_stream_init_validation(L):
+    f = L.minikv_stream_init
+    npk, nres = ctypes.c_int(-7), ctypes.c_int(-7)
+    ok = dict(k=A, v=A, idx=A, B=2, Hkv=4, T=256, D=128, n=100, cap=128, kc=A, ks=A, vc=A, vs=A, kr=A, vr=A,
+              np_=ctypes.byref(npk), nr=ctypes.byref(nres))
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["k"], a["v"], a["idx"], a["B"], a["Hkv"], a["T"], a["D"], a["n"], a["cap"], a["kc"], a["ks"],
+                 a["vc"], a["vs"], a["kr"], a["vr"], a["np_"], a["nr"], None)
+
+    assert call(idx=None) == _lib.ERR_NULL
+    assert call(vr=None) == _lib.ERR_NULL
+    assert call(np_=None) == _lib.ERR_NULL
+    assert call(n=0) == _lib.ERR_SHAPE
+    assert call(n=257) == _lib.ERR_SHAPE           # more kept tokens than the context
+    assert call(cap=100) == _lib.ERR_SHAPE         # capacity not whole groups
+    assert call(cap=64) == _lib.ERR_SHAPE          # 96 packed tokens do not fit 64
+    assert call(n=127, cap=64) == _lib.ERR_SHAPE   # 96 packed + 31 in the window: too many
+    assert call(D=96) == _lib.ERR_UNSUPPORTED
+    assert call(kr=MIS) == _lib.ERR_ALIGN
+    assert (npk.value, nres.value) == (-7, -7)     # rejected calls leave the counts alone
+
+
+def test_stream_append_token_validation(L):
+    """Counts out of range, and a token that would fill the window with no room
+    left to pack it, are rejected before anything is enqueued."""
+    f = L.minikv_stream_append_token
+
+    def call(n_packed, n_res, cap=128, D=128, kn=A, kr=A):
+        a, b = ctypes.c_int(n_packed), ctypes.c_int(n_res)
+        st = f(kn, A, 2, 4, D, cap, ctypes.byref(a), ctypes.byref(b), A, A, A, A, kr, A, None)
+        assert (a.value, b.value) == (n_packed, n_res)
+        return st
+
+    assert call(0, 0, kn=None) == _lib.ERR_NULL
+    assert f(A, A, 2, 4, 128, 128, None, None, A, A, A, A, A, A, None) == _lib.ERR_NULL
+    assert call(16, 0) == _lib.ERR_SHAPE           # packed count not whole groups
+    assert call(160, 0) == _lib.ERR_SHAPE          # packed count past the capacity
+    assert call(0, 32) == _lib.ERR_SHAPE           # a window holds at most 31
+    assert call(0, -1) == _lib.ERR_SHAPE
+    assert call(128, 31) == _lib.ERR_SHAPE         # the 32nd token cannot be packed: full
+    assert call(96, 31, D=96) == _lib.ERR_UNSUPPORTED
+    assert call(96, 31, kr=MIS) == _lib.ERR_ALIGN
 
 
 def test_quant_pack_validation(L):

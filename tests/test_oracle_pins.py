@@ -96,8 +96,9 @@ def _cases():
 def test_quant_hand_derived(case):
     x = np.array([float.fromhex(h) for h in case["x"]], dtype=np.float32)
     codes, s, z, _ = oracle.quant_group_ref(x)
-    assert float(s) == float.fromhex(case["scale"])
-    assert float(z) == float.fromhex(case["zero"])
+    # compared as fp16 bit patterns, so the sign of a zero counts
+    assert np.float16(s).view(np.uint16) == np.float16(float.fromhex(case["scale"])).view(np.uint16)
+    assert np.float16(z).view(np.uint16) == np.float16(float.fromhex(case["zero"])).view(np.uint16)
     assert codes.tolist() == case["codes"]
     # the same case evaluated with exact rationals agrees
     ce, se, ze = quant_group_exact(x)
@@ -201,6 +202,87 @@ def test_quant_exact_groups_reconstruct():
         assert sorted(set(codes.tolist())) == [0, 3]
         xh = codes * float(s) + float(z)
         assert np.array_equal(xh, x.astype(np.float64))
+
+
+def _total_order_key(x):
+    """IEEE 754 totalOrder as an integer key of fp32 values (-0 below +0)."""
+    b = np.asarray(x, np.float32).view(np.int32).astype(np.int64)
+    return np.where(b < 0, -(b & 0x7FFFFFFF) - 1, b)
+
+
+def test_group_min_max_follow_total_order():
+    """Every group of 1..4 elements from {-0, +0, 0.5, -0.5, 2}: the oracle's
+    minimum / maximum are the totalOrder extremes (so -0 < +0), the stored
+    zero point z = fp16(min) carries that sign, and no permutation of a group
+    changes its fp16 words or codes."""
+    vals = np.array([-0.0, 0.0, 0.5, -0.5, 2.0], np.float32)
+    seen = 0
+    for size in range(1, 5):
+        for combo in itertools.product(range(len(vals)), repeat=size):
+            x = vals[list(combo)]
+            key = _total_order_key(x)
+            want_mn, want_mx = x[np.argmin(key)], x[np.argmax(key)]
+            mn, mx = oracle.group_min_max(x[None])
+            assert mn.view(np.uint32)[0, 0] == np.float32(want_mn).view(np.uint32)
+            assert mx.view(np.uint32)[0, 0] == np.float32(want_mx).view(np.uint32)
+            codes, s, z, _ = oracle.quant_group_ref(x)
+            assert np.float16(z).view(np.uint16) == np.float16(want_mn).view(np.uint16)
+            for perm in itertools.permutations(range(size)):
+                c2, s2, z2, _ = oracle.quant_group_ref(x[list(perm)])
+                assert np.float16(s2).view(np.uint16) == np.float16(s).view(np.uint16)
+                assert np.float16(z2).view(np.uint16) == np.float16(z).view(np.uint16)
+                assert c2.tolist() == codes[list(perm)].tolist()
+            seen += 1
+    assert seen == 5 + 25 + 125 + 625
+
+
+def test_signed_zero_groups_in_the_packed_cache():
+    """A key channel of alternating +0 / -0 and a value group starting with +0
+    then -0 store z = -0; all-+0 groups store +0 (fp16 bits)."""
+    k = np.zeros((1, 1, 32, 32), np.float32)
+    v = np.zeros((1, 1, 32, 32), np.float32)
+    k[0, 0, 1::2, 0] = -0.0       # channel 0: +0, -0, +0, ...
+    k[0, 0, 0::2, 1] = -0.0       # channel 1: -0, +0, ...
+    v[0, 0, 0, 1] = -0.0          # token 0: +0, -0, +0, ...
+    v[0, 0, 1, 0] = -0.0          # token 1: -0, +0, ...
+    p = oracle.quant_pack_ref(k, v)
+    kz = p["k_zero"].view(np.uint16)[0, 0, 0]
+    vz = p["v_zero"].view(np.uint16)[0, 0, :, 0]
+    assert kz[0] == 0x8000 and kz[1] == 0x8000 and not kz[2:].any()
+    assert vz[0] == 0x8000 and vz[1] == 0x8000 and not vz[2:].any()
+    assert not p["k_scale"].view(np.uint16).any() and not p["v_scale"].view(np.uint16).any()
+
+
+def test_code_near_ties_hand_cases():
+    """Near-ties are |u - (m + 1/2)| < 1e-6 for m = 0, 1, 2 on the fp32 ratio u.
+    fp32 spacing is 2^-24 below 0.5 ... 2^-22 near 2.5, so the cases step by ulps."""
+    f = np.float32
+    cases = [
+        (f(0.5), True), (f(1.5), True), (f(2.5), True),
+        (f(0.5) + f(2 ** -20), True),            # 9.5e-7 above 0.5
+        (f(0.5) + f(2 ** -19), False),           # 1.9e-6 above
+        (f(1.5) - f(2 ** -20), True),            # 9.5e-7 below 1.5
+        (f(1.5) - f(2 ** -19), False),
+        (f(2.5) + f(4 * 2 ** -22), True),        # 4 ulps (9.5e-7) above 2.5
+        (f(2.5) + f(5 * 2 ** -22), False),       # 5 ulps (1.19e-6)
+        (f(3.5), False), (f(-0.5), False),       # past the clamp: not a boundary
+        (f(1.0), False), (f(0.0), False), (f(3.0), False),
+        (f(np.nan), False),                      # a group with s == 0
+    ]
+    u = np.array([c[0] for c in cases], np.float32)
+    assert oracle.code_near_ties(u).tolist() == [c[1] for c in cases]
+    # a group whose second element lands exactly on u = 1.5: x = 0, 1.5, 3 (s = 1, z = 0)
+    p = oracle.quant_pack_ref(np.array([0.0, 1.5, 3.0] + [0.0] * 29, np.float32).reshape(1, 1, 32, 1)
+                              .repeat(32, axis=3), np.zeros((1, 1, 32, 32), np.float32), return_u=True)
+    near = oracle.code_near_ties(p["k_u"])
+    assert near[0, 0, 1].all() and near.sum() == 32
+    assert not oracle.code_near_ties(p["v_u"]).any()
+    # parity counting: a flipped code on a near-tie is counted apart from other mismatches
+    ref = np.array([0, 2, 3, 1])
+    uu = np.array([0.1, 1.5, 2.9, 0.9], np.float32)
+    assert oracle.code_parity(np.array([0, 1, 3, 1]), ref, uu) == (0, 1, 1)
+    assert oracle.code_parity(np.array([1, 2, 3, 1]), ref, uu) == (1, 1, 0)
+    assert oracle.code_parity(ref, ref, uu) == (0, 1, 0)
 
 
 # ---------------------------------------------------------------------------

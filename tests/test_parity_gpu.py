@@ -12,7 +12,7 @@ import torch
 import oracle
 import synth
 import bit_quantized_kv_quant_amd as mk
-from gpu_util import (assert_attn_close, assert_packed_equal, packed_to_np, require_gpu, to_np)
+from gpu_util import (assert_attn_close, check_selection, pack_parity, packed_to_np, require_gpu, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,15 +30,15 @@ def say(*a):
 # quantise + pack
 # ---------------------------------------------------------------------------
 
-def _pack_and_compare(k, v, idx, dev):
+def _pack_and_compare(k, v, idx, dev, what="pack"):
     kd = torch.from_numpy(k).to(dev) if isinstance(k, np.ndarray) else k
     vd = torch.from_numpy(v).to(dev) if isinstance(v, np.ndarray) else v
     idd = None if idx is None else torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to(dev)
     cache = mk.quant_pack(kd, vd, idd)
     torch.cuda.synchronize()
     got = packed_to_np(cache)
-    ref = oracle.quant_pack_ref(to_np(kd), to_np(vd), idx)
-    assert_packed_equal(got, ref)
+    ref = oracle.quant_pack_ref(to_np(kd), to_np(vd), idx, return_u=True)
+    pack_parity(got, ref, what)
     return cache
 
 
@@ -77,6 +77,44 @@ def test_quant_pack_special_groups(dev):
     v[0, 0, :, 32:] = 7.5                                      # constant value group
     v[0, 1] = np.random.default_rng(4).standard_normal((T, D)).astype(np.float32) * 100
     _pack_and_compare(k, v, None, dev)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quant_pack_signed_zero_groups(dev, dtype):
+    """Groups whose minimum is zero with -0 and +0 mixed in both orders, all -0,
+    all +0, and zero maxima of non-positive groups: the stored zero point takes
+    -0 below +0 (its fp16 sign bit), bit for bit with the oracle; full and
+    partial key groups."""
+    say("quant_pack signed zeros", dtype)
+    T, D = 40, 64
+    k = np.zeros((1, 2, T, D), np.float32)
+    v = np.zeros((1, 2, T, D), np.float32)
+    k[0, 0, 1::2, 0] = -0.0                      # +0, -0, +0, ...
+    k[0, 0, 0::2, 1] = -0.0                      # -0, +0, -0, ...
+    k[0, 0, :, 2] = -0.0                         # all -0
+    k[0, 0, ::3, 4] = 1.5                        # +0 minimum with a positive maximum
+    k[0, 0, 1::3, 5] = -0.0
+    k[0, 0, ::3, 5] = 1.5                        # -0 minimum with a positive maximum
+    k[0, 0, ::2, 6] = -1.5
+    k[0, 0, 1::4, 6] = -0.0                      # zero maximum of a non-positive group
+    k[0, 0, 39, 7] = -0.0                        # a -0 only in the partial last group
+    rng = np.random.default_rng(17)
+    k[0, 1] = np.where(rng.random((T, D)) < 0.5, np.float32(-0.0), np.float32(0.0))
+    k[0, 1, :, ::3] += rng.integers(0, 4, (T, (D + 2) // 3)).astype(np.float32) * 0.5
+    v[0, 0, 0, 1::2] = -0.0                      # token 0: +0, -0, ... in both value groups
+    v[0, 0, 1, 0::2] = -0.0                      # token 1: -0, +0, ...
+    v[0, 0, 2, :] = -0.0
+    v[0, 0, 3, ::5] = 0.75
+    v[0, 0, 3, 1::5] = -0.0
+    v[0, 1] = np.where(rng.random((T, D)) < 0.5, np.float32(-0.0), np.float32(0.0))
+    v[0, 1, ::2] -= rng.integers(0, 3, ((T + 1) // 2, D)).astype(np.float32) * 0.25
+    kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    if dtype == "bf16":
+        kd, vd = kd.to(torch.bfloat16), vd.to(torch.bfloat16)
+        assert (kd.view(torch.int16) == -32768).any()   # the -0 survives the cast
+    cache = _pack_and_compare(kd, vd, None, dev, f"signed zeros {dtype}")
+    kz = (cache.k_sz.cpu().numpy().view(np.uint32) >> 16)[0, 0, 0]
+    assert kz[0] == 0x8000 and kz[1] == 0x8000 and kz[2] == 0x8000 and kz[4] == 0
 
 
 def test_quant_pack_llama7b_shape(dev):
@@ -251,10 +289,15 @@ def test_prefill_lse_only_matches(dev):
     assert torch.equal(lse1, lse2) and torch.equal(sc1, sc2)
 
 
-def test_prefill_16k_sampled(dev):
-    """32 heads x 16384 causal tokens: o / lse on sampled rows, every window score."""
+def test_prefill_16k_chain(dev):
+    """The 16k prefill-and-compress workload end to end at its own sizes (1 x 32
+    heads x 16384 causal tokens, W = 32, 15 % budget): o / lse on sampled rows,
+    every window score; then selection of 1966 heavy + 491 recent tokens on those
+    scores (exact on the GPU's scores, near-ties only against fp64), the 2-bit
+    pack of the 2457 kept tokens x 32 heads (codes with near-ties counted, every
+    byte), and one decode query over the packed cache."""
     wl = synth.WORKLOADS["prefill_16k"]
-    say("prefill 16k H32 D128 sampled rows")
+    say("prefill 16k H32 D128: prefill + scores")
     q, k, v, _ = synth.make_qkv(wl, dev)
     o, lse, sc = mk.prefill_attn_scores(q, k, v, wl.window)
     torch.cuda.synchronize()
@@ -264,8 +307,24 @@ def test_prefill_16k_sampled(dev):
     assert_attn_close(to_np(o)[:, :, rows], o_ref, "prefill 16k o")
     assert np.abs(to_np(lse)[:, :, rows] - lse_ref).max() < 1e-4
     sc_ref = oracle.window_scores_ref(qb, kb, wl.window)
-    rel = np.abs(to_np(sc) - sc_ref) / np.maximum(sc_ref, 1e-6)
+    sc_np = to_np(sc)
+    rel = np.abs(sc_np - sc_ref) / np.maximum(sc_ref, 1e-6)
     assert rel.max() < 1e-4
+    del o, q, o_ref
+    say("prefill 16k: select 1966 + 491, pack 2457 x 32 heads, decode")
+    n_keep = oracle.keep_count(wl.T, wl.budget_pct)
+    nh, nr = oracle.split_heavy_recent(n_keep)
+    assert (n_keep, nh, nr) == (2457, 1966, 491)
+    idx = mk.select_topk(sc, nh, nr)
+    cache = mk.quant_pack(k, v, idx)
+    qdec = synth.make_decode_q(wl, dev)
+    out = mk.decode_attn(qdec, cache)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    check_selection(idx_np, sc_np, sc_ref, nh, nr, "16k select")
+    got = packed_to_np(cache)
+    pack_parity(got, oracle.quant_pack_ref(kb, vb, idx_np, return_u=True), "16k pack")
+    assert_attn_close(to_np(out), oracle.decode_ref(to_np(qdec), got), "16k decode")
 
 
 # ---------------------------------------------------------------------------
@@ -284,25 +343,16 @@ def _chain(dev, q, k, v, qdec, W, n_heavy, n_recent, k_pack=None, v_pack=None):
     qdd = torch.from_numpy(qdec).to(dev).to(torch.bfloat16) if isinstance(qdec, np.ndarray) else qdec
     out = mk.decode_attn(qdd, cache)
     torch.cuda.synchronize()
-    # selection: exact against the oracle run on the GPU's fp32 scores ...
+    # selection: exact against the oracle run on the GPU's fp32 scores, and
+    # against the oracle's own fp64 scores different only on near-ties
     sc_np = to_np(sc)
     idx_np = idx.cpu().numpy()
-    assert np.array_equal(idx_np, oracle.select_ref(sc_np, n_heavy, n_recent))
-    # ... and, against the oracle's own fp64 scores, different only on near-ties
     sc_ref = oracle.window_scores_ref(to_np(qd), to_np(kd), W)
-    idx_ref = oracle.select_ref(sc_ref, n_heavy, n_recent)
-    near = oracle.index_near_ties(sc_ref, n_heavy, n_recent)
-    flat_g = idx_np.reshape(-1, idx_np.shape[-1])
-    flat_r = idx_ref.reshape(-1, idx_ref.shape[-1])
-    n_diff = 0
-    for row in range(flat_g.shape[0]):
-        sym = set(flat_g[row].tolist()) ^ set(flat_r[row].tolist())
-        assert sym <= set(near[row].tolist()), f"row {row}: {sorted(sym)[:8]} not near-ties"
-        n_diff += len(sym)
-    # packing of the GPU's selection: bit-exact
-    ref_pack = oracle.quant_pack_ref(to_np(kp), to_np(vp), idx_np)
+    n_diff, _ = check_selection(idx_np, sc_np, sc_ref, n_heavy, n_recent, "chain select")
+    # packing of the GPU's selection: codes with near-ties counted, then bit-exact
+    ref_pack = oracle.quant_pack_ref(to_np(kp), to_np(vp), idx_np, return_u=True)
     got_pack = packed_to_np(cache)
-    assert_packed_equal(got_pack, ref_pack)
+    pack_parity(got_pack, ref_pack, "chain pack")
     # decode on the packed cache
     ref_out = oracle.decode_ref(to_np(qdd), got_pack)
     err = assert_attn_close(to_np(out), ref_out, "chain decode")
@@ -422,7 +472,7 @@ def test_gqa_44k_chain_sampled(dev):
     assert np.array_equal(idx_np, oracle.select_ref(sc_np, nh, nr))
     del o, q
     got = packed_to_np(cache)
-    assert_packed_equal(got, oracle.quant_pack_ref(to_np(k), to_np(v), idx_np))
+    pack_parity(got, oracle.quant_pack_ref(to_np(k), to_np(v), idx_np, return_u=True), "gqa 44k pack")
     assert_attn_close(to_np(out), oracle.decode_ref(to_np(qdec), got), "gqa decode")
 
 

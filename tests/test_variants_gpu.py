@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import bit_quantized_kv_quant_amd as mk
-from gpu_util import assert_attn_close, assert_packed_equal, packed_to_np, require_gpu, to_np
+from gpu_util import assert_attn_close, check_selection, pack_parity, packed_to_np, require_gpu, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,7 @@ def test_policy_matches_oracle(dev, policy, B, Hq, Hkv, T, n_layers, layer):
     assert_attn_close(to_np(o)[:, :, rows], o_ref, f"{policy} o")
     if idx is None:
         assert n_keep == T
-        ref_pack = oracle.quant_pack_ref(kn, vn, None)
+        ref_pack = oracle.quant_pack_ref(kn, vn, None, return_u=True)
     else:
         _, lse, sc = mk.prefill_attn_scores(q, k, v, W, with_o=False)
         sc_np = to_np(sc)
@@ -68,15 +68,9 @@ def test_policy_matches_oracle(dev, policy, B, Hq, Hkv, T, n_layers, layer):
         assert rel.max() < 1e-4, f"scores rel err {rel.max()}"
         idx_np = idx.cpu().numpy()
         assert idx_np.shape == (B, Hkv, n_keep)
-        assert np.array_equal(idx_np, oracle.select_ref(sc_np, nh, nr))
-        idx_ref = oracle.select_ref(sc_ref, nh, nr)
-        near = oracle.index_near_ties(sc_ref, nh, nr)
-        fg, fr = idx_np.reshape(-1, n_keep), idx_ref.reshape(-1, n_keep)
-        for row in range(fg.shape[0]):
-            sym = set(fg[row].tolist()) ^ set(fr[row].tolist())
-            assert sym <= set(near[row].tolist()), f"row {row}: {sorted(sym)[:8]} not near-ties"
-        ref_pack = oracle.quant_pack_ref(kn, vn, idx_np)
+        check_selection(idx_np, sc_np, sc_ref, nh, nr, f"{policy} select")
+        ref_pack = oracle.quant_pack_ref(kn, vn, idx_np, return_u=True)
     got = packed_to_np(cache)
-    assert_packed_equal(got, ref_pack)
+    pack_parity(got, ref_pack, f"{policy} pack")
     assert cache.nbytes() == oracle.packed_bytes_ref(B, Hkv, n_keep, D)
     assert_attn_close(to_np(out), oracle.decode_ref(to_np(qd), got), f"{policy} decode")
