@@ -22,6 +22,7 @@ ERR_LAUNCH = -6
 F32 = 0
 BF16 = 1
 GROUP = 32
+DECODE_SCRATCH_BYTES = 32 << 20  # MINIKV_DECODE_SCRATCH_BYTES
 
 # Every function the header declares, with its ctypes signature.
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -53,6 +54,7 @@ SIGNATURES = {
     "minikv_select_ws_bytes": (_sz, [_i, _i, _i]),
     "minikv_quant_pack": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(PackedT), _vp]),
     "minikv_decode_attn": (_i, [_vp, ctypes.POINTER(PackedT), _i, _f, _vp, _vp, _sz, _vp]),
+    "minikv_decode_attn_noalloc": (_i, [_vp, ctypes.POINTER(PackedT), _i, _f, _vp, _vp]),
     "minikv_stream_pack": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "minikv_stream_append": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "minikv_stream_decode": (_i, [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _f, _vp, _vp,

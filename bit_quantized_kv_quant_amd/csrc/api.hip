@@ -188,6 +188,32 @@ int minikv_decode_attn(const void* q, const minikv_packed_t* cache, int Hq, floa
                                            as_stream(stream)));
 }
 
+int minikv_decode_attn_noalloc(const void* q, const minikv_packed_t* cache, int Hq, float sm_scale, void* out,
+                               void* stream) {
+    static_assert(minikv::kDecodeScratchBytes == MINIKV_DECODE_SCRATCH_BYTES, "scratch size");
+    if (!q || !cache || !out || !cache->k_codes || !cache->k_sz || !cache->v_codes || !cache->v_sz)
+        return MINIKV_ERR_NULL;
+    const int B = cache->B, Hkv = cache->Hkv, n = cache->n_keep, D = cache->D;
+    if (B < 1 || Hkv < 1 || n < 1 || Hq < 1 || Hq % Hkv) return MINIKV_ERR_SHAPE;
+    if (!supported_d(D) || cache->group != MINIKV_GROUP) return MINIKV_ERR_UNSUPPORTED;
+    const int R = Hq / Hkv;
+    if (R != 1 && R != 2 && R != 4) return MINIKV_ERR_UNSUPPORTED;
+    if (misaligned(q) || misaligned(out) || misaligned(cache->k_codes) || misaligned(cache->k_sz) ||
+        misaligned(cache->v_codes) || misaligned(cache->v_sz))
+        return MINIKV_ERR_ALIGN;
+    const minikv::DecodePlan plan = minikv::decode_plan(B, Hq, Hkv, n, D);
+    // one token range per KV head writes the output directly: no scratch used
+    void* ws = nullptr;
+    if (plan.splits > 1) {
+        if (minikv::decode_ws_bytes(B, Hq, D, plan) > minikv::kDecodeScratchBytes) return MINIKV_ERR_WORKSPACE;
+        ws = minikv::decode_scratch();
+        if (!ws) return MINIKV_ERR_LAUNCH;
+    }
+    return status_of(minikv::launch_decode(q, cache->k_codes, cache->k_sz, cache->v_codes, cache->v_sz, B, Hq,
+                                           Hkv, n, D, resolve_scale(sm_scale, D), out, ws, plan,
+                                           as_stream(stream)));
+}
+
 int minikv_stream_pack(const void* k, const void* v, int in_dtype, const int32_t* idx, int idx_stride, int B,
                        int Hkv, int T, int D, int n, int cap, int tok0, uint8_t* k_codes, uint32_t* k_sz,
                        uint8_t* v_codes, uint32_t* v_sz, void* stream) {

@@ -790,7 +790,28 @@ hipError_t launch_d(const void* q, const DecodeSrc& src, int B, int Hq, int Hkv,
     }
 }
 
+// Split partials of the allocation-free decode entry point: a library-owned
+// device array of kDecodeScratchBytes per GPU, held until the process ends.
+// Host code never passes this name to a kernel (on the host it is only a
+// stand-in symbol); decode_scratch() resolves its device address once per
+// device and every launch takes that address.
+__device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
 }  // namespace
+
+void* decode_scratch() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void*> addr[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // with the device current: this device's copy of the array
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev].store(p, std::memory_order_release);  // concurrent first calls store the same address
+    }
+    return p;
+}
 
 DecodePlan decode_plan(int B, int Hq, int Hkv, int n_keep, int D) {
     (void)Hq;

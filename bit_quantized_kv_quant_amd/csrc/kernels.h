@@ -46,6 +46,12 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int n_keep, int D);
 size_t decode_ws_bytes(int B, int Hq, int D, const DecodePlan& plan);
 size_t stream_decode_ws_bytes(int B, int Hq, int D, int n_packed, int n_res, const DecodePlan& plan);
 
+// Bytes of the allocation-free decode's scratch array (one per device).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+// Device address of the current device's scratch array (resolved once per
+// device), or nullptr if the runtime cannot resolve it.
+void* decode_scratch();
+
 hipError_t launch_decode(const void* q, const uint8_t* k_codes, const uint32_t* k_sz,
                          const uint8_t* v_codes, const uint32_t* v_sz, int B, int Hq, int Hkv,
                          int n_keep, int D, float sm_scale, void* out, void* ws,

@@ -177,6 +177,27 @@ int minikv_quant_pack(const void *k, const void *v, int in_dtype, const int32_t 
 int minikv_decode_attn(const void *q, const minikv_packed_t *cache, int Hq, float sm_scale,
                        void *out, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * For callers that cannot allocate device memory - code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc:
+ * minikv_decode_attn without a workspace argument.  The split partial results
+ * go to a library-owned device array of MINIKV_DECODE_SCRATCH_BYTES on each
+ * GPU the library runs on, held until the process ends; no hipMalloc,
+ * hipFree or allocating routine is called.  Same arguments (minus ws),
+ * results and errors as minikv_decode_attn, plus WORKSPACE when the split
+ * plan's partials (minikv_decode_ws_bytes) exceed the array - no plan of a
+ * supported shape does: at most about 8192 (head, range) parts of (D + 2)
+ * floats per query head, 17 MB at four query heads per KV head, D = 128; a
+ * plan with one range per KV head uses no scratch - and LAUNCH when the
+ * array's device address cannot be resolved.  Every call on a GPU
+ * shares that GPU's array, which keeps the last call's partials (nothing in
+ * it needs to start at zero): calls that overlap on one GPU (other streams,
+ * other threads) race.
+ */
+#define MINIKV_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+int minikv_decode_attn_noalloc(const void *q, const minikv_packed_t *cache, int Hq, float sm_scale,
+                               void *out, void *stream);
+
 /* ---- streaming decode: generated tokens join the cache ----
  *
  * Keys are quantised per channel over 32-token groups (method details), so a

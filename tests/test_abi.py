@@ -337,3 +337,39 @@ def test_single_pass_rule(L):
         for W in (1, 16, 32):
             assert f(64, T, 4, 4, W) == int(W <= min(32, last, T))
     assert f(0, 10, 1, 1, 1) == 0 and f(1, 10, 3, 2, 1) == 0 and f(1, 10, 1, 1, 11) == 0
+
+
+def test_decode_noalloc_validation(L):
+    """Argument checks of the allocation-free decode (no HIP call is reached)."""
+    f = L.minikv_decode_attn_noalloc
+    byref = ctypes.byref
+    p = packed(B=2, Hkv=4, n=100, D=128)
+    assert f(None, byref(p), 8, 0.0, A, None) == _lib.ERR_NULL
+    assert f(A, None, 8, 0.0, A, None) == _lib.ERR_NULL
+    assert f(A, byref(p), 8, 0.0, None, None) == _lib.ERR_NULL
+    assert f(A, byref(packed(ptr=None)), 8, 0.0, A, None) == _lib.ERR_NULL
+    assert f(A, byref(p), 6, 0.0, A, None) == _lib.ERR_SHAPE
+    assert f(A, byref(p), 32, 0.0, A, None) == _lib.ERR_UNSUPPORTED
+    assert f(A, byref(packed(B=2, Hkv=4, n=100, D=96)), 8, 0.0, A, None) == _lib.ERR_UNSUPPORTED
+    assert f(A, byref(packed(group=16)), 1, 0.0, A, None) == _lib.ERR_UNSUPPORTED
+    assert f(MIS, byref(p), 8, 0.0, A, None) == _lib.ERR_ALIGN
+    assert f(A, byref(p), 8, 0.0, MIS, None) == _lib.ERR_ALIGN
+
+
+def test_every_decode_split_plan_fits_the_scratch_array(L):
+    """The split partials of any supported decode shape fit the allocation-free
+    entry point's array: (sequence, KV head) units x ranges stay below about
+    8192 whenever a head is split (one range per head needs no scratch)."""
+    worst = 0
+    for units in list(range(1, 300)) + list(range(300, 4200, 7)) + [4095, 4096, 5000, 20000]:
+        for n in (1, 129, 614, 6600, 65536, 1 << 20):
+            for R in (1, 2, 4):
+                for D in (64, 128):
+                    ws = L.minikv_decode_ws_bytes(units, R, 1, n, D)
+                    splits = ws // (units * R * (D + 2) * 4)
+                    assert splits * units * R * (D + 2) * 4 == ws and splits >= 1
+                    if splits > 1:
+                        assert units * splits < 8192
+                        worst = max(worst, ws)
+    assert worst <= _lib.DECODE_SCRATCH_BYTES
+    print("largest split workspace:", worst)
