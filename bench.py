@@ -61,6 +61,8 @@ def parse():
                     help="batch of the headline 40-layer pyramid decode (1133 fills about 250 GB)")
     ap.add_argument("--headline-only", action="store_true",
                     help="run the headline decode only (e.g. under a counter profiler)")
+    ap.add_argument("--only", choices=["prefill_16k", "chain"], default=None,
+                    help="run one extra alone and print it (no headline; e.g. under a counter profiler)")
     ap.add_argument("--chain-warmup", type=int, default=25,
                     help="warm-up steps of the chain extra (a fresh process runs its first chain steps slow)")
     ap.add_argument("--pyramid-sweep", default="",
@@ -744,7 +746,14 @@ def main():
     import synth
 
     print(f"# libminikv build {mk.build_id()} ({mk.lib_path()})", file=sys.stderr, flush=True)
-    dev = torch.device("cuda:0")
+    if args.only == "prefill_16k":
+        print(json.dumps({"prefill_16k": prefill_layer(torch, mk, synth, synth.WORKLOADS["prefill_16k"],
+                                                       reps=args.steps)}), flush=True)
+        return
+    if args.only == "chain":
+        ch, roof, dec = chain(torch, mk, synth, args)
+        print(json.dumps({"chain": ch, "prefill_roofline": roof, "decode": dec}), flush=True)
+        return
 
     # ---- headline: 40-layer pyramid decode at the ~250 GB batch ----
     head, sample = pyramid_headline(torch, mk, synth, args.pyramid_batch, args.steps, args.warmup,
