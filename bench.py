@@ -86,7 +86,7 @@ def decode_layers(torch, mk, synth, wl, B, budgets, reps=3, chunk=64, n_queries=
     qs = [synth.make_decode_q(wl, dev, B=B, step=i) for i in range(max(1, n_queries))]
     q = qs[0]
     out = torch.empty_like(q)
-    ws = torch.empty(max(16, max(mk.decode_ws_bytes(B, wl.Hq, wl.Hkv, c.n_keep, wl.D) for c in caches)),
+    ws = torch.zeros(max(16, max(mk.decode_ws_bytes(B, wl.Hq, wl.Hkv, c.n_keep, wl.D) for c in caches)),
                      dtype=torch.uint8, device=dev)
     for c in caches:  # warm-up pass
         mk.decode_attn(q, c, out=out, ws=ws)
@@ -181,7 +181,7 @@ def pyramid_headline(torch, mk, synth, B, steps, warmup, sample_seqs=0):
     n_q = 4  # distinct seeded query sets, cycled step by step
     qs = [synth.make_decode_q(pw, dev, B=B, step=i) for i in range(n_q)]
     out = torch.empty_like(qs[0])
-    ws = torch.empty(max(16, max(mk.decode_ws_bytes(B, pw.Hq, pw.Hkv, c.n_keep, pw.D) for c in caches)),
+    ws = torch.zeros(max(16, max(mk.decode_ws_bytes(B, pw.Hq, pw.Hkv, c.n_keep, pw.D) for c in caches)),
                      dtype=torch.uint8, device=dev)
     cache_bytes = [c.nbytes() for c in caches]
     print(f"# pyramid cache: batch {B}, {sum(cache_bytes) / 1e9:.1f} GB packed, built in {build_s:.1f} s",
@@ -312,8 +312,8 @@ def decode_stream(torch, mk, synth, wl, steps):
     vn = [torch.randn((B, wl.Hkv, wl.D), generator=g, device=dev).to(torch.bfloat16) for _ in range(pool)]
     qs = [synth.make_decode_q(wl, dev, step=i, B=B) for i in range(pool)]
     out = torch.empty_like(qs[0])
-    ws = torch.empty(max(16, max(mk.decode_ws_bytes(B, wl.Hq, wl.Hkv, cap, wl.D), 1) * 2), dtype=torch.uint8,
-                     device=dev)
+    # the largest streaming workspace: the whole capacity packed and a full window
+    ws = torch.zeros(max(16, caches[0].step_ws_bytes(wl.Hq)), dtype=torch.uint8, device=dev)
     res0 = caches[0].n_res
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -338,7 +338,7 @@ def decode_stream(torch, mk, synth, wl, steps):
         c.init(k, v, idx).to_device_counts()
         del k, v, idx
     k_in, v_in, q_in = kn[0].clone(), vn[0].clone(), qs[0].clone()
-    ws_g = torch.empty(max(16, caches[0].step_ws_bytes(wl.Hq)), dtype=torch.uint8, device=dev)
+    ws_g = torch.zeros(max(16, caches[0].step_ws_bytes(wl.Hq)), dtype=torch.uint8, device=dev)
     scratch = mk.StreamCache.alloc(B, wl.Hkv, cap, wl.D, dev)
     scratch.n_packed, scratch.n_res = 0, 0
     scratch.to_device_counts()
@@ -592,7 +592,7 @@ def chain(torch, mk, synth, args):
     idx = torch.empty((B, Hkv, n_keep), dtype=torch.int32, device=dev)
     cache = mk.PackedCache.alloc(B, Hkv, n_keep, D, dev)
     out = torch.empty_like(qdec)
-    ws = torch.empty(mk.decode_ws_bytes(B, Hq, Hkv, n_keep, D), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(mk.decode_ws_bytes(B, Hq, Hkv, n_keep, D), dtype=torch.uint8, device=dev)
 
     # single pass: the window scores come out of the pass-1 kernel (one launch)
     fused = mk.prefill_fuses_scores(B, T, Hq, Hkv, W)

@@ -23,6 +23,7 @@ F32 = 0
 BF16 = 1
 GROUP = 32
 DECODE_SCRATCH_BYTES = 32 << 20  # MINIKV_DECODE_SCRATCH_BYTES
+DECODE_TICKET_BYTES = 16384      # MINIKV_DECODE_TICKET_BYTES
 
 # Every function the header declares, with its ctypes signature.
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t

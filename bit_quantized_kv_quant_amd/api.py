@@ -186,7 +186,7 @@ def decode_attn(q, cache, sm_scale=None, out=None, ws=None):
     _need(out, torch.bfloat16, (B, Hq, D), "out")
     need = decode_ws_bytes(B, Hq, cache.Hkv, cache.n_keep, D)
     if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
     s = cache.struct()
     st = _lib.lib().minikv_decode_attn(_ptr(q), ctypes.byref(s), Hq, float(sm_scale or 0.0), _ptr(out),
                                        _ptr(ws), ws.numel() * ws.element_size(), _stream())
@@ -314,7 +314,7 @@ class StreamCache:
             out = torch.empty_like(q)
         _need(out, torch.bfloat16, (self.B, Hq, self.D), "out")
         if ws is None:
-            ws = torch.empty(max(self.step_ws_bytes(Hq), 16), dtype=torch.uint8, device=q.device)
+            ws = torch.zeros(max(self.step_ws_bytes(Hq), 16), dtype=torch.uint8, device=q.device)
         st = _lib.lib().minikv_stream_step_decode(_ptr(q), self.B, Hq, self.Hkv, self.D, self.cap, _ptr(self.counts),
                                                   _ptr(self.k_codes), _ptr(self.k_sz), _ptr(self.v_codes),
                                                   _ptr(self.v_sz), _ptr(self.k_res), _ptr(self.v_res),
@@ -332,7 +332,7 @@ class StreamCache:
         _need(out, torch.bfloat16, (self.B, Hq, self.D), "out")
         need = self.ws_bytes(Hq)
         if ws is None:
-            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+            ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
         st = _lib.lib().minikv_stream_decode(_ptr(q), self.B, Hq, self.Hkv, self.D, self.cap, self.n_packed,
                                              _ptr(self.k_codes), _ptr(self.k_sz), _ptr(self.v_codes),
                                              _ptr(self.v_sz), _ptr(self.k_res), _ptr(self.v_res), self.n_res,

@@ -191,6 +191,7 @@ int minikv_decode_attn(const void* q, const minikv_packed_t* cache, int Hq, floa
 int minikv_decode_attn_noalloc(const void* q, const minikv_packed_t* cache, int Hq, float sm_scale, void* out,
                                void* stream) {
     static_assert(minikv::kDecodeScratchBytes == MINIKV_DECODE_SCRATCH_BYTES, "scratch size");
+    static_assert(minikv::kTicketBytes == MINIKV_DECODE_TICKET_BYTES, "ticket area");
     if (!q || !cache || !out || !cache->k_codes || !cache->k_sz || !cache->v_codes || !cache->v_sz)
         return MINIKV_ERR_NULL;
     const int B = cache->B, Hkv = cache->Hkv, n = cache->n_keep, D = cache->D;

@@ -188,23 +188,133 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Ticket-mode epilogue of a workgroup (all 256 threads): s_tp holds the four
+// waves' parts of (sequence, KV head) `unit`, each (head r) a row of D sums
+// 2^(l - m) v, then m and the sum of 2^(l - m) (log2 units).  They are merged
+// against their common maximum; with one workgroup per head (nwg == 1) the
+// result is the output, otherwise it is part `wg` of the head in the
+// workspace (ws_acc [unit][nwg][R][D], ws_ml [unit][nwg][R][2]) and the
+// workgroup that takes the head's last ticket merges the nwg parts the same
+// way, writes the output and resets the ticket to zero.  Empty parts (m = -inf,
+// sum 0) get weight 0; the reference maximum is finite whenever one part is not
+// empty.
+//
+// The workgroups of a head may sit on different XCDs, whose L2 caches are not
+// coherent with each other for ordinary accesses.  The parts are therefore
+// written and read with agent-scope atomic stores and loads (device-coherent
+// accesses that bypass the non-coherent caches) rather than behind full L2
+// write-back / invalidate fences: every wave waits for its part stores to
+// complete before the workgroup takes its ticket, and the last workgroup
+// reads the parts only after its ticket has come back.
+template <int D, int R>
+__device__ __forceinline__ void ticket_merge(float (*s_tp)[R][D + 2], int* s_last, int unit, int wg, int nwg,
+                                             float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+                                             __bf16* __restrict__ out, int32_t* __restrict__ tickets) {
+    auto st_dev = [](float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    auto ld_dev = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    __syncthreads();  // the four parts are in LDS
+    for (int i = threadIdx.x; i < R * D; i += 256) {
+        const int r = i / D, c = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_tp[w][r][D]);
+        const float Ms = M == -INFINITY ? 0.0f : M;
+        float L = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float f = exp2f(s_tp[w][r][D] - Ms);
+            L = fmaf(s_tp[w][r][D + 1], f, L);
+            O = fmaf(s_tp[w][r][c], f, O);
+        }
+        const size_t row = (size_t)unit * R + r;
+        if (nwg == 1) {
+            out[row * D + c] = (__bf16)(O / L);
+        } else {
+            const size_t part = ((size_t)unit * nwg + wg) * R + r;
+            st_dev(&ws_acc[part * D + c], O);
+            if (c == 0) {
+                st_dev(&ws_ml[part * 2 + 0], M);
+                st_dev(&ws_ml[part * 2 + 1], L);
+            }
+        }
+    }
+    if (nwg == 1) return;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part stores have completed at device scope ...
+    __syncthreads();                // ... for every wave, before the ticket is taken
+    if (threadIdx.x == 0) *s_last = atomicAdd(&tickets[unit], 1) == nwg - 1;
+    __syncthreads();
+    if (!*s_last) return;
+    // every part's (m, sum) in one round of loads, into LDS (nwg * R <= 252
+    // pairs; the LDS parts above are no longer needed), then the weights
+    float* s_ml = &s_tp[0][0][0];
+    const size_t base = (size_t)unit * nwg * R;
+    for (int i = threadIdx.x; i < nwg * R; i += 256) {
+        const float m = ld_dev(&ws_ml[(base + i) * 2]), l = ld_dev(&ws_ml[(base + i) * 2 + 1]);
+        s_ml[2 * i] = m;
+        s_ml[2 * i + 1] = l;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nwg * R; i += 256) {  // weight of part i against its head's maximum
+        const int r = i % R;
+        float M = -INFINITY;
+        for (int w = 0; w < nwg; ++w) M = fmaxf(M, s_ml[2 * (w * R + r)]);
+        s_ml[2 * nwg * R + i] = exp2f(s_ml[2 * i] - (M == -INFINITY ? 0.0f : M));
+    }
+    __syncthreads();
+    const float* s_f = s_ml + 2 * nwg * R;
+    for (int i = threadIdx.x; i < R * D; i += 256) {
+        const int r = i / D, c = i % D;
+        float L = 0.0f, O = 0.0f;
+        for (int w0 = 0; w0 < nwg; w0 += 8) {  // eight parts' loads in flight at once
+            float a[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                a[j] = w0 + j < nwg ? ld_dev(&ws_acc[(base + (size_t)(w0 + j) * R + r) * D + c]) : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (w0 + j < nwg) {
+                    const int pi = (w0 + j) * R + r;
+                    L = fmaf(s_ml[2 * pi + 1], s_f[pi], L);
+                    O = fmaf(a[j], s_f[pi], O);
+                }
+            }
+        }
+        out[((size_t)unit * R + r) * D + c] = (__bf16)(O / L);
+    }
+    if (threadIdx.x == 0)  // zero again for the next call
+        __hip_atomic_store(&tickets[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Work item = (sequence, KV head, range of `chunk` tokens), numbered
 // item = unit * splits + split with unit = b * Hkv + g.  Each wave is
 // independent: it walks items blockIdx.x * 4 + wave, + 4 gridDim.x, ..., all
 // 128-token steps of an item in order, and issues the first loads of its next
 // item while it finishes the current one.
-template <int D, int R>
+//
+// With kTicket (a split head, no residual window) the grid is one item per
+// wave and a workgroup's four waves hold four consecutive token ranges of one
+// (sequence, KV head): the four parts are merged through LDS, each workgroup
+// writes one part to the workspace (ws_splits = workgroups per KV head) and
+// takes a ticket on the head; the workgroup that takes the last ticket merges
+// the head's parts, writes the output and puts the ticket back to zero, so
+// the whole decode is one launch with no spinning.
+template <int D, int R, bool kTicket>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes, const uint32_t* __restrict__ k_sz,
     const uint8_t* __restrict__ v_codes, const uint32_t* __restrict__ v_sz, int n, int tok_stride, int grp_stride,
     int chunk, int splits, int ws_splits, int direct, int n_items, float scale_log2, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml, __bf16* __restrict__ out, const int32_t* __restrict__ counts) {
+    float* __restrict__ ws_ml, __bf16* __restrict__ out, const int32_t* __restrict__ counts,
+    int32_t* __restrict__ tickets) {
     constexpr int NG = D / 32;  // 32-channel groups: key K blocks and value scale groups
     constexpr int NT = D / 16;  // 16-channel value tiles
     constexpr int GPL = NG * R / 4 > 1 ? NG * R / 4 : 1;  // value groups per lane in the weight prep
     __shared__ __align__(16) uint8_t s_qa[4][4][R][4][128];   // wave, block, head, piece, K position
     __shared__ __align__(16) uint8_t s_wa[4][R][NG][4][128];  // wave, head, value group, piece, K position
     __shared__ float s_z[4][R][NG];
+    // ticket mode: the four waves' parts (sum 2^(l - m) v per channel, then m and
+    // the sum of 2^(l - m)) and the last-ticket flag
+    __shared__ float s_tp[kTicket ? 4 : 1][R][D + 2];
+    __shared__ int s_last;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: keeps bases scalar
     const int lane = threadIdx.x % kWave;
@@ -502,6 +612,18 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
             if (col == 0 && wlane) s_z[wave][myh][gbase + i] = zs;
         }
         wave_sync_lds();
+        if constexpr (kTicket) {
+            if (blk < R) {
+#pragma unroll
+                for (int T = 0; T < NT; ++T) s_tp[wave][blk][16 * T + col] = acc[T] + s_z[wave][blk][T / 2];
+                if (col == 0) {
+                    s_tp[wave][blk][D] = m_run;
+                    s_tp[wave][blk][D + 1] = lsum;
+                }
+            }
+            ticket_merge<D, R>(s_tp, &s_last, ps.unit, blockIdx.x % ws_splits, ws_splits, ws_acc, ws_ml, out, tickets);
+            break;  // one item per wave
+        }
         if (blk < R) {
             const size_t row = (size_t)ps.unit * R + blk;  // query head b * Hq + g * R + blk
 #pragma unroll
@@ -716,7 +838,8 @@ template <int D, int R>
 int resident_workgroups() {
     static const int per_cu = [] {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partial_kernel<D, R>, 256, 0) != hipSuccess || nb < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partial_kernel<D, R, false>, 256, 0) != hipSuccess ||
+            nb < 1)
             nb = 1;
         return nb;
     }();
@@ -758,18 +881,33 @@ hipError_t launch_dr(const void* q, const DecodeSrc& src, int B, int Hq, int Hkv
                            src.v_res, src.res_stride, src.n_res, Hq, Hkv, scale_log2, o);
         return hipGetLastError();
     }
+    // workspace: the tickets of split heads first (kTicketBytes, zero between
+    // calls), then the parts
+    int32_t* tickets = static_cast<int32_t*>(ws);
+    float* ws_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kTicketBytes);
+    const int parts = plan.splits;
+    const long items = (long)B * Hkv * plan.splits;
+    if (plan.ticket && !res && !src.counts) {
+        // one launch: one item per wave, four ranges of a head per workgroup,
+        // the last workgroup of each head merges (plan.splits % 4 == 0)
+        const int nwg = parts / 4;
+        float* ws_ml = ws_acc + (size_t)B * Hq * nwg * D;
+        hipLaunchKernelGGL((decode_partial_kernel<D, R, true>), dim3((unsigned)(items / 4)), dim3(256), 0, stream, qq,
+                           src.k_codes, src.k_sz, src.v_codes, src.v_sz, src.n, src.tok_stride, src.grp_stride,
+                           plan.chunk, plan.splits, nwg, 0, (int)items, scale_log2, ws_acc, ws_ml, o, src.counts,
+                           tickets);
+        return hipGetLastError();
+    }
     // packed ranges: plan.splits parts in the workspace (the output itself when
     // it is the only part); the window, if any, is computed and merged by the
     // merge kernel
-    const int parts = plan.splits;
     const bool direct = parts == 1 && !res;
-    float* ws_acc = static_cast<float*>(ws);
     float* ws_ml = ws_acc + (size_t)B * Hq * parts * D;
-    const long items = (long)B * Hkv * plan.splits;
     const long grid = std::min<long>((items + 3) / 4, resident_workgroups<D, R>());
-    hipLaunchKernelGGL((decode_partial_kernel<D, R>), dim3((unsigned)grid), dim3(256), 0, stream, qq, src.k_codes,
-                       src.k_sz, src.v_codes, src.v_sz, src.n, src.tok_stride, src.grp_stride, plan.chunk, plan.splits,
-                       parts, direct ? 1 : 0, (int)items, scale_log2, ws_acc, ws_ml, o, src.counts);
+    hipLaunchKernelGGL((decode_partial_kernel<D, R, false>), dim3((unsigned)grid), dim3(256), 0, stream, qq,
+                       src.k_codes, src.k_sz, src.v_codes, src.v_sz, src.n, src.tok_stride, src.grp_stride, plan.chunk,
+                       plan.splits, parts, direct ? 1 : 0, (int)items, scale_log2, ws_acc, ws_ml, o, src.counts,
+                       tickets);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(B * Hq), dim3(D + (res ? kWave : 0)), 0, stream, ws_acc,
@@ -820,19 +958,32 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int n_keep, int D) {
     const int steps = (n_keep + kStep - 1) / kStep;
     const long want = (4096 + units - 1) / units;  // aim for >= 4096 work items
     int splits = (int)(want < 1 ? 1 : (want > steps ? steps : want));
-    if (splits > kMaxSplits - 1) splits = kMaxSplits - 1;  // one merge slot stays free for a residual part
-    const int per = (steps + splits - 1) / splits;
+    if (splits > kMaxSplits - 4) splits = kMaxSplits - 4;  // room for a residual part in the merge
+    int per = (steps + splits - 1) / splits;
     splits = (steps + per - 1) / per;
-    return {splits, per * kStep};
+    bool ticket = false;
+    const int split4 = (splits + 3) / 4 * 4;
+    if (splits > 1 && split4 <= 4 * kTicketMaxWorkgroups) {
+        // one launch: a split head takes whole workgroups of four ranges
+        // (ranges past the last token are empty parts, fewer than four)
+        splits = split4;
+        per = (steps + splits - 1) / splits;
+        ticket = true;
+    }
+    return {splits, per * kStep, ticket};
 }
 
 size_t decode_ws_bytes(int B, int Hq, int D, const DecodePlan& plan) {
-    return (size_t)B * Hq * plan.splits * (D + 2) * sizeof(float);
+    // one-launch plans: one part per workgroup of four ranges after the first
+    // (a head in one workgroup merges in LDS); merge-kernel plans: one part
+    // per range; a head of one range needs none
+    const int parts = plan.ticket ? (plan.splits > 4 ? plan.splits / 4 : 0) : (plan.splits > 1 ? plan.splits : 0);
+    return kTicketBytes + (size_t)B * Hq * parts * (D + 2) * sizeof(float);
 }
 
 size_t stream_decode_ws_bytes(int B, int Hq, int D, int n_packed, int n_res, const DecodePlan& plan) {
     const int parts = (n_packed > 0 ? plan.splits : 0) + (n_res > 0 ? 1 : 0);
-    return (size_t)B * Hq * parts * (D + 2) * sizeof(float);
+    return kTicketBytes + (size_t)B * Hq * parts * (D + 2) * sizeof(float);
 }
 
 hipError_t launch_decode(const void* q, const uint8_t* k_codes, const uint32_t* k_sz, const uint8_t* v_codes,

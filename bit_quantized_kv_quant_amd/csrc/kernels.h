@@ -39,13 +39,22 @@ hipError_t launch_select_topk(const float* scores, int B, int Hkv, int T_ctx, in
 
 // Decode: split plan shared by the workspace-size query and the launcher.
 struct DecodePlan {
-    int splits;  // token ranges per (sequence, KV head)
-    int chunk;   // tokens per split (multiple of 128)
+    int splits;   // token ranges per (sequence, KV head)
+    int chunk;    // tokens per split (multiple of 128)
+    bool ticket;  // a split head merged inside the launch (splits a multiple of 4)
 };
+// Most workgroups of four ranges per head merged inside the decode launch
+// (workgroup parts handed over by a ticket); heads split further use the
+// separate merge kernel, whose launch costs less than that many handovers.
+constexpr int kTicketMaxWorkgroups = 4;
 DecodePlan decode_plan(int B, int Hq, int Hkv, int n_keep, int D);
 size_t decode_ws_bytes(int B, int Hq, int D, const DecodePlan& plan);
 size_t stream_decode_ws_bytes(int B, int Hq, int D, int n_packed, int n_res, const DecodePlan& plan);
 
+// Head of every decode workspace: one int32 ticket per (sequence, KV head)
+// of a split plan (split plans have fewer than 4096 such heads).  It must
+// hold zeros before a workspace's first use; every decode leaves it zero.
+constexpr size_t kTicketBytes = 4096 * sizeof(int32_t);
 // Bytes of the allocation-free decode's scratch array (one per device).
 constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
 // Device address of the current device's scratch array (resolved once per

@@ -169,11 +169,16 @@ int minikv_quant_pack(const void *k, const void *v, int in_dtype, const int32_t 
  * q bf16 [B][Hq][D] -> out bf16 [B][Hq][D]:
  *   out[b,h] = sum_t softmax_t(q . khat_t * sm_scale) vhat_t over the n_keep packed tokens,
  * khat / vhat = code * s + z.  ws: device workspace of at least
- * minikv_decode_ws_bytes(B, Hq, Hkv, n_keep, D) bytes (split partial results).
- * sm_scale <= 0 means 1/sqrt(D).
+ * minikv_decode_ws_bytes(B, Hq, Hkv, n_keep, D) bytes.  Its first
+ * MINIKV_DECODE_TICKET_BYTES bytes must hold zeros before the buffer's first
+ * use by any decode call: a head whose tokens are split over several
+ * workgroups takes a ticket there, the last workgroup merges the head's
+ * parts (which follow the tickets), and every call leaves the tickets zero
+ * again.  sm_scale <= 0 means 1/sqrt(D).
  * Errors: NULL; SHAPE (Hq % cache->Hkv, sizes < 1); UNSUPPORTED (D, group,
  * Hq/Hkv not 1, 2 or 4); ALIGN; WORKSPACE; LAUNCH.
  */
+#define MINIKV_DECODE_TICKET_BYTES ((size_t)16384)
 int minikv_decode_attn(const void *q, const minikv_packed_t *cache, int Hq, float sm_scale,
                        void *out, void *ws, size_t ws_bytes, void *stream);
 
@@ -185,14 +190,15 @@ int minikv_decode_attn(const void *q, const minikv_packed_t *cache, int Hq, floa
  * GPU the library runs on, held until the process ends; no hipMalloc,
  * hipFree or allocating routine is called.  Same arguments (minus ws),
  * results and errors as minikv_decode_attn, plus WORKSPACE when the split
- * plan's partials (minikv_decode_ws_bytes) exceed the array - no plan of a
- * supported shape does: at most about 8192 (head, range) parts of (D + 2)
- * floats per query head, 17 MB at four query heads per KV head, D = 128; a
- * plan with one range per KV head uses no scratch - and LAUNCH when the
- * array's device address cannot be resolved.  Every call on a GPU
- * shares that GPU's array, which keeps the last call's partials (nothing in
- * it needs to start at zero): calls that overlap on one GPU (other streams,
- * other threads) race.
+ * plan's workspace (minikv_decode_ws_bytes) exceeds the array - no plan of a
+ * supported shape does: at most about 8192 (KV head, part) pairs of (D + 2)
+ * floats per query head, 17 MB at four query heads per KV head and D = 128,
+ * after the tickets; a plan with one range per KV head uses no scratch - and
+ * LAUNCH when the array's device address cannot be resolved.
+ * Every call on a GPU shares that GPU's array: its tickets start at zero
+ * (the array is zero-initialised) and every call leaves them zero; the parts
+ * keep the last call's values.  Calls that overlap on one GPU (other
+ * streams, other threads) race.
  */
 #define MINIKV_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
 int minikv_decode_attn_noalloc(const void *q, const minikv_packed_t *cache, int Hq, float sm_scale,

@@ -357,19 +357,24 @@ def test_decode_noalloc_validation(L):
 
 
 def test_every_decode_split_plan_fits_the_scratch_array(L):
-    """The split partials of any supported decode shape fit the allocation-free
-    entry point's array: (sequence, KV head) units x ranges stay below about
-    8192 whenever a head is split (one range per head needs no scratch)."""
+    """The decode workspace of any supported shape - the 16 KiB ticket area,
+    then one part of D + 2 floats per query head and token range (merged by
+    the merge kernel) or per workgroup of four ranges after a head's first
+    (merged inside the launch) - fits the allocation-free entry point's array:
+    (sequence, KV head) units x parts stay below 8192 (one range per head, or
+    one workgroup, needs no parts)."""
     worst = 0
     for units in list(range(1, 300)) + list(range(300, 4200, 7)) + [4095, 4096, 5000, 20000]:
         for n in (1, 129, 614, 6600, 65536, 1 << 20):
             for R in (1, 2, 4):
                 for D in (64, 128):
                     ws = L.minikv_decode_ws_bytes(units, R, 1, n, D)
-                    splits = ws // (units * R * (D + 2) * 4)
-                    assert splits * units * R * (D + 2) * 4 == ws and splits >= 1
-                    if splits > 1:
-                        assert units * splits < 8192
-                        worst = max(worst, ws)
+                    assert ws >= _lib.DECODE_TICKET_BYTES
+                    parts = (ws - _lib.DECODE_TICKET_BYTES) // (units * R * (D + 2) * 4)
+                    assert parts * units * R * (D + 2) * 4 + _lib.DECODE_TICKET_BYTES == ws
+                    if units >= 4096 or n <= 128:
+                        assert parts == 0           # one range per head: the output is written directly
+                    assert units * parts < 8192
+                    worst = max(worst, ws)
     assert worst <= _lib.DECODE_SCRATCH_BYTES
-    print("largest split workspace:", worst)
+    print("largest decode workspace:", worst)

@@ -188,6 +188,9 @@ def _decode_case(dev, B, Hq, Hkv, n, D, seed, kmul=3.0, vstd=1.0):
     (1, 4, 1, 6600, 128), (4, 2, 1, 129, 64), (8, 32, 32, 614, 128),
     # more token ranges than merge threads: 157 ranges at D = 64, 129 at D = 128
     (1, 2, 1, 20000, 64), (1, 2, 1, 33000, 128),
+    # heads merged inside the launch: one, two, three and four workgroups of
+    # four ranges per head (the last ones with empty ranges)
+    (3, 8, 4, 300, 128), (2, 8, 2, 1000, 128), (1, 4, 4, 1500, 128), (2, 8, 2, 2000, 64),
 ])
 def test_decode_matches_oracle(dev, B, Hq, Hkv, n, D):
     say("decode B", B, "Hq", Hq, "Hkv", Hkv, "n", n, "D", D)
@@ -489,7 +492,7 @@ def test_decode_graph_replay_matches_eager(dev):
         caches.append(mk.quant_pack(k.to(torch.bfloat16), v.to(torch.bfloat16)))
     q = torch.from_numpy(synth.bf16_round(rng.standard_normal((B, Hq, D)).astype(np.float32))).to(dev).to(torch.bfloat16)
     outs = [torch.empty_like(q) for _ in caches]
-    ws = torch.empty(max(mk.decode_ws_bytes(B, Hq, Hkv, c.n_keep, D) for c in caches) + 16, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(mk.decode_ws_bytes(B, Hq, Hkv, c.n_keep, D) for c in caches) + 16, dtype=torch.uint8, device=dev)
     for c, o in zip(caches, outs):
         mk.decode_attn(q, c, out=o, ws=ws)
     torch.cuda.synchronize()
@@ -507,7 +510,7 @@ def test_decode_graph_replay_matches_eager(dev):
     for rep in range(3):
         for o in outs:
             o.zero_()
-        mk.decode_attn(q, caches[3], out=torch.empty_like(q), ws=torch.empty_like(ws))  # eager work between replays
+        mk.decode_attn(q, caches[3], out=torch.empty_like(q), ws=torch.zeros_like(ws))  # eager work between replays
         graph.replay()
         torch.cuda.synchronize()
         for i, (o, e) in enumerate(zip(outs, eager)):

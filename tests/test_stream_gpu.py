@@ -160,7 +160,7 @@ def test_device_step_matches_oracle(dev, Hq, Hkv, D, n_sel, steps):
     cap = 32 * ((n_sel + steps) // 32 + 2)
     rng, c, st = _start(dev, n_sel + 1, B, Hkv, T, D, n_sel, cap)
     c.to_device_counts()
-    ws = torch.empty(c.step_ws_bytes(Hq), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(c.step_ws_bytes(Hq), dtype=torch.uint8, device=dev)
     for step in range(steps):
         kn, vn = _token(rng, B, Hkv, D), _token(rng, B, Hkv, D, 0.5)
         c.step_append(torch.from_numpy(kn).to(dev).to(torch.bfloat16), torch.from_numpy(vn).to(dev).to(torch.bfloat16))
@@ -184,7 +184,7 @@ def test_device_step_graph_replays(dev):
     for l in range(2):
         rng, c, st = _start(dev, 50 + l, B, Hkv, T, D, n_sel, cap)
         c.to_device_counts()
-        layers.append([rng, c, st, torch.empty(c.step_ws_bytes(Hq), dtype=torch.uint8, device=dev)])
+        layers.append([rng, c, st, torch.zeros(c.step_ws_bytes(Hq), dtype=torch.uint8, device=dev)])
     # one eager step on a scratch cache of the same shapes (host-side launch set-up happens outside the capture)
     _, scratch, _ = _start(dev, 99, B, Hkv, T, D, n_sel, cap)
     scratch.to_device_counts()
