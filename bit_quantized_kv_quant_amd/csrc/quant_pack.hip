@@ -75,10 +75,13 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
 // bound s (c + t) lies less than one fp32 ulp from c s, on the side that makes the fp32 decision
 // d > s/2, d >= 3s/2, d > 5s/2 (no fp32 value falls between c s and the bound).  Checked for every
 // positive fp16 s against the division (tests/test_code_thresholds_exhaustive.py).  With s == 0 the
-// thresholds are infinite and the code is 0.
+// thresholds are infinite and the code is 0.  The three tests are taken as a two-step search:
+// d >= 3s/2 decides the high bit, and the low bit is d > 5s/2 above it or d > s/2 below it (the
+// same decisions, one comparison fewer).
 __device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
     const float d = x - p.z;
-    return (uint32_t)(d > p.h1) + (uint32_t)(d >= p.h2) + (uint32_t)(d > p.h3);
+    const bool hi = d >= p.h2;
+    return (hi ? 2u : 0u) + (uint32_t)(d > (hi ? p.h3 : p.h1));
 }
 
 // Where one call packs: tokens 0..n-1 of its selection (index row stride
