@@ -188,7 +188,7 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Ticket-mode epilogue of a workgroup (all 256 threads): s_tp holds the four
+// Ticket-mode epilogue of a workgroup (all 64 NW threads): s_tp holds the NW
 // waves' parts of (sequence, KV head) `unit`, each (head r) a row of D sums
 // 2^(l - m) v, then m and the sum of 2^(l - m) (log2 units).  They are merged
 // against their common maximum; with one workgroup per head (nwg == 1) the
@@ -206,22 +206,23 @@ __device__ __forceinline__ void wave_sync_lds() {
 // write-back / invalidate fences: every wave waits for its part stores to
 // complete before the workgroup takes its ticket, and the last workgroup
 // reads the parts only after its ticket has come back.
-template <int D, int R>
+template <int D, int R, int NW>
 __device__ __forceinline__ void ticket_merge(float (*s_tp)[R][D + 2], int* s_last, int unit, int wg, int nwg,
                                              float* __restrict__ ws_acc, float* __restrict__ ws_ml,
                                              __bf16* __restrict__ out, int32_t* __restrict__ tickets) {
     auto st_dev = [](float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
     auto ld_dev = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-    __syncthreads();  // the four parts are in LDS
-    for (int i = threadIdx.x; i < R * D; i += 256) {
+    constexpr int NTH = 64 * NW;
+    __syncthreads();  // the waves' parts are in LDS
+    for (int i = threadIdx.x; i < R * D; i += NTH) {
         const int r = i / D, c = i % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_tp[w][r][D]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_tp[w][r][D]);
         const float Ms = M == -INFINITY ? 0.0f : M;
         float L = 0.0f, O = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const float f = exp2f(s_tp[w][r][D] - Ms);
             L = fmaf(s_tp[w][r][D + 1], f, L);
             O = fmaf(s_tp[w][r][c], f, O);
@@ -248,13 +249,13 @@ __device__ __forceinline__ void ticket_merge(float (*s_tp)[R][D + 2], int* s_las
     // pairs; the LDS parts above are no longer needed), then the weights
     float* s_ml = &s_tp[0][0][0];
     const size_t base = (size_t)unit * nwg * R;
-    for (int i = threadIdx.x; i < nwg * R; i += 256) {
+    for (int i = threadIdx.x; i < nwg * R; i += NTH) {
         const float m = ld_dev(&ws_ml[(base + i) * 2]), l = ld_dev(&ws_ml[(base + i) * 2 + 1]);
         s_ml[2 * i] = m;
         s_ml[2 * i + 1] = l;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nwg * R; i += 256) {  // weight of part i against its head's maximum
+    for (int i = threadIdx.x; i < nwg * R; i += NTH) {  // weight of part i against its head's maximum
         const int r = i % R;
         float M = -INFINITY;
         for (int w = 0; w < nwg; ++w) M = fmaxf(M, s_ml[2 * (w * R + r)]);
@@ -262,7 +263,7 @@ __device__ __forceinline__ void ticket_merge(float (*s_tp)[R][D + 2], int* s_las
     }
     __syncthreads();
     const float* s_f = s_ml + 2 * nwg * R;
-    for (int i = threadIdx.x; i < R * D; i += 256) {
+    for (int i = threadIdx.x; i < R * D; i += NTH) {
         const int r = i / D, c = i % D;
         float L = 0.0f, O = 0.0f;
         for (int w0 = 0; w0 < nwg; w0 += 8) {  // eight parts' loads in flight at once
@@ -292,14 +293,14 @@ __device__ __forceinline__ void ticket_merge(float (*s_tp)[R][D + 2], int* s_las
 // item while it finishes the current one.
 //
 // With kTicket (a split head, no residual window) the grid is one item per
-// wave and a workgroup's four waves hold four consecutive token ranges of one
-// (sequence, KV head): the four parts are merged through LDS, each workgroup
+// wave and a workgroup's NW waves hold NW consecutive token ranges of one
+// (sequence, KV head): the NW parts are merged through LDS, each workgroup
 // writes one part to the workspace (ws_splits = workgroups per KV head) and
 // takes a ticket on the head; the workgroup that takes the last ticket merges
 // the head's parts, writes the output and puts the ticket back to zero, so
 // the whole decode is one launch with no spinning.
-template <int D, int R, bool kTicket>
-__global__ __launch_bounds__(256) void decode_partial_kernel(
+template <int D, int R, int NW, bool kTicket>
+__global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes, const uint32_t* __restrict__ k_sz,
     const uint8_t* __restrict__ v_codes, const uint32_t* __restrict__ v_sz, int n, int tok_stride, int grp_stride,
     int chunk, int splits, int ws_splits, int direct, int n_items, float scale_log2, float* __restrict__ ws_acc,
@@ -308,20 +309,20 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     constexpr int NG = D / 32;  // 32-channel groups: key K blocks and value scale groups
     constexpr int NT = D / 16;  // 16-channel value tiles
     constexpr int GPL = NG * R / 4 > 1 ? NG * R / 4 : 1;  // value groups per lane in the weight prep
-    __shared__ __align__(16) uint8_t s_qa[4][4][R][4][128];   // wave, block, head, piece, K position
-    __shared__ __align__(16) uint8_t s_wa[4][R][NG][4][128];  // wave, head, value group, piece, K position
-    __shared__ float s_z[4][R][NG];
-    // ticket mode: the four waves' parts (sum 2^(l - m) v per channel, then m and
-    // the sum of 2^(l - m)) and the last-ticket flag
-    __shared__ float s_tp[kTicket ? 4 : 1][R][D + 2];
+    __shared__ __align__(16) uint8_t s_qa[NW][4][R][4][128];   // wave, block, head, piece, K position
+    __shared__ __align__(16) uint8_t s_wa[NW][R][NG][4][128];  // wave, head, value group, piece, K position
+    __shared__ float s_z[NW][R][NG];
+    // ticket mode: the waves' parts (sum 2^(l - m) v per channel, then m and the
+    // sum of 2^(l - m)) and the last-ticket flag
+    __shared__ float s_tp[kTicket ? NW : 1][R][D + 2];
     __shared__ int s_last;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: keeps bases scalar
     const int lane = threadIdx.x % kWave;
     const int col = lane % 16, blk = lane / 16;
     const int myh = blk % R;  // head of this lane's MFMA result rows
-    const int nwaves = gridDim.x * 4;
-    int item = blockIdx.x * 4 + wave;
+    const int nwaves = gridDim.x * NW;
+    int item = blockIdx.x * NW + wave;
     if (item >= n_items) return;  // wave-uniform; the kernel has no workgroup barrier
     // a device-side streaming step: the packed token count is read here (the
     // split plan covers the capacity n; ranges past the count are empty parts)
@@ -621,7 +622,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
                     s_tp[wave][blk][D + 1] = lsum;
                 }
             }
-            ticket_merge<D, R>(s_tp, &s_last, ps.unit, blockIdx.x % ws_splits, ws_splits, ws_acc, ws_ml, out, tickets);
+            ticket_merge<D, R, NW>(s_tp, &s_last, ps.unit, blockIdx.x % ws_splits, ws_splits, ws_acc, ws_ml, out,
+                                   tickets);
             break;  // one item per wave
         }
         if (blk < R) {
@@ -838,7 +840,7 @@ template <int D, int R>
 int resident_workgroups() {
     static const int per_cu = [] {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partial_kernel<D, R, false>, 256, 0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partial_kernel<D, R, 4, false>, 256, 0) != hipSuccess ||
             nb < 1)
             nb = 1;
         return nb;
@@ -888,14 +890,21 @@ hipError_t launch_dr(const void* q, const DecodeSrc& src, int B, int Hq, int Hkv
     const int parts = plan.splits;
     const long items = (long)B * Hkv * plan.splits;
     if (plan.ticket && !res && !src.counts) {
-        // one launch: one item per wave, four ranges of a head per workgroup,
-        // the last workgroup of each head merges (plan.splits % 4 == 0)
-        const int nwg = parts / 4;
+        // one launch: one item per wave, plan.nw ranges of a head per
+        // workgroup, the last workgroup of each head merges (plan.splits %
+        // plan.nw == 0)
+        const int nwg = parts / plan.nw;
         float* ws_ml = ws_acc + (size_t)B * Hq * nwg * D;
-        hipLaunchKernelGGL((decode_partial_kernel<D, R, true>), dim3((unsigned)(items / 4)), dim3(256), 0, stream, qq,
-                           src.k_codes, src.k_sz, src.v_codes, src.v_sz, src.n, src.tok_stride, src.grp_stride,
-                           plan.chunk, plan.splits, nwg, 0, (int)items, scale_log2, ws_acc, ws_ml, o, src.counts,
-                           tickets);
+        if (plan.nw == 8)
+            hipLaunchKernelGGL((decode_partial_kernel<D, R, 8, true>), dim3((unsigned)(items / 8)), dim3(512), 0,
+                               stream, qq, src.k_codes, src.k_sz, src.v_codes, src.v_sz, src.n, src.tok_stride,
+                               src.grp_stride, plan.chunk, plan.splits, nwg, 0, (int)items, scale_log2, ws_acc, ws_ml,
+                               o, src.counts, tickets);
+        else
+            hipLaunchKernelGGL((decode_partial_kernel<D, R, 4, true>), dim3((unsigned)(items / 4)), dim3(256), 0,
+                               stream, qq, src.k_codes, src.k_sz, src.v_codes, src.v_sz, src.n, src.tok_stride,
+                               src.grp_stride, plan.chunk, plan.splits, nwg, 0, (int)items, scale_log2, ws_acc, ws_ml,
+                               o, src.counts, tickets);
         return hipGetLastError();
     }
     // packed ranges: plan.splits parts in the workspace (the output itself when
@@ -904,7 +913,7 @@ hipError_t launch_dr(const void* q, const DecodeSrc& src, int B, int Hq, int Hkv
     const bool direct = parts == 1 && !res;
     float* ws_ml = ws_acc + (size_t)B * Hq * parts * D;
     const long grid = std::min<long>((items + 3) / 4, resident_workgroups<D, R>());
-    hipLaunchKernelGGL((decode_partial_kernel<D, R, false>), dim3((unsigned)grid), dim3(256), 0, stream, qq,
+    hipLaunchKernelGGL((decode_partial_kernel<D, R, 4, false>), dim3((unsigned)grid), dim3(256), 0, stream, qq,
                        src.k_codes, src.k_sz, src.v_codes, src.v_sz, src.n, src.tok_stride, src.grp_stride, plan.chunk,
                        plan.splits, parts, direct ? 1 : 0, (int)items, scale_log2, ws_acc, ws_ml, o, src.counts,
                        tickets);
@@ -962,22 +971,29 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int n_keep, int D) {
     int per = (steps + splits - 1) / splits;
     splits = (steps + per - 1) / per;
     bool ticket = false;
-    const int split4 = (splits + 3) / 4 * 4;
-    if (splits > 1 && split4 <= 4 * kTicketMaxWorkgroups) {
-        // one launch: a split head takes whole workgroups of four ranges
-        // (ranges past the last token are empty parts, fewer than four)
-        splits = split4;
-        per = (steps + splits - 1) / splits;
-        ticket = true;
+    int nw = 4;
+    if (splits > 1) {
+        // one launch: a split head takes whole workgroups of nw ranges (ranges
+        // past the last token are empty parts, fewer than nw): one 4-wave
+        // workgroup up to four ranges, 8-wave workgroups beyond, at most
+        // kTicketMaxWorkgroups of them per head
+        nw = splits <= 4 ? 4 : 8;
+        const int rounded = (splits + nw - 1) / nw * nw;
+        if (rounded <= nw * kTicketMaxWorkgroups) {
+            splits = rounded;
+            per = (steps + splits - 1) / splits;
+            ticket = true;
+        }
     }
-    return {splits, per * kStep, ticket};
+    return {splits, per * kStep, ticket, nw};
 }
 
 size_t decode_ws_bytes(int B, int Hq, int D, const DecodePlan& plan) {
-    // one-launch plans: one part per workgroup of four ranges after the first
+    // one-launch plans: one part per workgroup of nw ranges after the first
     // (a head in one workgroup merges in LDS); merge-kernel plans: one part
     // per range; a head of one range needs none
-    const int parts = plan.ticket ? (plan.splits > 4 ? plan.splits / 4 : 0) : (plan.splits > 1 ? plan.splits : 0);
+    const int parts =
+        plan.ticket ? (plan.splits > plan.nw ? plan.splits / plan.nw : 0) : (plan.splits > 1 ? plan.splits : 0);
     return kTicketBytes + (size_t)B * Hq * parts * (D + 2) * sizeof(float);
 }
 

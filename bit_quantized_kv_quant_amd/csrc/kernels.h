@@ -41,12 +41,16 @@ hipError_t launch_select_topk(const float* scores, int B, int Hkv, int T_ctx, in
 struct DecodePlan {
     int splits;   // token ranges per (sequence, KV head)
     int chunk;    // tokens per split (multiple of 128)
-    bool ticket;  // a split head merged inside the launch (splits a multiple of 4)
+    bool ticket;  // a split head merged inside the launch (splits a multiple of nw)
+    int nw;       // waves (token ranges) per workgroup of such a launch: 4 or 8
 };
-// Most workgroups of four ranges per head merged inside the decode launch
+// Most workgroups of ranges per head merged inside the decode launch
 // (workgroup parts handed over by a ticket); heads split further use the
-// separate merge kernel, whose launch costs less than that many handovers.
-constexpr int kTicketMaxWorkgroups = 4;
+// separate merge kernel.  Measured: 7 workgroups of 8 ranges per head (a
+// 6600-token head, 4 x 8 KV heads) merge faster in the launch than through
+// the merge kernel (0.47 against 0.52 ms per 32-layer step); 13 workgroups
+// of 4 ranges were slower (0.56).
+constexpr int kTicketMaxWorkgroups = 8;
 DecodePlan decode_plan(int B, int Hq, int Hkv, int n_keep, int D);
 size_t decode_ws_bytes(int B, int Hq, int D, const DecodePlan& plan);
 size_t stream_decode_ws_bytes(int B, int Hq, int D, int n_packed, int n_res, const DecodePlan& plan);

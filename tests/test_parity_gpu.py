@@ -188,9 +188,11 @@ def _decode_case(dev, B, Hq, Hkv, n, D, seed, kmul=3.0, vstd=1.0):
     (1, 4, 1, 6600, 128), (4, 2, 1, 129, 64), (8, 32, 32, 614, 128),
     # more token ranges than merge threads: 157 ranges at D = 64, 129 at D = 128
     (1, 2, 1, 20000, 64), (1, 2, 1, 33000, 128),
-    # heads merged inside the launch: one, two, three and four workgroups of
-    # four ranges per head (the last ones with empty ranges)
+    # heads merged inside the launch: one 4-wave or one 8-wave workgroup per
+    # head (LDS merge), and two, three and four 8-wave workgroups per head
+    # (ticket handover; some with empty ranges)
     (3, 8, 4, 300, 128), (2, 8, 2, 1000, 128), (1, 4, 4, 1500, 128), (2, 8, 2, 2000, 64),
+    (1, 4, 4, 2900, 128), (2, 8, 2, 4000, 64),
 ])
 def test_decode_matches_oracle(dev, B, Hq, Hkv, n, D):
     say("decode B", B, "Hq", Hq, "Hkv", Hkv, "n", n, "D", D)

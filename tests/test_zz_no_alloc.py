@@ -41,12 +41,13 @@ def _noalloc(q, cache):
 
 def test_noalloc_decode_matches_workspace_entry_point():
     dev = require_gpu()
-    # a split plan (52 token ranges per KV head: 13 workgroups merged by the
-    # last one's ticket) and a smaller one right after it (12 ranges, three
-    # workgroups), so the second call reuses the tickets the first left zero
-    # and the array that still holds its parts; then one workgroup per head,
-    # and a plan with one range per KV head, which uses no scratch
-    cases = [(4, 32, 8, 6600, 128, 1), (2, 8, 2, 1300, 64, 2), (2, 4, 4, 301, 128, 3), (64, 64, 64, 200, 128, 4)]
+    # a split plan (52 token ranges per KV head, merged by the merge kernel)
+    # and a smaller one right after it (16 ranges: two 8-wave workgroups per
+    # head, handed over by a ticket), then 24 ranges (three workgroups, which
+    # take the tickets the previous call left zero again), one workgroup per
+    # head, and a plan with one range per KV head, which uses no scratch
+    cases = [(4, 32, 8, 6600, 128, 1), (2, 8, 2, 1300, 64, 2), (1, 4, 4, 2900, 128, 5), (2, 4, 4, 301, 128, 3),
+             (64, 64, 64, 200, 128, 4)]
     for B, Hq, Hkv, n, D, seed in cases:
         print("noalloc decode B", B, "Hq", Hq, "Hkv", Hkv, "n", n, "D", D, flush=True)
         q, cache = _case(dev, B, Hq, Hkv, n, D, seed)
