@@ -8,14 +8,20 @@
 //   code = s == 0 ? 0 : clamp(rint(fl32(x - z) / s), 0, 3)
 // The file is compiled with -ffp-contract=off so no multiply-add is fused and
 // the divide by 3 stays correctly rounded; the codes come from exact threshold
-// tests (code_of: three comparisons with exact multiples of s) and match a
+// tests (code_of: comparisons with exact multiples of s) and match a
 // plain IEEE evaluation of the rule bit for bit.
 // Inputs are finite (-fno-honor-nans: min / max need no NaN handling).
 //
-// HBM-bound gather: each kept row is read once (coalesced 4-byte lane loads of
-// two channels), each packed byte written once (key codes: dword stores
-// assembled with DPP ORs; value codes: one 16-byte store per lane).  Keys and
-// values of a token group are packed by the two waves of one workgroup.
+// HBM-bound gather: each kept row is read once, each packed byte written once.
+// Keys and values of a token group are packed by the two waves of one
+// workgroup.  A wave loads its group's 32 rows as whole-row 16-byte chunks
+// (every load instruction covers complete rows), derives the group parameters
+// with cross-lane reductions (keys: a reduce-scatter over the lanes holding the
+// same channels, parameters computed once per channel and handed back; values:
+// DPP over the lanes of a 32-channel group), builds the 2-bit codes a bit at a
+// time from the comparison masks, and writes them through a small LDS staging
+// area so that every global store is a whole 16-byte piece of the packed
+// layout.
 #include <type_traits>
 
 #include "common.h"
@@ -75,14 +81,31 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
 // bound s (c + t) lies less than one fp32 ulp from c s, on the side that makes the fp32 decision
 // d > s/2, d >= 3s/2, d > 5s/2 (no fp32 value falls between c s and the bound).  Checked for every
 // positive fp16 s against the division (tests/test_code_thresholds_exhaustive.py).  With s == 0 the
-// thresholds are infinite and the code is 0.  The three tests are taken as a two-step search:
-// d >= 3s/2 decides the high bit, and the low bit is d > 5s/2 above it or d > s/2 below it (the
-// same decisions, one comparison fewer).
-__device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
+// thresholds are infinite and the code is 0.  The code is the number of tests passed, so its
+// high bit is d >= 3s/2 and its low bit the parity of the three outcomes.  The bits are kept as
+// the wave's comparison masks (bit l: lane l), so the parity is two scalar XORs.
+struct Code {
+    uint64_t hi, lo;
+};
+__device__ __forceinline__ Code code_of(float x, const GroupParams& p) {
     const float d = x - p.z;
-    const bool hi = d >= p.h2;
-    return (hi ? 2u : 0u) + (uint32_t)(d > (hi ? p.h3 : p.h1));
+    const uint64_t m1 = __builtin_amdgcn_ballot_w64(d > p.h1);
+    const uint64_t m2 = __builtin_amdgcn_ballot_w64(d >= p.h2);
+    const uint64_t m3 = __builtin_amdgcn_ballot_w64(d > p.h3);
+    return {m2, m1 ^ m2 ^ m3};
 }
+
+// Packed codes are built a bit at a time from the most significant end:
+// w <- 2 w + (bit of this lane in m), one add whose carry-in is the mask.
+// (Written out: the compiler would otherwise select each bit to 0 / 1 and
+// shift it into place, three operations per bit.)
+__device__ __forceinline__ uint32_t push_bit(uint32_t w, uint64_t m) {
+    uint32_t r;
+    uint64_t carry_out;
+    asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(w), "s"(m));
+    return r;
+}
+__device__ __forceinline__ uint32_t push_code(uint32_t w, Code c) { return push_bit(push_bit(w, c.hi), c.lo); }
 
 // Where one call packs: tokens 0..n-1 of its selection (index row stride
 // idx_stride) go to tokens tok0.. of a destination laid out for tok_stride
@@ -92,260 +115,289 @@ struct PackGeom {
     int n, idx_stride, tok_stride, grp_stride, tok0;
 };
 
-// Lane S of each 16-lane row, to the whole row (DPP row_newbcast).
-template <int S>
-__device__ __forceinline__ float row_bcast(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + S, 0xF, 0xF, false));
-}
 
-// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
-
-// One stage of the row reduce-scatter: lanes paired by DPP pattern P (which
-// flips bit B of lane % 16, among others already resolved) exchange the
-// tokens whose bit B differs from their own and keep the min / max of the
-// rest; slot t (bit B of t clear) ends with the kept token's value.
-template <int P, int B>
-__device__ __forceinline__ void rs_stage(float (&mn)[kGroup], float (&mx)[kGroup], int lane) {
-    const bool hi = (lane >> B) & 1;
-    static_for<0, kGroup>([&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        if constexpr ((t & (1 << B)) == 0) {
-            constexpr int u = t | (1 << B);
-            const float kmn = hi ? mn[u] : mn[t], smn = hi ? mn[t] : mn[u];
-            const float kmx = hi ? mx[u] : mx[t], smx = hi ? mx[t] : mx[u];
-            mn[t] = fminf(kmn, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, smn), P, 0xF, 0xF, false)));
-            mx[t] = fmaxf(kmx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, smx), P, 0xF, 0xF, false)));
-        }
-    });
-}
-
-// Per-token min / max over each 16-lane row, scattered: afterwards mn[0],
-// mx[0] hold token lane % 16 and mn[16], mx[16] token 16 + lane % 16.  The
-// partners are row_mirror (lane ^ 15), row_half_mirror (^ 7), quad_perm
-// [3,2,1,0] (^ 3) and [1,0,3,2] (^ 1); each flips the bit it resolves and, besides
-// it, only bits still unresolved, so partners always hold the same tokens.
-__device__ __forceinline__ void row_reduce_scatter(float (&mn)[kGroup], float (&mx)[kGroup], int lane) {
-    rs_stage<0x140, 3>(mn, mx, lane);
-    rs_stage<0x141, 2>(mn, mx, lane);
-    rs_stage<0x1B, 1>(mn, mx, lane);
-    rs_stage<0xB1, 0>(mn, mx, lane);
-}
-
-// OR over aligned groups of 8 lanes: quad swaps, then the mirrored half row.
-__device__ __forceinline__ uint32_t or8(uint32_t x) {
-    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
-    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
-    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, true);  // row_half_mirror
-    return x;
-}
-
-// Keys: one wave per (group of 32 kept tokens, KV head, sequence).
-// Lane l owns channels 2l, 2l+1 (D/2 active lanes).
+// ---- one group of 32 kept rows, loaded whole ----
+// A wave reads the group's 32 rows (K or V) as 16-byte chunks, every load
+// instruction covering RPI whole rows: lane l takes chunk c = l % CH of rows
+// NI r .. NI r + NI - 1, r = l / CH.  Each lane so holds NI rows x EPC
+// channels.  Rows are read through a buffer resource over the (sequence, KV
+// head) slice: a position outside [0, T) reads as zeros instead of faulting.
 template <typename T, int D>
-__device__ __forceinline__ void pack_keys(
-    const T* __restrict__ k, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int gi, int unit,
-    uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz) {
-    const int lane = threadIdx.x % kWave;
-    const bool active = lane < D / 2;
-    const int c = 2 * (active ? lane : 0);
-    const int t0 = gi * kGroup;
-    const int cnt = min(kGroup, pg.n - t0);
-    const T* base = k + (size_t)unit * T_ctx * D;
-    const int32_t* ids = idx ? idx + (size_t)unit * pg.idx_stride + t0 : nullptr;
+struct Tile {
+    static constexpr int EPC = 16 / (int)sizeof(T);  // channels per 16-byte chunk
+    static constexpr int CH = D / EPC;                // chunks per row
+    static constexpr int RPI = kWave / CH;            // rows per load instruction
+    static constexpr int NI = kGroup / RPI;           // rows per lane
+    static_assert(CH * RPI == kWave && NI * RPI == kGroup, "tile shape");
+};
 
-    Pair x[kGroup];
-    float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < kGroup; ++t) {
-        if (t < cnt) {
-            const int pos = ids ? ids[t] : t0 + t;
-            x[t] = load_pair<T>(base + (size_t)pos * D, c);
-            mn0 = fminf(mn0, x[t].a); mx0 = fmaxf(mx0, x[t].a);
-            mn1 = fminf(mn1, x[t].b); mx1 = fmaxf(mx1, x[t].b);
-        } else {
-            x[t] = {0.0f, 0.0f};
-        }
+template <typename T>
+__device__ __forceinline__ float elem(const u32x4& x, int e) {  // e: compile-time after unrolling
+    if constexpr (std::is_same_v<T, float>) {
+        return __uint_as_float(x[e]);
+    } else {
+        const uint32_t w = x[e / 2];
+        return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
     }
-    const GroupParams p0 = group_params(mn0, mx0);
-    const GroupParams p1 = group_params(mn1, mx1);
-    if (active) {
-        uint2 w = make_uint2(p0.word, p1.word);
-        *reinterpret_cast<uint2*>(k_sz + ((size_t)unit * pg.grp_stride + pg.tok0 / kGroup + gi) * D + c) = w;
-    }
-    uint8_t* crow = k_codes + ((size_t)unit * pg.tok_stride + pg.tok0 + t0) * (D / 4);
-#pragma unroll
-    for (int t = 0; t < kGroup; ++t) {
-        if (t < cnt) {  // uniform across the wave
-            uint32_t nib = active ? (code_of(x[t].a, p0) | (code_of(x[t].b, p1) << 2)) : 0u;
-            uint32_t word = or8(nib << (4 * (lane & 7)));
-            if (active && (lane & 7) == 0)
-                *reinterpret_cast<uint32_t*>(crow + (size_t)t * (D / 4) + 4 * (lane >> 3)) = word;
-        }
+}
+// The same value, widened by an operation the compiler cannot merge with
+// elem(): a pass that reads every element once more later widens again (one
+// operation) instead of holding all widened values in registers in between.
+template <typename T>
+__device__ __forceinline__ float elem_once(const u32x4& x, int e) {
+    if constexpr (std::is_same_v<T, float>) {
+        return __uint_as_float(x[e]);
+    } else {
+        const uint32_t w = x[e / 2];
+        uint32_t r;
+        if (e & 1) asm("v_and_b32 %0, 0xffff0000, %1" : "=v"(r) : "v"(w));
+        else asm("v_lshlrev_b32 %0, 16, %1" : "=v"(r) : "v"(w));
+        return __uint_as_float(r);
     }
 }
 
-// Values: one wave per (block of 32 kept tokens, KV head, sequence).  Lane l
-// owns channels 2l, 2l+1 (D/2 active lanes); a 16-lane row is one 32-channel
-// group, so each token's min / max is a row reduction.  The codes are gathered
-// along tokens: the lane ends with the 32 codes of each of its two channels
-// (8 bytes each, the block's token 4m+j in bits 2j..2j+1 of byte m) and stores
-// both in one 16-byte write; tokens past the call's count stay code 0.
+// Rows t0 + NI r + q (q < NI) of the call's selection for this lane; tokens at
+// or past n read position 0 (their values are never used).
 template <typename T, int D>
-__device__ __forceinline__ void pack_values(
-    const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int gi, int unit,
-    uint8_t* __restrict__ v_codes, uint32_t* __restrict__ v_sz) {
-    const int lane = threadIdx.x % kWave;
-    const bool active = lane < D / 2;
-    const int c = 2 * (active ? lane : 0);
-    const int t0 = gi * kGroup;
-    const int cnt = min(kGroup, pg.n - t0);
-    const T* base = v + (size_t)unit * T_ctx * D;
-    const int32_t* ids = idx ? idx + (size_t)unit * pg.idx_stride + t0 : nullptr;
-
-    Pair x[kGroup];
+__device__ __forceinline__ void load_tile(const T* __restrict__ x, const int32_t* __restrict__ idx, int T_ctx,
+                                          const PackGeom& pg, int unit, int t0, int lane,
+                                          u32x4 (&X)[Tile<T, D>::NI]) {
+    using G = Tile<T, D>;
+    const int c = lane % G::CH, r = lane / G::CH;
+    const auto rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(x + (size_t)unit * T_ctx * D), 0,
+                                                      T_ctx * D * (int)sizeof(T), 0x00020000);
+    int pos[G::NI];
+    if (idx) {  // wave-uniform
+        const auto ri = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(idx + (size_t)unit * pg.idx_stride), 0,
+                                                          pg.n * 4, 0x00020000);
 #pragma unroll
-    for (int t = 0; t < kGroup; ++t) {
-        x[t] = {0.0f, 0.0f};
-        if (t < cnt && active) {
-            const int pos = ids ? ids[t] : t0 + t;
-            x[t] = load_pair<T>(base + (size_t)pos * D, c);
-        }
-    }
-    uint32_t wa[2] = {0u, 0u}, wb[2] = {0u, 0u};
-#pragma unroll
-    for (int t = 0; t < kGroup; ++t) {
-        if (t < cnt) {  // uniform across the wave
-            const float mn = dpp_min<16>(fminf(x[t].a, x[t].b));
-            const float mx = dpp_max<16>(fmaxf(x[t].a, x[t].b));
-            const GroupParams p = group_params(mn, mx);
-            wa[t / 16] |= code_of(x[t].a, p) << (2 * (t % 16));
-            wb[t / 16] |= code_of(x[t].b, p) << (2 * (t % 16));
-            if (active && (lane & 15) == 0)
-                v_sz[((size_t)unit * pg.tok_stride + pg.tok0 + t0 + t) * (D / 32) + (lane >> 4)] = p.word;
-        }
-    }
-    if (active)
-        *reinterpret_cast<uint4*>(v_codes + (((size_t)unit * pg.grp_stride + pg.tok0 / kGroup + gi) * D + c) * 8) =
-            make_uint4(wa[0], wa[1], wb[0], wb[1]);
-}
-
-// Full groups (32 kept tokens): the same rule without per-token branches.  Rows
-// are gathered through a buffer resource sized to the head's T rows (a position
-// outside [0, T) reads as zeros instead of faulting); key-code words and value
-// parameters are collected in registers and written four and two stores per
-// lane at the end.
-template <typename T> __device__ __forceinline__ Pair load_pair_buf(__amdgpu_buffer_rsrc_t r, int off);
-template <> __device__ __forceinline__ Pair load_pair_buf<float>(__amdgpu_buffer_rsrc_t r, int off) {
-    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-    return {__uint_as_float(w.x), __uint_as_float(w.y)};
-}
-template <> __device__ __forceinline__ Pair load_pair_buf<uint16_t>(__amdgpu_buffer_rsrc_t r, int off) {
-    const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-    return {bf16_bits_to_f32(w & 0xFFFFu), bf16_bits_to_f32(w >> 16)};
-}
-
-template <typename T, int D>
-__device__ __forceinline__ void gather_full(const T* __restrict__ x, const int32_t* __restrict__ idx, int T_ctx,
-                                            int idx_stride, int unit, int t0, int c, Pair (&out)[kGroup]) {
-    const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(x + (size_t)unit * T_ctx * D), 0,
-                                                     T_ctx * D * (int)sizeof(T), 0x00020000);
-    if (idx) {  // one branch per wave: the positions are read once, as scalars
-        const int32_t* ids = idx + (size_t)unit * idx_stride + t0;
-        int pos[kGroup];
-#pragma unroll
-        for (int t = 0; t < kGroup; ++t) pos[t] = ids[t];
-#pragma unroll
-        for (int t = 0; t < kGroup; ++t) out[t] = load_pair_buf<T>(r, (pos[t] * D + c) * (int)sizeof(T));
+        for (int q = 0; q < G::NI; ++q) pos[q] = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, (t0 + G::NI * r + q) * 4, 0, 0);
     } else {
 #pragma unroll
-        for (int t = 0; t < kGroup; ++t) out[t] = load_pair_buf<T>(r, ((t0 + t) * D + c) * (int)sizeof(T));
+        for (int q = 0; q < G::NI; ++q) pos[q] = t0 + G::NI * r + q;
+    }
+    // each row is read once: non-temporal loads (cache policy nt) keep them from
+    // displacing other data in L2 / MALL
+#pragma unroll
+    for (int q = 0; q < G::NI; ++q)
+        X[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (pos[q] * D + G::EPC * c) * (int)sizeof(T), 0, 2));
+}
+
+// ---- combining the lanes that hold other rows of the same chunk ----
+// Those lanes differ in lane bits log2(CH) .. 5.  A permlane swap of two
+// registers A, B across lane bit 4 (16) or 5 (32) leaves the lanes with that
+// bit clear holding (own A, partner's A) and the others (partner's B, own B),
+// so one swap and one min / max reduce a pair of entries to one, each lane
+// keeping the entry its bit selects (a reduce-scatter); the same swap applied
+// to a value and a copy of it hands the entries back (an all-gather).  Bit 3
+// (only when CH = 8) is reduced in full by DPP.
+template <int B>  // lane bit 4 or 5
+__device__ __forceinline__ void swap_pair(float& a, float& b) {
+    if constexpr (B == 4) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        a = __uint_as_float(p[0]);
+        b = __uint_as_float(p[1]);
+    } else {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        a = __uint_as_float(p[0]);
+        b = __uint_as_float(p[1]);
+    }
+}
+// Entries i and i + N/2 (i < N/2) of mn / mx become entry i: the lanes with
+// bit B clear keep entry i's label, the others entry i + N/2's.
+template <int B, int N>
+__device__ __forceinline__ void scatter_stage(float (&mn)[N], float (&mx)[N]) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+        float a = mn[i], b = mn[i + N / 2];
+        swap_pair<B>(a, b);
+        mn[i] = fminf(a, b);
+        a = mx[i], b = mx[i + N / 2];
+        swap_pair<B>(a, b);
+        mx[i] = fmaxf(a, b);
+    }
+}
+// The inverse hand-back for one quantity: entries i (i < N) become entries i
+// (label with bit B clear) and i + N (bit B set).
+template <int B, int N, int M>
+__device__ __forceinline__ void gather_stage(float (&v)[M]) {
+    static_assert(M >= 2 * N, "room for the handed-back entries");
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        float a = v[i], b = v[i];
+        swap_pair<B>(a, b);
+        v[i] = a;
+        v[i + N] = b;
     }
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void pack_keys_full(
-    const T* __restrict__ k, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int gi, int unit,
-    uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz) {
-    const int lane = threadIdx.x % kWave;
-    const bool active = lane < D / 2;
-    const int c = 2 * (active ? lane : 0);
-    const int t0 = gi * kGroup;
-    Pair x[kGroup];
-    gather_full<T, D>(k, idx, T_ctx, pg.idx_stride, unit, t0, c, x);
-    float mn0 = x[0].a, mx0 = x[0].a, mn1 = x[0].b, mx1 = x[0].b;
+// Keys (quantised per channel over the group's cnt tokens).  Each lane folds
+// its EPC channels over its NI rows, the lanes of the same chunk combine, and
+// every lane derives its channels' parameters.  A token's codes for the
+// lane's channels are 2 EPC bits of the token's packed row; they are written
+// to the wave's staging area in the packed order and copied out as whole
+// 16-byte pieces (only rows below cnt).
+template <typename T, int D, bool kFull>
+__device__ __forceinline__ void pack_keys_tile(const u32x4 (&X)[Tile<T, D>::NI], int cnt, const PackGeom& pg, int gi,
+                                               int unit, int lane, uint8_t* __restrict__ stage,
+                                               uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz) {
+    using G = Tile<T, D>;
+    constexpr int EPC = G::EPC, NI = G::NI;
+    const int c = lane % G::CH, r = lane / G::CH;
+    float mn[EPC], mx[EPC];
 #pragma unroll
-    for (int t = 1; t < kGroup; ++t) {
-        mn0 = fminf(mn0, x[t].a); mx0 = fmaxf(mx0, x[t].a);
-        mn1 = fminf(mn1, x[t].b); mx1 = fmaxf(mx1, x[t].b);
+    for (int e = 0; e < EPC; ++e) {
+        mn[e] = kFull ? elem_once<T>(X[0], e) : INFINITY;
+        mx[e] = kFull ? mn[e] : -INFINITY;
+#pragma unroll
+        for (int q = kFull ? 1 : 0; q < NI; ++q) {
+            const float v = elem_once<T>(X[q], e);
+            const bool ok = kFull || NI * r + q < cnt;
+            mn[e] = fminf(mn[e], ok ? v : INFINITY);
+            mx[e] = fmaxf(mx[e], ok ? v : -INFINITY);
+        }
+        if constexpr (G::CH <= 8) {  // lane bit 3: row_ror:8
+            mn[e] = fminf(mn[e], __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, mn[e]), 0x128, 0xF, 0xF, false)));
+            mx[e] = fmaxf(mx[e], __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, mx[e]), 0x128, 0xF, 0xF, false)));
+        }
     }
-    const GroupParams p0 = group_params(mn0, mx0);
-    const GroupParams p1 = group_params(mn1, mx1);
-    if (active) *reinterpret_cast<uint2*>(k_sz + ((size_t)unit * pg.grp_stride + pg.tok0 / kGroup + gi) * D + c) = make_uint2(p0.word, p1.word);
-    // Token t's word for channel block lane / 8 is kept by the lane with lane % 8 == t % 8.
-    uint32_t kw[kGroup / 8] = {0u, 0u, 0u, 0u};
+    // Reduce-scatter over lane bits 4 (when CH <= 16) and 5: the lane ends with
+    // NE channels, entry i being channel i + (EPC / 4) b5 + (EPC / 2) b4 (both
+    // stages) or i + (EPC / 2) b5 (bit 5 only), b4 / b5 its lane bits.
+    constexpr bool kB4 = G::CH <= 16;
+    constexpr int NE = kB4 ? EPC / 4 : EPC / 2;
+    static_assert(NE >= 1, "a lane keeps at least one channel");
+    float zz[EPC], h1[EPC], h2[EPC], h3[EPC];
+    {
+        float m1[EPC / 2], x1[EPC / 2];
+        if constexpr (kB4) {
+            scatter_stage<4, EPC>(mn, mx);
 #pragma unroll
-    for (int t = 0; t < kGroup; ++t) {
-        const uint32_t nib = code_of(x[t].a, p0) | (code_of(x[t].b, p1) << 2);
-        const uint32_t word = or8(nib << (4 * (lane & 7)));
-        kw[t / 8] = (lane & 7) == (t & 7) ? word : kw[t / 8];
+            for (int i = 0; i < EPC / 2; ++i) { m1[i] = mn[i]; x1[i] = mx[i]; }
+            scatter_stage<5, EPC / 2>(m1, x1);
+        } else {
+            scatter_stage<5, EPC>(mn, mx);
+#pragma unroll
+            for (int i = 0; i < EPC / 2; ++i) { m1[i] = mn[i]; x1[i] = mx[i]; }
+        }
+        const int b4 = (lane >> 4) & 1, b5 = lane >> 5;
+        const int first = kB4 ? (EPC / 4) * b5 + (EPC / 2) * b4 : (EPC / 2) * b5;  // channel of entry 0
+        uint32_t words[NE];
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const GroupParams p = group_params(m1[i], x1[i]);
+            words[i] = p.word;
+            zz[i] = p.z;
+            h1[i] = p.h1;
+            h2[i] = p.h2;
+            h3[i] = p.h3;
+        }
+        uint32_t* dst = k_sz + ((size_t)unit * pg.grp_stride + pg.tok0 / kGroup + gi) * D + EPC * c + first;
+        if constexpr (NE == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(words[0], words[1]);
+        else dst[0] = words[0];
     }
-    uint8_t* crow = k_codes + ((size_t)unit * pg.tok_stride + pg.tok0 + t0) * (D / 4);
-    if (active) {
+    // All-gather the code thresholds back to every lane of the chunk (bit 5, then bit 4).
+    gather_stage<5, NE>(zz);
+    gather_stage<5, NE>(h1);
+    gather_stage<5, NE>(h2);
+    gather_stage<5, NE>(h3);
+    if constexpr (kB4) {
+        gather_stage<4, 2 * NE>(zz);
+        gather_stage<4, 2 * NE>(h1);
+        gather_stage<4, 2 * NE>(h2);
+        gather_stage<4, 2 * NE>(h3);
+    }
+    GroupParams pk[EPC];
 #pragma unroll
-        for (int m = 0; m < kGroup / 8; ++m)
-            *reinterpret_cast<uint32_t*>(crow + (size_t)(8 * m + (lane & 7)) * (D / 4) + 4 * (lane >> 3)) = kw[m];
+    for (int e = 0; e < EPC; ++e) {
+        pk[e].z = zz[e];
+        pk[e].h1 = h1[e];
+        pk[e].h2 = h2[e];
+        pk[e].h3 = h3[e];
+    }
+    // token q's codes: channel e in bits 2e .. 2e + 1 of a 2 EPC-bit field
+    constexpr int FB = 2 * EPC;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+        uint32_t f = 0u;
+#pragma unroll
+        for (int e = EPC - 1; e >= 0; --e) f = push_code(f, code_of(elem<T>(X[q], e), pk[e]));
+        uint8_t* dst = stage + (NI * r + q) * (D / 4) + c * (FB / 8);
+        if constexpr (FB == 16) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f;
+        else *dst = (uint8_t)f;
+    }
+    constexpr int BYTES = kGroup * D / 4;  // the group's packed rows
+    if (16 * lane < BYTES && 16 * lane < cnt * (D / 4)) {
+        const uint4 w = *reinterpret_cast<const uint4*>(stage + 16 * lane);
+        *reinterpret_cast<uint4*>(k_codes + ((size_t)unit * pg.tok_stride + pg.tok0 + gi * kGroup) * (D / 4) + 16 * lane) = w;
     }
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void pack_values_full(
-    const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, const PackGeom& pg, int gi, int unit,
-    uint8_t* __restrict__ v_codes, uint32_t* __restrict__ v_sz) {
-    const int lane = threadIdx.x % kWave;
-    const bool active = lane < D / 2;
-    const int c = 2 * (active ? lane : 0);
-    const int t0 = gi * kGroup;
-    Pair x[kGroup];
-    gather_full<T, D>(v, idx, T_ctx, pg.idx_stride, unit, t0, c, x);
-    // Every 16-lane row (32 channels) reduces each token's min / max so that
-    // the lane with lane % 16 == j ends with those of tokens j and j + 16
-    // (a reduce-scatter), derives their parameters once, and the row reads them
-    // back by DPP broadcast, instead of all 16 lanes deriving every token's.
-    float mn[kGroup], mx[kGroup];
+// Values (quantised per token over 32-channel groups).  A group is GC = 32 / EPC
+// neighbouring lanes of one row; each lane folds its EPC channels per token,
+// the GC lanes combine by DPP, and every lane derives its rows' parameters.
+// A channel's codes over the lane's rows are 2 NI bits of the channel's 64-bit
+// word (token t at bits 2t); they are written to the staging area in the
+// packed order (all D channels of the block, tokens past cnt as code 0) and
+// copied out as 16-byte pieces, the scale / zero words likewise (rows below cnt).
+template <typename T, int D, bool kFull>
+__device__ __forceinline__ void pack_values_tile(const u32x4 (&X)[Tile<T, D>::NI], int cnt, const PackGeom& pg,
+                                                 int gi, int unit, int lane, uint8_t* __restrict__ stage,
+                                                 uint8_t* __restrict__ v_codes, uint32_t* __restrict__ v_sz) {
+    using G = Tile<T, D>;
+    constexpr int EPC = G::EPC, NI = G::NI, GC = kGroup / EPC, NG = D / kGroup;
+    const int c = lane % G::CH, r = lane / G::CH;
+    // Rows one at a time: the token's minimum / maximum, parameters and codes;
+    // channel e's field f[e] takes token q's code in bits 2q .. 2q + 1 (2 NI-bit
+    // fields; rows are pushed from the last, so bits fill from the top).
+    constexpr int FB = 2 * NI;
+    uint32_t* sz_stage = reinterpret_cast<uint32_t*>(stage + D * 8);
+    uint32_t f[EPC];
 #pragma unroll
-    for (int t = 0; t < kGroup; ++t) {
-        mn[t] = fminf(x[t].a, x[t].b);
-        mx[t] = fmaxf(x[t].a, x[t].b);
+    for (int e = 0; e < EPC; ++e) f[e] = 0u;
+#pragma unroll
+    for (int q = NI - 1; q >= 0; --q) {
+        float mn = elem<T>(X[q], 0), mx = mn;
+#pragma unroll
+        for (int e = 1; e < EPC; ++e) {
+            mn = fminf(mn, elem<T>(X[q], e));
+            mx = fmaxf(mx, elem<T>(X[q], e));
+        }
+        mn = dpp_min<GC>(mn);
+        mx = dpp_max<GC>(mx);
+        const GroupParams p = group_params(mn, mx);
+        if (c % GC == 0) sz_stage[(NI * r + q) * NG + c / GC] = p.word;
+        const uint64_t valid = kFull ? ~0ull : __builtin_amdgcn_ballot_w64(NI * r + q < cnt);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+            Code cd = code_of(elem<T>(X[q], e), p);
+            cd.hi &= valid;
+            cd.lo &= valid;
+            f[e] = push_code(f[e], cd);
+        }
     }
-    row_reduce_scatter(mn, mx, lane);
-    const float own_mn[2] = {mn[0], mn[16]}, own_mx[2] = {mx[0], mx[16]};
-    const GroupParams own[2] = {group_params(own_mn[0], own_mx[0]), group_params(own_mn[1], own_mx[1])};
-    uint32_t wa[2] = {0u, 0u}, wb[2] = {0u, 0u};
-    const uint32_t vw[2] = {own[0].word, own[1].word};  // token 16 h + lane % 16 of row lane / 16
-    static_for<0, kGroup>([&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        GroupParams p;
-        p.z = row_bcast<t & 15>(own[t / 16].z);
-        p.h1 = row_bcast<t & 15>(own[t / 16].h1);
-        p.h2 = row_bcast<t & 15>(own[t / 16].h2);
-        p.h3 = row_bcast<t & 15>(own[t / 16].h3);
-        wa[t / 16] |= code_of(x[t].a, p) << (2 * (t % 16));
-        wb[t / 16] |= code_of(x[t].b, p) << (2 * (t % 16));
-    });
-    if (active) {
-        *reinterpret_cast<uint4*>(v_codes + (((size_t)unit * pg.grp_stride + pg.tok0 / kGroup + gi) * D + c) * 8) = make_uint4(wa[0], wa[1], wb[0], wb[1]);
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-            v_sz[((size_t)unit * pg.tok_stride + pg.tok0 + t0 + 16 * h + (lane & 15)) * (D / 32) + (lane >> 4)] = vw[h];
+    for (int e = 0; e < EPC; ++e) {
+        uint8_t* dst = stage + (EPC * c + e) * 8 + r * (FB / 8);
+        if constexpr (FB == 32) *reinterpret_cast<uint32_t*>(dst) = f[e];
+        else if constexpr (FB == 16) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f[e];
+        else *dst = (uint8_t)f[e];
+    }
+    if (16 * lane < D * 8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(stage + 16 * lane);
+        *reinterpret_cast<uint4*>(v_codes + ((size_t)unit * pg.grp_stride + pg.tok0 / kGroup + gi) * D * 8 + 16 * lane) = w;
+    }
+    if (lane < cnt) {  // token `lane`'s NG words
+        uint32_t* dst = v_sz + ((size_t)unit * pg.tok_stride + pg.tok0 + gi * kGroup + lane) * NG;
+        if constexpr (NG == 4) *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(sz_stage + lane * NG);
+        else *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(sz_stage + lane * NG);
     }
 }
+
+// Bytes of one wave's staging area: packed codes of a group (8 D) and, for
+// values, its scale / zero words (4 D).
+template <int D>
+constexpr int kStageBytes = 12 * D;
 
 // One workgroup per (group of 32 kept tokens, KV head, sequence): wave 0 packs
 // the keys, wave 1 the values.
@@ -354,15 +406,20 @@ __global__ __launch_bounds__(128) void quant_pack_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ idx, int T_ctx, PackGeom pg,
     int Hkv, uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz, uint8_t* __restrict__ v_codes,
     uint32_t* __restrict__ v_sz) {
-    const bool full = (blockIdx.x + 1) * kGroup <= pg.n;
+    __shared__ __align__(16) uint8_t stage[2][kStageBytes<D>];
     const int gi = blockIdx.x;
+    const int cnt = min(kGroup, pg.n - gi * kGroup);
     const int unit = blockIdx.z * Hkv + blockIdx.y;
-    if (threadIdx.x < kWave) {
-        if (full) pack_keys_full<T, D>(k, idx, T_ctx, pg, gi, unit, k_codes, k_sz);
-        else pack_keys<T, D>(k, idx, T_ctx, pg, gi, unit, k_codes, k_sz);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    u32x4 X[Tile<T, D>::NI];
+    load_tile<T, D>(wave == 0 ? k : v, idx, T_ctx, pg, unit, gi * kGroup, lane, X);
+    // full groups (all but a call's last) take the branch-free instance
+    if (wave == 0) {
+        if (cnt == kGroup) pack_keys_tile<T, D, true>(X, cnt, pg, gi, unit, lane, stage[0], k_codes, k_sz);
+        else pack_keys_tile<T, D, false>(X, cnt, pg, gi, unit, lane, stage[0], k_codes, k_sz);
     } else {
-        if (full) pack_values_full<T, D>(v, idx, T_ctx, pg, gi, unit, v_codes, v_sz);
-        else pack_values<T, D>(v, idx, T_ctx, pg, gi, unit, v_codes, v_sz);
+        if (cnt == kGroup) pack_values_tile<T, D, true>(X, cnt, pg, gi, unit, lane, stage[1], v_codes, v_sz);
+        else pack_values_tile<T, D, false>(X, cnt, pg, gi, unit, lane, stage[1], v_codes, v_sz);
     }
 }
 
@@ -381,8 +438,9 @@ __global__ __launch_bounds__(128) void stream_step_append_kernel(
     uint8_t* __restrict__ k_codes, uint32_t* __restrict__ k_sz, uint8_t* __restrict__ v_codes,
     uint32_t* __restrict__ v_sz) {
     constexpr int W = D / 2;  // dwords per bf16 row
+    __shared__ __align__(16) uint8_t stage[2][kStageBytes<D>];
     const int unit = blockIdx.z * Hkv + blockIdx.y;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int n_packed = counts[0], n_res = counts[1], flag = counts[2];
     const bool ok = flag == 0 && n_res >= 0 && n_res < kGroup && n_packed >= 0 && n_packed % kGroup == 0 &&
                     n_packed <= cap;
@@ -396,8 +454,10 @@ __global__ __launch_bounds__(128) void stream_step_append_kernel(
     __syncthreads();  // the new row is visible to both waves
     if (pack) {
         const PackGeom pg{kGroup, kGroup, cap, cap / kGroup, n_packed};
-        if (wave == 0) pack_keys_full<uint16_t, D>(k_res, nullptr, kGroup, pg, 0, unit, k_codes, k_sz);
-        else pack_values_full<uint16_t, D>(v_res, nullptr, kGroup, pg, 0, unit, v_codes, v_sz);
+        u32x4 X[Tile<uint16_t, D>::NI];
+        load_tile<uint16_t, D>(wave == 0 ? k_res : v_res, nullptr, kGroup, pg, unit, 0, lane, X);
+        if (wave == 0) pack_keys_tile<uint16_t, D, true>(X, kGroup, pg, 0, unit, lane, stage[0], k_codes, k_sz);
+        else pack_values_tile<uint16_t, D, true>(X, kGroup, pg, 0, unit, lane, stage[1], v_codes, v_sz);
     }
     __syncthreads();
     if (threadIdx.x == 0) {
