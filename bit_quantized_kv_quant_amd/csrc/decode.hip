@@ -245,14 +245,33 @@ __device__ __forceinline__ void ticket_merge(float (*s_tp)[R][D + 2], int* s_las
     if (threadIdx.x == 0) *s_last = atomicAdd(&tickets[unit], 1) == nwg - 1;
     __syncthreads();
     if (!*s_last) return;
-    // every part's (m, sum) in one round of loads, into LDS (nwg * R <= 252
-    // pairs; the LDS parts above are no longer needed), then the weights
-    float* s_ml = &s_tp[0][0][0];
+    // One round of loads for everything the merge reads: every part's (m, sum)
+    // (nwg * R <= 64 pairs, one per thread) and, per thread, its outputs' nwg
+    // partial sums (at most kTicketMaxWorkgroups parts of ITER outputs); the
+    // weights need the maximum over parts first, so the pairs go through LDS
+    // (the LDS parts above are no longer needed).
+    constexpr int ITER = (R * D + NTH - 1) / NTH;
+    static_assert(kTicketMaxWorkgroups <= 8, "one batch of part loads");
     const size_t base = (size_t)unit * nwg * R;
-    for (int i = threadIdx.x; i < nwg * R; i += NTH) {
-        const float m = ld_dev(&ws_ml[(base + i) * 2]), l = ld_dev(&ws_ml[(base + i) * 2 + 1]);
-        s_ml[2 * i] = m;
-        s_ml[2 * i + 1] = l;
+    float m_i = 0.0f, l_i = 0.0f;
+    const bool has_ml = (int)threadIdx.x < nwg * R;
+    if (has_ml) {
+        m_i = ld_dev(&ws_ml[(base + threadIdx.x) * 2]);
+        l_i = ld_dev(&ws_ml[(base + threadIdx.x) * 2 + 1]);
+    }
+    float a[ITER][8];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int i = threadIdx.x + it * NTH;
+        const int r = i / D, c = i % D;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            a[it][j] = (i < R * D && j < nwg) ? ld_dev(&ws_acc[(base + (size_t)j * R + r) * D + c]) : 0.0f;
+    }
+    float* s_ml = &s_tp[0][0][0];
+    if (has_ml) {
+        s_ml[2 * threadIdx.x] = m_i;
+        s_ml[2 * threadIdx.x + 1] = l_i;
     }
     __syncthreads();
     for (int i = threadIdx.x; i < nwg * R; i += NTH) {  // weight of part i against its head's maximum
@@ -263,21 +282,18 @@ __device__ __forceinline__ void ticket_merge(float (*s_tp)[R][D + 2], int* s_las
     }
     __syncthreads();
     const float* s_f = s_ml + 2 * nwg * R;
-    for (int i = threadIdx.x; i < R * D; i += NTH) {
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int i = threadIdx.x + it * NTH;
+        if (i >= R * D) break;
         const int r = i / D, c = i % D;
         float L = 0.0f, O = 0.0f;
-        for (int w0 = 0; w0 < nwg; w0 += 8) {  // eight parts' loads in flight at once
-            float a[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                a[j] = w0 + j < nwg ? ld_dev(&ws_acc[(base + (size_t)(w0 + j) * R + r) * D + c]) : 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (w0 + j < nwg) {
-                    const int pi = (w0 + j) * R + r;
-                    L = fmaf(s_ml[2 * pi + 1], s_f[pi], L);
-                    O = fmaf(a[j], s_f[pi], O);
-                }
+        for (int j = 0; j < 8; ++j) {
+            if (j < nwg) {
+                const int pi = j * R + r;
+                L = fmaf(s_ml[2 * pi + 1], s_f[pi], L);
+                O = fmaf(a[it][j], s_f[pi], O);
             }
         }
         out[((size_t)unit * R + r) * D + c] = (__bf16)(O / L);
