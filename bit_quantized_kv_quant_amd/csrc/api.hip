@@ -16,6 +16,10 @@ float resolve_scale(float sm_scale, int D) { return sm_scale > 0.0f ? sm_scale :
 
 bool supported_d(int D) { return D == 64 || D == 128; }
 
+// The kernels address one (sequence, head) slice of K / V (T rows of D
+// elements) through a 32-bit buffer range, so its bytes must stay below 2 GiB.
+bool slice_fits(int T, int D, int elem_bytes) { return (long long)T * D * elem_bytes <= 0x7fffffffLL; }
+
 }  // namespace
 
 extern "C" {
@@ -83,7 +87,7 @@ namespace {
 int check_prefill_args(const void* q, const void* k, const void* v, int B, int T, int Hq, int Hkv, int D) {
     if (!q || !k || !v) return MINIKV_ERR_NULL;
     if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return MINIKV_ERR_SHAPE;
-    if (!supported_d(D)) return MINIKV_ERR_UNSUPPORTED;
+    if (!supported_d(D) || !slice_fits(T, D, 2)) return MINIKV_ERR_UNSUPPORTED;
     if (misaligned(q) || misaligned(k) || misaligned(v)) return MINIKV_ERR_ALIGN;
     return MINIKV_OK;
 }
@@ -161,6 +165,7 @@ int minikv_quant_pack(const void* k, const void* v, int in_dtype, const int32_t*
     if (!idx && n_keep != T) return MINIKV_ERR_SHAPE;
     if (!supported_d(D) || out->group != MINIKV_GROUP) return MINIKV_ERR_UNSUPPORTED;
     if (in_dtype != MINIKV_F32 && in_dtype != MINIKV_BF16) return MINIKV_ERR_UNSUPPORTED;
+    if (!slice_fits(T, D, in_dtype == MINIKV_BF16 ? 2 : 4)) return MINIKV_ERR_UNSUPPORTED;
     if (misaligned(k) || misaligned(v) || (idx && misaligned(idx)) || misaligned(out->k_codes) ||
         misaligned(out->k_sz) || misaligned(out->v_codes) || misaligned(out->v_sz))
         return MINIKV_ERR_ALIGN;
@@ -224,6 +229,7 @@ int minikv_stream_pack(const void* k, const void* v, int in_dtype, const int32_t
     if (idx ? idx_stride < n : n > T) return MINIKV_ERR_SHAPE;
     if (!supported_d(D)) return MINIKV_ERR_UNSUPPORTED;
     if (in_dtype != MINIKV_F32 && in_dtype != MINIKV_BF16) return MINIKV_ERR_UNSUPPORTED;
+    if (!slice_fits(T, D, in_dtype == MINIKV_BF16 ? 2 : 4)) return MINIKV_ERR_UNSUPPORTED;
     if (misaligned(k) || misaligned(v) || misaligned(k_codes) || misaligned(k_sz) || misaligned(v_codes) ||
         misaligned(v_sz))
         return MINIKV_ERR_ALIGN;
@@ -236,7 +242,7 @@ int minikv_stream_append(const void* k, const void* v, const int32_t* idx, int i
     if (!k || !v || !k_res || !v_res) return MINIKV_ERR_NULL;
     if (B < 1 || Hkv < 1 || T < 1 || n < 1 || slot < 0 || slot + n > MINIKV_GROUP) return MINIKV_ERR_SHAPE;
     if (idx ? idx_stride < n : n > T) return MINIKV_ERR_SHAPE;
-    if (!supported_d(D)) return MINIKV_ERR_UNSUPPORTED;
+    if (!supported_d(D) || !slice_fits(T, D, 2)) return MINIKV_ERR_UNSUPPORTED;
     if (misaligned(k) || misaligned(v) || misaligned(k_res) || misaligned(v_res)) return MINIKV_ERR_ALIGN;
     return status_of(minikv::launch_stream_append(k, v, idx, idx ? idx_stride : n, B, Hkv, T, D, n, slot, k_res,
                                                   v_res, as_stream(stream)));
@@ -252,7 +258,7 @@ int minikv_stream_init(const void* k, const void* v, const int32_t* idx, int B, 
     // whole 32-token groups are packed; the rest (at most 31) wait in the window
     const int pk = MINIKV_GROUP * (n_keep / MINIKV_GROUP), rest = n_keep - pk;
     if (pk > cap) return MINIKV_ERR_SHAPE;
-    if (!supported_d(D)) return MINIKV_ERR_UNSUPPORTED;
+    if (!supported_d(D) || !slice_fits(T, D, 2)) return MINIKV_ERR_UNSUPPORTED;
     if (misaligned(k) || misaligned(v) || misaligned(idx) || misaligned(k_codes) || misaligned(k_sz) ||
         misaligned(v_codes) || misaligned(v_sz) || misaligned(k_res) || misaligned(v_res))
         return MINIKV_ERR_ALIGN;

@@ -29,6 +29,10 @@
  *    overlap.
  *  - Preconditions not checked on the device: inputs are finite and
  *    |x| < 65504 (scales and zeros are stored in fp16).
+ *  - One (sequence, head) slice of K or V, T rows of D elements, is at most
+ *    2^31 - 1 bytes (the kernels address it through a 32-bit buffer range):
+ *    T <= 8,388,607 for bf16 and 4,194,303 for fp32 at D = 128.  Calls that
+ *    take such a slice return UNSUPPORTED beyond it.
  */
 #ifndef MINIKV_H
 #define MINIKV_H
@@ -104,7 +108,8 @@ typedef struct {
  * minikv_window_scores.  Otherwise it enqueues the two passes.
  * sm_scale <= 0 means 1/sqrt(D).
  * Errors: NULL q/k/v/lse/scores; SHAPE if any size < 1, Hq % Hkv, W > T;
- * UNSUPPORTED if D is not 64 or 128; ALIGN; LAUNCH.
+ * UNSUPPORTED if D is not 64 or 128 or a K / V slice exceeds 2 GiB; ALIGN;
+ * LAUNCH.
  * minikv_prefill_fuses_scores returns 1 or 0 (0 for invalid sizes too); its
  * only HIP call is a query of the current device's compute-unit count (256
  * is assumed when there is no device).
@@ -156,8 +161,9 @@ size_t minikv_select_ws_bytes(int B, int Hkv, int T);
  *   code = s == 0 ? 0 : clamp(rint(fl32(x - z) / s), 0, 3)
  * with the stored fp16 s, z; a short last K group uses its valid tokens only.
  * Errors: NULL; SHAPE (sizes < 1, n_keep > T, out->B/Hkv/n_keep/D mismatch,
- * idx NULL with n_keep != T); UNSUPPORTED (D, group != 32, in_dtype); ALIGN;
- * LAUNCH.  idx entries outside [0, T) are not checked on the device.
+ * idx NULL with n_keep != T); UNSUPPORTED (D, group != 32, in_dtype, a K / V
+ * slice over 2 GiB); ALIGN; LAUNCH.  idx entries outside [0, T) are not
+ * checked on the device (such rows read as zeros).
  */
 int minikv_quant_pack(const void *k, const void *v, int in_dtype, const int32_t *idx,
                       int B, int Hkv, int T, int D, int n_keep,
@@ -233,7 +239,7 @@ int minikv_decode_attn_noalloc(const void *q, const minikv_packed_t *cache, int 
  * depend on where they are placed.
  * Errors: NULL; SHAPE (sizes < 1, n or tok0 not multiples of 32, tok0 + n > cap,
  * cap not a multiple of 32, idx_stride < n, n > T with idx NULL);
- * UNSUPPORTED (D, in_dtype); ALIGN; LAUNCH.
+ * UNSUPPORTED (D, in_dtype, a K / V slice over 2 GiB); ALIGN; LAUNCH.
  */
 int minikv_stream_pack(const void *k, const void *v, int in_dtype, const int32_t *idx, int idx_stride,
                        int B, int Hkv, int T, int D, int n, int cap, int tok0,
@@ -244,7 +250,8 @@ int minikv_stream_pack(const void *k, const void *v, int in_dtype, const int32_t
  * Copy n bf16 tokens into residual slots slot .. slot+n-1 (slot + n <= 32) of
  * k_res, v_res bf16 [B][Hkv][32][D]: rows idx[b][g][j] (row stride idx_stride)
  * of k, v bf16 [B][Hkv][T][D], or rows 0..n-1 with idx NULL (a generated token:
- * T = 1, n = 1).  Errors: NULL; SHAPE; UNSUPPORTED (D); ALIGN; LAUNCH.
+ * T = 1, n = 1).  Errors: NULL; SHAPE; UNSUPPORTED (D, a K / V slice over
+ * 2 GiB); ALIGN; LAUNCH.
  */
 int minikv_stream_append(const void *k, const void *v, const int32_t *idx, int idx_stride,
                          int B, int Hkv, int T, int D, int n, int slot,
@@ -278,7 +285,7 @@ size_t minikv_stream_decode_ws_bytes(int B, int Hq, int Hkv, int n_packed, int n
  * n_keep mod 32 are copied into window slots 0.., and *n_packed, *n_res are
  * set to those two counts.  Errors: NULL (any pointer); SHAPE (sizes < 1,
  * n_keep > T, cap not a positive multiple of 32, the packed part > cap);
- * UNSUPPORTED (D); ALIGN; LAUNCH.  On an error nothing is enqueued (LAUNCH
+ * UNSUPPORTED (D, a K / V slice over 2 GiB); ALIGN; LAUNCH.  On an error nothing is enqueued (LAUNCH
  * aside) and the counts are unchanged.
  *
  * minikv_stream_append_token appends k_new, v_new bf16 [B][Hkv][D] into window

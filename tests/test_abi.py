@@ -66,6 +66,10 @@ def test_prefill_validation(L):
     assert call(W=257) == _lib.ERR_SHAPE
     assert call(W=0) == _lib.ERR_SHAPE
     assert call(D=96) == _lib.ERR_UNSUPPORTED
+    # one (sequence, head) slice of K / V over 2 GiB (8,388,608 bf16 rows of 128)
+    assert call(T=1 << 23, D=128) == _lib.ERR_UNSUPPORTED
+    assert L.minikv_window_scores(A, A, A, 1, 1 << 23, 2, 2, 128, 16, 0.0, A, None) == _lib.ERR_UNSUPPORTED
+    assert L.minikv_prefill_attn(A, A, A, 1, 1 << 24, 2, 2, 64, 0.0, A, A, None) == _lib.ERR_UNSUPPORTED
     assert call(k=MIS) == _lib.ERR_ALIGN
     assert call(o=MIS) == _lib.ERR_ALIGN
 
@@ -121,6 +125,7 @@ def test_stream_init_validation(L):
     assert call(cap=64) == _lib.ERR_SHAPE          # 96 packed tokens do not fit 64
     assert call(n=127, cap=64) == _lib.ERR_SHAPE   # 96 packed + 31 in the window: too many
     assert call(D=96) == _lib.ERR_UNSUPPORTED
+    assert call(T=1 << 23) == _lib.ERR_UNSUPPORTED  # a bf16 K / V slice over 2 GiB
     assert call(kr=MIS) == _lib.ERR_ALIGN
     assert (npk.value, nres.value) == (-7, -7)     # rejected calls leave the counts alone
 
@@ -166,6 +171,9 @@ def test_quant_pack_validation(L):
     assert f(A, MIS, _lib.BF16, A, 1, 1, 256, 128, 64, byref(p), None) == _lib.ERR_ALIGN
     pm = packed(ptr=MIS)
     assert f(A, A, _lib.BF16, A, 1, 1, 256, 128, 64, byref(pm), None) == _lib.ERR_ALIGN
+    # a K / V slice over 2 GiB: 4,194,304 fp32 rows or 8,388,608 bf16 rows of 128
+    assert f(A, A, _lib.F32, A, 1, 1, 1 << 22, 128, 64, byref(p), None) == _lib.ERR_UNSUPPORTED
+    assert f(A, A, _lib.BF16, A, 1, 1, 1 << 23, 128, 64, byref(p), None) == _lib.ERR_UNSUPPORTED
 
 
 def test_decode_validation(L):
@@ -209,6 +217,8 @@ def test_stream_pack_validation(L):
     assert call(idx=None, T=32) == _lib.ERR_SHAPE  # identity rows beyond T
     assert call(D=96) == _lib.ERR_UNSUPPORTED
     assert call(dtype=7) == _lib.ERR_UNSUPPORTED
+    assert call(T=1 << 23) == _lib.ERR_UNSUPPORTED                 # bf16 K / V slice over 2 GiB
+    assert call(T=1 << 22, dtype=_lib.F32) == _lib.ERR_UNSUPPORTED  # fp32 likewise
     assert call(k=MIS) == _lib.ERR_ALIGN
     assert call(k_codes=MIS) == _lib.ERR_ALIGN
     assert len(args) == 17
@@ -223,6 +233,7 @@ def test_stream_append_validation(L):
     assert f(A, A, A, 4, 2, 4, 600, 128, 8, 0, A, A, None) == _lib.ERR_SHAPE     # idx stride < n
     assert f(A, A, None, 1, 2, 4, 1, 128, 2, 0, A, A, None) == _lib.ERR_SHAPE    # 2 rows of a 1-row source
     assert f(A, A, None, 1, 2, 4, 1, 96, 1, 0, A, A, None) == _lib.ERR_UNSUPPORTED
+    assert f(A, A, A, 8, 2, 4, 1 << 23, 128, 8, 0, A, A, None) == _lib.ERR_UNSUPPORTED  # K / V slice over 2 GiB
     assert f(A, MIS, None, 1, 2, 4, 1, 128, 1, 0, A, A, None) == _lib.ERR_ALIGN
 
 
