@@ -60,6 +60,25 @@ def test_quant_pack_bf16_ragged(dev, n):
     _pack_and_compare(kd, vd, idx, dev)
 
 
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("n,T,with_idx", [(5, 40, True), (70, 70, False), (161, 500, True)])
+def test_quant_pack_each_tile_shape(dev, dtype, D, n, T, with_idx):
+    """Every load tile of the pack kernel: fp32 and bf16 rows of 64 and 128
+    channels (16-byte chunks of 4 or 8 channels, 2 to 8 rows per load
+    instruction), full and partial groups, gathered and identity rows."""
+    say("quant_pack tile", dtype, "D", D, "n", n, "T", T, "idx", with_idx)
+    rng = np.random.default_rng(1000 * D + n)
+    k = rng.standard_normal((2, 3, T, D)).astype(np.float32) * 2
+    k[..., 5] *= 30.0                                     # an outlier channel
+    v = rng.standard_normal((2, 3, T, D)).astype(np.float32)
+    idx = (np.sort(np.stack([[rng.choice(T, n, replace=False) for _ in range(3)] for _ in range(2)]), -1)
+           if with_idx else None)
+    kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    if dtype == "bf16":
+        kd, vd = kd.to(torch.bfloat16), vd.to(torch.bfloat16)
+    _pack_and_compare(kd, vd, idx, dev, f"tile {dtype} D{D} n{n}")
+
+
 def test_quant_pack_special_groups(dev):
     """Constant groups, exact ties, fp16 zero rounding up, subnormal and vanishing scales."""
     say("quant_pack special groups fp32 D64")
