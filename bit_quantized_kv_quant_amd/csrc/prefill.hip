@@ -10,10 +10,13 @@
 // probabilities without storing any T x T matrix.
 //
 // gfx950 design: a workgroup of 8 waves owns 256 query rows (32 per wave) and
-// streams 64-key tiles of K and V through two LDS stages (register-prefetched
-// one tile ahead for V and two for K; one barrier per tile).  Workgroups are ordered XCD-aware so the K/V prefix a head's query
-// blocks share stays in one L2.  Each wave software-pipelines its tiles: the
-// QK^T MFMAs of tile t+1 are issued while the softmax of tile t runs.  Each wave computes S^T = K Q^T with
+// streams 64-key tiles of K and V through two LDS stages (register-prefetched;
+// one barrier per tile).  Workgroups are ordered XCD-aware so the K/V prefix a
+// head's query blocks share stays in one L2.  Each wave software-pipelines its
+// tiles: while the softmax of tile t runs on the VALU, the matrix cores take
+// the PV product of tile t-1 and the QK^T product of tile t+1, one MFMA per
+// slot with a share of the vector work between them, so that the VALU and the
+// matrix cores of a SIMD work side by side.  Each wave computes S^T = K Q^T with
 // bf16 MFMA 32x32x16, so an accumulator column is one query: a lane owns the
 // softmax state (running max, partial sum) of its query, and the row max needs
 // one permlane32 swap.  P^T is already in the B-operand layout of the second
@@ -132,7 +135,7 @@ __device__ __forceinline__ void fa_block(
     const int goff0 = (row0 * D + col0) * 2;  // byte offset of chunk 0 inside a tile
     auto tile_rsrc = [&](const uint16_t* base, int n0) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + (kvbase + (size_t)n0) * D), 0,
-                                                 (T_ctx - n0) * D * 2, 0x00020000);
+                                                 max(T_ctx - n0, 0) * D * 2, 0x00020000);
     };
     auto load_k_into = [&](int n0, u32x4 (&dst)[LOADS]) {
         const auto rk = tile_rsrc(k, n0);
@@ -140,12 +143,13 @@ __device__ __forceinline__ void fa_block(
         for (int i = 0; i < LOADS; ++i)
             dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, goff0 + i * kRowStep * D * 2, 0, 0));
     };
+    auto store_k_part = [&](int buf, const u32x4 (&src)[LOADS], int i) {
+        const int r = row0 + kRowStep * i, c = col0 / 8;
+        *reinterpret_cast<u32x4*>(sK + buf * TILE + (32 * (r >> 5) + key_lane(r & 31)) * KST + 8 * c) = src[i];
+    };
     auto store_k_from = [&](int buf, const u32x4 (&src)[LOADS]) {
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int r = row0 + kRowStep * i, c = col0 / 8;
-            *reinterpret_cast<u32x4*>(sK + buf * TILE + (32 * (r >> 5) + key_lane(r & 31)) * KST + 8 * c) = src[i];
-        }
+        for (int i = 0; i < LOADS; ++i) store_k_part(buf, src, i);
     };
     auto load_k = [&](int n0) { load_k_into(n0, pk); };
     auto store_k = [&](int buf) { store_k_from(buf, pk); };
@@ -155,7 +159,7 @@ __device__ __forceinline__ void fa_block(
     // j = 16 bk + 8 half + 4 s + dw, and writes the eight fp16 pairs
     // (V[2j][8c+e], V[2j+1][8c+e]) as dwords of V^T rows 8c+e.
     const int vw = wave;
-    const bool v_active = vw < 4 * CH2;  // D = 64 needs half of the waves
+    const bool v_active = 4 * CH2 >= WAVES || vw < 4 * CH2;  // D = 64 needs half of the waves
     const int v_chi = vw % CH2, v_s = (vw / CH2) & 1, v_bk = (vw / CH2 / 2) & 1;
     const int v_clo = lane & 7, v_dw = (lane >> 3) & 3, v_half = lane >> 5;
     const int v_j = 16 * v_bk + 8 * v_half + 4 * v_s + v_dw;
@@ -172,20 +176,21 @@ __device__ __forceinline__ void fa_block(
         }
     };
 
-    auto store_v = [&](int buf) {
+    auto store_v_part = [&](int buf, int w) {
         if constexpr (kWithO) {
             if (v_active) {
                 char* dst = sV + buf * VT_BYTES + woffv;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const f16x2 lo = {(_Float16)__uint_as_float(pv[0][w] << 16), (_Float16)__uint_as_float(pv[1][w] << 16)};
-                    const f16x2 hi = {(_Float16)__uint_as_float(pv[0][w] & 0xFFFF0000u),
-                                      (_Float16)__uint_as_float(pv[1][w] & 0xFFFF0000u)};
-                    *reinterpret_cast<f16x2*>(dst + kVtLine * (2 * w)) = lo;
-                    *reinterpret_cast<f16x2*>(dst + kVtLine * (2 * w + 1)) = hi;
-                }
+                const f16x2 lo = {(_Float16)__uint_as_float(pv[0][w] << 16), (_Float16)__uint_as_float(pv[1][w] << 16)};
+                const f16x2 hi = {(_Float16)__uint_as_float(pv[0][w] & 0xFFFF0000u),
+                                  (_Float16)__uint_as_float(pv[1][w] & 0xFFFF0000u)};
+                *reinterpret_cast<f16x2*>(dst + kVtLine * (2 * w)) = lo;
+                *reinterpret_cast<f16x2*>(dst + kVtLine * (2 * w + 1)) = hi;
             }
         }
+    };
+    auto store_v = [&](int buf) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) store_v_part(buf, w);
     };
 
     // Softmax state of this lane's query, log2 domain.  m_ref is the reference
@@ -261,82 +266,209 @@ __device__ __forceinline__ void fa_block(
         lsum = fmaf(lsum, alpha, psum);
         return moved;
     };
-    // O^T += V^T P^T, one 32-wide block of the head dim at a time; the next
-    // block's V^T operands are requested before this block's MFMAs.
+
+    // this wave's diagonal tile, the last one it needs (wave-uniform)
+    const int t_last = __builtin_amdgcn_readfirstlane(min(qw0 / kBN, ntiles - 1));
+
+    // O^T += V^T P^T of the tile in stage `buf`, one 32-wide block of the head
+    // dim at a time (the order every accumulator takes its products in).
     auto pv_mma = [&](int buf, const f16x8 (&pb)[2][2]) {
         const char* tv = sV + buf * VT_BYTES + voff;
-        auto read_v = [&](int d, f16x8 (&av)[2][2]) {
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
 #pragma unroll
             for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    av[bk][s] = *reinterpret_cast<const f16x8*>(
+                for (int s = 0; s < 2; ++s) {
+                    const f16x8 a = *reinterpret_cast<const f16x8*>(
                         tv + kVtLine * 8 * ((bk * 2 + s) * CH2 + (d >> 1)) + 64 * (d & 1));
-        };
-        f16x8 va[2][2][2];
-        read_v(0, va[0]);
+                    oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[bk][s], oacc[d], 0, 0, 0);
+                }
+    };
+    auto rescale = [&](bool moved, float alpha) {
+        if constexpr (kWithO) {
+            if (__ballot(moved)) {  // wave-uniform, rare
 #pragma unroll
-        for (int d = 0; d < DB; ++d) {
-            if (d + 1 < DB) read_v(d + 1, va[(d + 1) & 1]);
+                for (int d = 0; d < DB; ++d)
 #pragma unroll
-            for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[d & 1][bk][s], pb[bk][s], oacc[d], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+                    for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+            }
         }
     };
 
-    // Software pipeline over the key tiles of this wave: while the softmax of
-    // tile t runs on the VALU, the QK^T MFMAs of tile t+1 are already issued
-    // (they read the other K stage), then tile t's PV MFMAs follow.  K is staged
-    // two tiles ahead, V one tile ahead.
-    const int t_last = __builtin_amdgcn_readfirstlane(min(qw0 / kBN, ntiles - 1));  // wave-uniform
-    {  // first two K tiles and the first V tile: all loads in flight at once
-        u32x4 pk1[LOADS];
-        load_k(0);
-        load_v(0);
-        if (ntiles > 1) load_k_into(kBN, pk1);
-        store_k(0);
-        store_v(0);
-        if (ntiles > 1) store_k_from(1, pk1);
-    }
-    __syncthreads();
-    f32x16 sacc[2];
-    qk(0, sacc);
-    for (int t = 0; t < ntiles; ++t) {
+    // Steady-state tile t (0 < t < this wave's diagonal tile): the PV product of
+    // tile t-1 (stage (t-1)&1, probabilities pbp) and the QK^T product of tile
+    // t+1 (stage (t+1)&1, into sn) go to the matrix cores one MFMA per slot,
+    // while the online softmax of tile t (sc, into pbn) is spread over the same
+    // slots on the VALU, as are the staging writes of V(t) and K(t+2) into stage
+    // t&1 and the loads of K(t+2) and V(t+1).  Scheduling barriers between the
+    // slots and empty asm statements that pin values to their slot keep that
+    // order; the arithmetic and its order are those of qk, softmax and pv_mma.
+    auto step_a = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2], const f16x8 (&pbp)[2][2], f16x8 (&pbn)[2][2]) {
         const int n0 = t * kBN;
         const int buf = t & 1;
-        if (t + 2 < ntiles) load_k(n0 + 2 * kBN);  // into registers; stored after this tile
-        if (t + 1 < ntiles) load_v(n0 + kBN);
+        const uint16_t* tk = sK + (buf ^ 1) * TILE + koff;
+        const char* tv = sV + (buf ^ 1) * VT_BYTES + voff;
+        constexpr int NM = 2 * KS;             // MFMAs of one QK^T (and of one PV)
+        constexpr int NPV = kWithO ? NM : 0;   // PV slots
+        constexpr int NS = NPV + NM;           // slots
+        constexpr int AHEAD = 4;               // operand reads in flight ahead of their MFMA
+        constexpr int MS = 3;                  // slots that take the row max
+        constexpr int ES = NS - MS;            // slots that take the exponentials
+        constexpr int VS0 = 1;                 // slots VS0..VS0+3 write V(t); V(t+1) is loaded after
+        constexpr int KS0 = NS - 1 - LOADS;    // slots that write K(t+2)
+        u32x4 op[NS];
+        auto read_op = [&](int r) {
+            if (r < NPV) {
+                const int bs = r / DB, d = r % DB, bk = bs >> 1, s = bs & 1;
+                op[r] = *reinterpret_cast<const u32x4*>(tv + kVtLine * 8 * ((bk * 2 + s) * CH2 + (d >> 1)) + 64 * (d & 1));
+            } else {
+                const int j = r - NPV;
+                op[r] = *reinterpret_cast<const u32x4*>(tk + 16 * (j % KS) + 32 * (j / KS) * KST);
+            }
+        };
+        auto pin = [](auto& x) { asm volatile("" : "+v"(x)); };
+        float tmax = -INFINITY, psum = 0.0f, alpha = 1.0f;
+        bool moved = false;
+        uint32_t pw[16];  // fp16 pairs of P(t)
+        __builtin_amdgcn_sched_barrier(0);
+        load_k(n0 + 2 * kBN);  // K(t+2); rows past the end read as zeros
+#pragma unroll
+        for (int r = 0; r < AHEAD; ++r) read_op(r);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            if (i + AHEAD < NS) read_op(i + AHEAD);
+            if (i < NPV) {
+                const int bs = i / DB, d = i % DB;
+                oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, op[i]), pbp[bs >> 1][bs & 1],
+                                                                 oacc[d], 0, 0, 0);
+            } else {
+                const int j = i - NPV;
+                if (j % KS == 0) sn[j / KS] = f32x16{};
+                sn[j / KS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, op[i]), qreg[j % KS],
+                                                                     sn[j / KS], 0, 0, 0);
+            }
+            if (i < MS) {
+#pragma unroll
+                for (int e = 32 * i / MS; e < 32 * (i + 1) / MS; ++e) tmax = fmaxf(tmax, sc[e >> 4][e & 15]);
+                if (i == MS - 1) {
+                    const float tm = fmaxf(tmax, swap_halves(tmax)) * scale_log2;
+                    const float m_new = tm > m_ref + 8.0f ? tm : m_ref;
+                    alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+                    moved = m_new != m_ref;
+                    m_ref = m_new;
+                    pin(m_ref);
+                }
+            } else {
+                const int jj = i - MS;
+                const int e0 = 32 * jj / ES, e1 = 32 * (jj + 1) / ES;
+#pragma unroll
+                for (int e = e0; e < e1; ++e) {
+                    float x = sc[e >> 4][e & 15];
+                    pin(x);
+                    sc[e >> 4][e & 15] = x;
+                }
+#pragma unroll
+                for (int e = e0; e < e1; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sc[e >> 4][e & 15], scale_log2, -m_ref));
+                    psum += p;
+                    sc[e >> 4][e & 15] = p;
+                    if (e & 1) {
+                        const f16x2 h = {(_Float16)sc[e >> 4][(e & 15) - 1], (_Float16)p};
+                        pw[e >> 1] = __builtin_bit_cast(uint32_t, h);
+                        pin(pw[e >> 1]);
+                    }
+                }
+                pin(psum);
+            }
+            if constexpr (kWithO) {
+                if (i >= VS0 && i < VS0 + 4) store_v_part(buf, i - VS0);  // V(t) -> stage t&1
+                if (i == VS0 + 4) load_v(n0 + kBN);                       // V(t+1)
+            }
+            if (i >= KS0 && i < KS0 + LOADS) store_k_part(buf, pk, i - KS0);  // K(t+2) -> stage t&1
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        lsum = fmaf(lsum, alpha, psum);
+#pragma unroll
+        for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+            for (int hs2 = 0; hs2 < 2; ++hs2)
+                pbn[bk][hs2] = __builtin_bit_cast(f16x8, u32x4{pw[8 * bk + 4 * hs2], pw[8 * bk + 4 * hs2 + 1],
+                                                              pw[8 * bk + 4 * hs2 + 2], pw[8 * bk + 4 * hs2 + 3]});
+        rescale(moved, alpha);
+    };
+
+    // Any other tile t, in plain order: PV(t-1), the staging of V(t) and the
+    // load of V(t+1), then the softmax of tile t (with the QK^T of tile t+1
+    // before the diagonal tile, masked on it), then the staging of K(t+2).
+    // Tile ntiles exists only for the PV of the last tile.
+    auto step_g = [&](int t, f32x16 (&sc)[2], f16x8 (&pb)[2][2]) {
+        const int n0 = t * kBN;
+        const int buf = t & 1;
+        if (t + 2 < ntiles) load_k(n0 + 2 * kBN);
+        if constexpr (kWithO) {
+            if (t >= 1 && t - 1 <= t_last) pv_mma(buf ^ 1, pb);
+            if (t < ntiles) store_v(buf);
+            if (t + 1 < ntiles) load_v(n0 + kBN);
+        }
         if (t <= t_last) {
-            f16x8 pb[2][2];
             bool moved;
-            float m_old = m_ref;
+            const float m_old = m_ref;
             if (t < t_last) {
                 f32x16 snext[2];
                 qk(buf ^ 1, snext);
-                moved = softmax(sacc, n0, std::false_type{}, pb);
-                sacc[0] = snext[0];
-                sacc[1] = snext[1];
+                moved = softmax(sc, n0, std::false_type{}, pb);
+                sc[0] = snext[0];
+                sc[1] = snext[1];
             } else {
-                moved = softmax(sacc, n0, std::true_type{}, pb);
+                moved = softmax(sc, n0, std::true_type{}, pb);
             }
-            if constexpr (kWithO) {
-                if (__ballot(moved)) {  // wave-uniform, rare
-                    const float alpha = __builtin_amdgcn_exp2f(m_old - m_ref);
-#pragma unroll
-                    for (int d = 0; d < DB; ++d)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
-                }
-                pv_mma(buf, pb);
-            }
+            rescale(moved, __builtin_amdgcn_exp2f(m_old - m_ref));
         }
-        // K(t)'s stage was consumed by the previous iteration's QK and V(t-1)'s
-        // stage by the previous PV, so both are free: one barrier per tile.
         if (t + 2 < ntiles) store_k(buf);
-        if (t + 1 < ntiles) store_v(buf ^ 1);
+    };
+
+    // Software pipeline over the key tiles: tile t's softmax runs while the
+    // matrix cores take tile t-1's PV and tile t+1's QK^T.  K is staged two
+    // tiles ahead (K(t+2) written during tile t), V one tile ahead of its use
+    // (V(t) written during tile t, read by PV(t) during tile t+1); one barrier
+    // per tile.  The stage a write reuses was last read before the previous
+    // barrier: K(t) by QK(t) during tile t-1, V(t-2) by PV(t-2) during tile t-1.
+    {  // first two K tiles and the first V tile: all loads in flight at once
+        u32x4 pk1[LOADS];
+        load_k(0);
+        load_v(0);  // V(0) stays in registers until tile 0 writes it
+        if (ntiles > 1) load_k_into(kBN, pk1);
+        store_k(0);
+        if (ntiles > 1) store_k_from(1, pk1);
+    }
+    __syncthreads();
+    f32x16 sacc[2], snext[2];
+    f16x8 pb[2][2], pbn[2][2];
+    qk(0, sacc);
+    __syncthreads();  // every wave has read K(0) before tile 0 writes K(2) over it
+    step_g(0, sacc, pb);
+    __syncthreads();
+    int t = 1;
+    for (; t + 1 < t_last; t += 2) {
+        step_a(t, sacc, snext, pb, pbn);
+        __syncthreads();
+        step_a(t + 1, snext, sacc, pbn, pb);
+        __syncthreads();
+    }
+    if (t < t_last) {
+        step_a(t, sacc, snext, pb, pbn);
+        sacc[0] = snext[0];
+        sacc[1] = snext[1];
+#pragma unroll
+        for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+            for (int hs2 = 0; hs2 < 2; ++hs2) pb[bk][hs2] = pbn[bk][hs2];
+        __syncthreads();
+        ++t;
+    }
+    for (; t <= ntiles; ++t) {
+        step_g(t, sacc, pb);
         __syncthreads();
     }
 
