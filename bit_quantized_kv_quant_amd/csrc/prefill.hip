@@ -60,21 +60,26 @@ __device__ __forceinline__ int key_lane(int r) { return (r & 3) | (((r >> 4) & 1
 
 // Staged K tile: the keys of each 32-key block are stored in the order the
 // lanes read them (row key_lane(r) holds key r), with rows padded by 16 bytes,
-// so a K-operand read (32 consecutive rows, one 16-byte chunk) and a staging
-// write (one row, all chunks) both touch distinct banks per 16 lanes, and every
-// operand address is one lane constant plus an immediate.
+// so a K-operand read (32 consecutive rows, one 16-byte chunk: lane l starts
+// at bank 4 l mod 64 within its half) touches distinct banks in every pass,
+// and every operand address is one lane constant plus an immediate.
 template <int D>
 constexpr int kKStride = D + 8;  // elements per staged K row
 
 // Staged V^T tile.  Element (key, d) with key = 32 bk + 16 half + 8 s + i and
 // d = 8 c + e, c = 8 c_hi + c_lo, sits in line
 //   ((bk * 2 + s) * (D / 64) + c_hi) * 8 + e
-// at byte 16 (c_lo + 8 half) + 2 i.  Lines are padded from 256 to 288 bytes, so
-// the 64 lanes of a transposed-store dword write (fixed e, varying c_lo, half
-// and key pair) and every 16 lanes of a PV operand read (16 consecutive rows d,
-// one chunk) each touch distinct LDS banks; both addresses are one lane
-// constant plus an immediate.
-constexpr int kVtLine = 288;
+// at byte 16 (c_lo + 8 half) + 2 i.  Lines are padded from 256 to 320 bytes.
+// The 64 lanes of a transposed-store dword write (fixed e, varying c_lo, half
+// and key pair) write 64 dwords of one line.  A 16-byte read is served in four
+// passes of 16 lanes: one half of the wave, and within it the four lane quads
+// whose quad index (lane / 4 mod 8) has the same bit parity.  In a PV operand
+// read a lane of row e = lane % 8 and chunk c = lane / 8 mod 4 starts at bank
+// 4 (4 e + c) mod 64 with this line stride, and the quads of one pass hold
+// distinct (e mod 4, c) pairs, so every pass touches 64 distinct banks (a
+// 288-byte stride, with 72 e + 4 c, wraps two lanes of a pass onto one bank).
+// Both addresses are one lane constant plus an immediate.
+constexpr int kVtLine = 320;
 
 // One block of 32 * WAVES query rows (query block qb of (sequence, head) hs),
 // staged through the workgroup's LDS.
