@@ -484,8 +484,39 @@ __device__ __forceinline__ void fa_block(
         // observation rows of a fused score pass: the log2-domain lse the second
         // pass would derive from the stored value, bit for bit
         if (s_wl && half == 0 && qi >= w0) s_wl[qi - w0] = lse_i * wmass::kLog2e;
-        if constexpr (kWithO) {
-            const float inv = 1.0f / ltot;
+    }
+    if constexpr (kWithO) {
+        const float inv = 1.0f / ltot;
+        if constexpr (D == 128) {
+            // The wave's 32 rows of O go through its own 4 KB slice of the V^T
+            // stages (free after the last tile: the next block writes them only
+            // after its first barrier), 64 columns at a time, so that every
+            // global store writes whole 128-byte half rows.  In the slice, row r
+            // keeps its 16-byte chunk c at chunk c ^ ((r >> 1) & 7), which leaves
+            // the lane-quad passes of the 16-byte reads free of bank conflicts.
+            char* so = sV + wave * (32 * 128);
+            const int r = lane & 31;
+#pragma unroll
+            for (int R = 0; R < 2; ++R) {
+#pragma unroll
+                for (int dd = 0; dd < 2; ++dd) {
+#pragma unroll
+                    for (int a4 = 0; a4 < 4; ++a4) {
+                        bf16x4 w;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[2 * R + dd][4 * a4 + e] * inv);
+                        *reinterpret_cast<bf16x4*>(so + r * 128 + 16 * ((4 * dd + a4) ^ ((r >> 1) & 7)) + 8 * half) = w;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = (lane >> 3) + 8 * i, c = lane & 7;
+                    const u32x4 val = *reinterpret_cast<const u32x4*>(so + rr * 128 + 16 * (c ^ ((rr >> 1) & 7)));
+                    if (qw0 + rr < T_ctx)
+                        *reinterpret_cast<u32x4*>(o + (qbase + qw0 + rr) * D + 64 * R + 8 * c) = val;
+                }
+            }
+        } else if (qi < T_ctx) {
 #pragma unroll
             for (int d = 0; d < DB; ++d) {
 #pragma unroll
