@@ -106,7 +106,11 @@ __device__ __forceinline__ void fa_block(
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int half = lane >> 5;
-    const int qw0 = q0 + 32 * wave;
+    // Waves w and w + 4 share a SIMD; giving them row groups w and 7 - w evens
+    // out the causal work per SIMD, so the lone wave of a SIMD near the diagonal
+    // has it to itself for longer.
+    const int rgrp = WAVES == 8 && wave >= 4 ? 11 - wave : wave;
+    const int qw0 = q0 + 32 * rgrp;
     const int qi = qw0 + (lane & 31);
 
     const size_t qbase = ((size_t)b * Hq + h) * T_ctx;
