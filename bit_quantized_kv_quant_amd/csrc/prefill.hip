@@ -116,15 +116,9 @@ __device__ __forceinline__ void fa_block(
     const size_t qbase = ((size_t)b * Hq + h) * T_ctx;
     const size_t kvbase = ((size_t)b * Hkv + g) * T_ctx;
 
-    // Q^T operand: lane holds q[qi][16 kk + 8 half + 0..7]
+    // Q^T operand: lane holds q[qi][16 kk + 8 half + 0..7] (loaded after the
+    // first K / V tiles, which are needed first)
     bf16x8 qreg[KS];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        if (qi < T_ctx)
-            qreg[kk] = *reinterpret_cast<const bf16x8*>(q + (qbase + qi) * D + 16 * kk + 8 * half);
-        else
-            qreg[kk] = bf16x8{};
-    }
 
     const int kv_end = min(T_ctx, q0 + BM);  // keys this workgroup needs
     const int ntiles = (kv_end + kBN - 1) / kBN;
@@ -448,6 +442,15 @@ __device__ __forceinline__ void fa_block(
         load_k(0);
         load_v(0);  // V(0) stays in registers until tile 0 writes it
         if (ntiles > 1) load_k_into(kBN, pk1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            if (qi < T_ctx)
+                qreg[kk] = *reinterpret_cast<const bf16x8*>(q + (qbase + qi) * D + 16 * kk + 8 * half);
+            else
+                qreg[kk] = bf16x8{};
+        }
+        __builtin_amdgcn_sched_barrier(0);
         store_k(0);
         if (ntiles > 1) store_k_from(1, pk1);
     }
