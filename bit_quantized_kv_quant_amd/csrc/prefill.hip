@@ -123,10 +123,11 @@ __device__ __forceinline__ void fa_block(
     const int kv_end = min(T_ctx, q0 + BM);  // keys this workgroup needs
     const int ntiles = (kv_end + kBN - 1) / kBN;
 
-    // K tiles are register-staged (global -> VGPR -> LDS, XOR-swizzled 16-byte
-    // chunks).  Loads go through a buffer resource based at the tile's first
-    // row and sized to the rows that exist: rows past T read as zeros, and such
-    // keys sit only in diagonal tiles, where they are masked.  (A
+    // K tiles are register-staged (global -> VGPR -> LDS, rows in lane order,
+    // see kKStride).  Loads go through a buffer resource based at the tile's
+    // first row and sized to the rows that exist: rows past T read as zeros
+    // (a tile that starts past T reads nothing), and such keys sit only in
+    // diagonal tiles, where they are masked, or in stages no QK^T reads.  (A
     // global_load_lds path would skip the VGPR hop, but the compiler then waits
     // for every outstanding load before any LDS read.)
     u32x4 pk[LOADS];
