@@ -241,13 +241,18 @@ __device__ __forceinline__ void fa_block(
     // moves.  Branch-free except the (rare, wave-uniform) rescale.
     auto softmax = [&](f32x16 (&sacc)[2], int n0, auto mask_tag, f16x8 (&pb)[2][2]) {
         constexpr bool kMask = decltype(mask_tag)::value;
+        // key 32 bk + e of the lane's half lies past its query when 32 bk + e >
+        // rel: the offsets are immediates, and rel is formed here, so no
+        // per-key position is kept across the block
+        int rel = qi - n0 - 16 * half;
+        if constexpr (kMask) asm volatile("" : "+v"(rel));
         float tmax = -INFINITY;
 #pragma unroll
         for (int bk = 0; bk < 2; ++bk) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 if constexpr (kMask) {
-                    if (n0 + 32 * bk + 16 * half + e > qi) sacc[bk][e] = -INFINITY;
+                    if (32 * bk + e > rel) sacc[bk][e] = -INFINITY;
                 }
                 tmax = fmaxf(tmax, sacc[bk][e]);
             }
@@ -503,7 +508,12 @@ __device__ __forceinline__ void fa_block(
             // keeps its 16-byte chunk c at chunk c ^ ((r >> 1) & 7), which leaves
             // the lane-quad passes of the 16-byte reads free of bank conflicts.
             char* so = sV + wave * (32 * 128);
-            const int r = lane & 31;
+            // lane index formed here, so the slice and store addresses are
+            // computed in the epilogue instead of being kept (spilled) across
+            // the tile loop
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int r = ln & 31;
 #pragma unroll
             for (int R = 0; R < 2; ++R) {
 #pragma unroll
@@ -518,7 +528,7 @@ __device__ __forceinline__ void fa_block(
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int rr = (lane >> 3) + 8 * i, c = lane & 7;
+                    const int rr = (ln >> 3) + 8 * i, c = ln & 7;
                     const u32x4 val = *reinterpret_cast<const u32x4*>(so + rr * 128 + 16 * (c ^ ((rr >> 1) & 7)));
                     if (qw0 + rr < T_ctx)
                         *reinterpret_cast<u32x4*>(o + (qbase + qw0 + rr) * D + 64 * R + 8 * c) = val;
