@@ -26,7 +26,8 @@
 // 32-key block is permuted (phys) so that accumulator register v of a lane is
 // key 16*half + v, which makes both operand layouts line up without shuffles.
 // Causal: tiles above the diagonal are never loaded; only tiles that cross it
-// apply the mask.  Query blocks are issued longest-first.
+// apply the mask.  Query blocks are issued longest-first.  O leaves through LDS,
+// so every global store writes whole 128-byte half rows.
 //
 // Single-pass selective attention: when each KV head has one query head and
 // the W <= 32 observation rows all fall in a head's last query block, the
@@ -93,7 +94,7 @@ __device__ __forceinline__ void fa_block(
     constexpr int CH = D / 8;               // 16-byte chunks per row
     constexpr int KS = D / 16;              // MFMA k-steps over the head dim
     constexpr int DB = D / 32;              // 32-wide output blocks over the head dim
-    constexpr int LOADS = kBN * CH / NT;    // V chunks per thread per tile
+    constexpr int LOADS = kBN * CH / NT;    // K chunks per thread per tile
     constexpr int KST = kKStride<D>;
     constexpr int TILE = kBN * KST;         // elements of one staged K tile
     constexpr int CH2 = D / 64;             // 64-wide halves of the head dim
