@@ -62,7 +62,7 @@ def parse():
                     help="batch of the headline 40-layer pyramid decode (1133 fills about 250 GB)")
     ap.add_argument("--headline-only", action="store_true",
                     help="run the headline decode only (e.g. under a counter profiler)")
-    ap.add_argument("--only", choices=["prefill_16k", "chain", "decode_gqa"], default=None,
+    ap.add_argument("--only", choices=["prefill_16k", "chain", "decode_gqa", "decode_stream"], default=None,
                     help="run one extra alone and print it (no headline; e.g. under a counter profiler)")
     ap.add_argument("--chain-warmup", type=int, default=25,
                     help="warm-up steps of the chain extra (a fresh process runs its first chain steps slow)")
@@ -787,6 +787,10 @@ def main():
         budgets = [mk.keep_count(gw.T, gw.budget_pct)] * gw.layers
         print(json.dumps({"decode_gqa": decode_layers(torch, mk, synth, gw, gw.B, budgets, reps=args.steps,
                                                       n_queries=args.steps)}), flush=True)
+        return
+    if args.only == "decode_stream":
+        gw = synth.WORKLOADS["mistral_44k"]
+        print(json.dumps({"decode_stream": decode_stream(torch, mk, synth, gw, args.steps)}), flush=True)
         return
 
     # ---- headline: 40-layer pyramid decode at the ~250 GB batch ----

@@ -36,9 +36,13 @@
 // walks its own items (no workgroup barrier): all 128-token steps of an item in
 // order, the next step's key loads issued once the current keys are consumed
 // and its value loads once the current values are, across item boundaries too.
-// With one range per KV head the wave writes the bf16 output itself; otherwise
-// partial (m, l, acc) per range go to the workspace and a small second kernel
-// merges them.
+// With one range per KV head the wave writes the bf16 output itself.  When a
+// KV head's ranges fit a few workgroups (small batches) the merge happens in
+// the same launch: the workgroups of a head combine their waves' parts in LDS
+// and the last one to take the head's ticket merges the workgroups' parts
+// (decode_partial_kernel with kTicket), a streaming cache's residual window
+// included.  Otherwise partial (m, l, acc) per range go to the workspace and a
+// small second kernel merges them (with the window, if any).
 #include <algorithm>
 #include <atomic>
 
@@ -188,6 +192,78 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Exact part of a streaming decode for one (sequence, query head) row, by one
+// wave: the residual tokens (bf16 K / V, at most 31, slots [B][Hkv][res_stride][D]).
+// Lane l holds channels 2l and 2l + 1 (lanes >= D / 2 carry zeros).  Every
+// window row is requested at once, one dword per lane and row, through buffer
+// resources sized to the n_res valid slots (slots past it read as zeros, no
+// branch); then one wave-wide sum per token.  The result: m, the sum of
+// 2^(l - m) (l = q.k in log2 units) and x[c] = sum of 2^(l - m) v[2 lane + c].
+constexpr int kResSlots = kGroup - 1;  // window slots that can hold a token
+struct ResRows {
+    uint32_t k[kResSlots], v[kResSlots];  // the lane's channel pair of every window row
+    uint32_t q;                           // the lane's channel pair of the query
+};
+template <int D>
+__device__ __forceinline__ void residual_load(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_res,
+                                              const uint16_t* __restrict__ v_res, int res_stride, int n_res, int Hq,
+                                              int Hkv, int row, int lane, ResRows& rr) {
+    const int b = row / Hq, h = row % Hq;
+    const int g = h / (Hq / Hkv);
+    const size_t unit = (size_t)b * Hkv + g;
+    const bool act = 2 * lane < D;
+    const int off = act ? 4 * lane : 0;  // byte offset of the lane's channel pair within a row
+    const int bytes = n_res * D * 2;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k_res + unit * res_stride * D), 0, bytes,
+                                                      0x00020000);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(v_res + unit * res_stride * D), 0, bytes,
+                                                      0x00020000);
+#pragma unroll
+    for (int t = 0; t < kResSlots; ++t) rr.k[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, off + t * D * 2, 0, 0);
+#pragma unroll
+    for (int t = 0; t < kResSlots; ++t) rr.v[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, off + t * D * 2, 0, 0);
+    rr.q = act ? *reinterpret_cast<const uint32_t*>(q + (size_t)row * D + 2 * lane) : 0u;
+}
+__device__ __forceinline__ void residual_reduce(const ResRows& rr, int n_res, float scale_log2, float& m_out,
+                                                float& l_out, float (&x)[2]) {
+    const float q0 = bf16_bits_to_f32(rr.q & 0xFFFFu), q1 = bf16_bits_to_f32(rr.q >> 16);
+    float l[kResSlots];
+    float m = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kResSlots; ++t) {
+        l[t] = -INFINITY;
+        if (t < n_res) {  // wave-uniform
+            const float d = fmaf(q0, bf16_bits_to_f32(rr.k[t] & 0xFFFFu), q1 * bf16_bits_to_f32(rr.k[t] >> 16));
+            l[t] = dpp_sum<kWave>(d) * scale_log2;
+            m = fmaxf(m, l[t]);
+        }
+    }
+    float lsum = 0.0f;
+    x[0] = 0.0f;
+    x[1] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kResSlots; ++t) {
+        if (t < n_res) {
+            const float p = exp2f(l[t] - m);
+            lsum += p;
+            x[0] = fmaf(p, bf16_bits_to_f32(rr.v[t] & 0xFFFFu), x[0]);
+            x[1] = fmaf(p, bf16_bits_to_f32(rr.v[t] >> 16), x[1]);
+        }
+    }
+    m_out = m;
+    l_out = lsum;
+}
+
+template <int D>
+__device__ __forceinline__ void residual_part(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_res,
+                                              const uint16_t* __restrict__ v_res, int res_stride, int n_res, int Hq,
+                                              int Hkv, float scale_log2, int row, int lane, float& m_out,
+                                              float& l_out, float (&x)[2]) {
+    ResRows rr;
+    residual_load<D>(q, k_res, v_res, res_stride, n_res, Hq, Hkv, row, lane, rr);
+    residual_reduce(rr, n_res, scale_log2, m_out, l_out, x);
+}
+
 // Ticket-mode epilogue of a workgroup (all 64 NW threads): s_tp holds the NW
 // waves' parts of (sequence, KV head) `unit`, each (head r) a row of D sums
 // 2^(l - m) v, then m and the sum of 2^(l - m) (log2 units).  They are merged
@@ -197,7 +273,9 @@ __device__ __forceinline__ void wave_sync_lds() {
 // workgroup that takes the head's last ticket merges the nwg parts the same
 // way, writes the output and resets the ticket to zero.  Empty parts (m = -inf,
 // sum 0) get weight 0; the reference maximum is finite whenever one part is not
-// empty.
+// empty.  With kWin, s_win (when not null) holds the exact part of a streaming
+// cache's residual window in the same form, one row per head, and joins this
+// workgroup's merge as one more part.
 //
 // The workgroups of a head may sit on different XCDs, whose L2 caches are not
 // coherent with each other for ordinary accesses.  The parts are therefore
@@ -206,10 +284,11 @@ __device__ __forceinline__ void wave_sync_lds() {
 // write-back / invalidate fences: every wave waits for its part stores to
 // complete before the workgroup takes its ticket, and the last workgroup
 // reads the parts only after its ticket has come back.
-template <int D, int R, int NW>
-__device__ __forceinline__ void ticket_merge(float (*s_tp)[R][D + 2], int* s_last, int unit, int wg, int nwg,
-                                             float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-                                             __bf16* __restrict__ out, int32_t* __restrict__ tickets) {
+template <int D, int R, int NW, bool kWin>
+__device__ __forceinline__ void ticket_merge(float (*s_tp)[R][D + 2], const float (*s_win)[D + 2], int* s_last,
+                                             int unit, int wg, int nwg, float* __restrict__ ws_acc,
+                                             float* __restrict__ ws_ml, __bf16* __restrict__ out,
+                                             int32_t* __restrict__ tickets) {
     auto st_dev = [](float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
     auto ld_dev = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
     constexpr int NTH = 64 * NW;
@@ -219,6 +298,9 @@ __device__ __forceinline__ void ticket_merge(float (*s_tp)[R][D + 2], int* s_las
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, s_tp[w][r][D]);
+        if constexpr (kWin) {
+            if (s_win) M = fmaxf(M, s_win[r][D]);  // workgroup-uniform
+        }
         const float Ms = M == -INFINITY ? 0.0f : M;
         float L = 0.0f, O = 0.0f;
 #pragma unroll
@@ -226,6 +308,13 @@ __device__ __forceinline__ void ticket_merge(float (*s_tp)[R][D + 2], int* s_las
             const float f = exp2f(s_tp[w][r][D] - Ms);
             L = fmaf(s_tp[w][r][D + 1], f, L);
             O = fmaf(s_tp[w][r][c], f, O);
+        }
+        if constexpr (kWin) {
+            if (s_win) {
+                const float f = exp2f(s_win[r][D] - Ms);
+                L = fmaf(s_win[r][D + 1], f, L);
+                O = fmaf(s_win[r][c], f, O);
+            }
         }
         const size_t row = (size_t)unit * R + r;
         if (nwg == 1) {
@@ -308,20 +397,26 @@ __device__ __forceinline__ void ticket_merge(float (*s_tp)[R][D + 2], int* s_las
 // 128-token steps of an item in order, and issues the first loads of its next
 // item while it finishes the current one.
 //
-// With kTicket (a split head, no residual window) the grid is one item per
-// wave and a workgroup's NW waves hold NW consecutive token ranges of one
-// (sequence, KV head): the NW parts are merged through LDS, each workgroup
-// writes one part to the workspace (ws_splits = workgroups per KV head) and
-// takes a ticket on the head; the workgroup that takes the last ticket merges
-// the head's parts, writes the output and puts the ticket back to zero, so
-// the whole decode is one launch with no spinning.
-template <int D, int R, int NW, bool kTicket>
+// With kTicket (a split head) the grid is one item per wave and a
+// workgroup's NW waves hold NW consecutive token ranges of one (sequence, KV
+// head): the NW parts are merged through LDS, each workgroup writes one part
+// to the workspace (ws_splits = workgroups per KV head) and takes a ticket on
+// the head; the workgroup that takes the last ticket merges the head's parts,
+// writes the output and puts the ticket back to zero, so the whole decode is
+// one launch with no spinning.  With kWin (a streaming cache's residual
+// window: n_res rows of k_res / v_res, slots [B][Hkv][res_stride][D]) the
+// last workgroup of each head also computes the window's exact part, waves
+// NW - R .. NW - 1 one query head each after their own ranges (the last
+// ranges, empty past the packed tokens), and merges it with its waves' parts.
+template <int D, int R, int NW, bool kTicket, bool kWin>
 __global__ __launch_bounds__(64 * NW, (!kTicket && R == 1) ? 4 : 1) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes, const uint32_t* __restrict__ k_sz,
     const uint8_t* __restrict__ v_codes, const uint32_t* __restrict__ v_sz, int n, int tok_stride, int grp_stride,
     int chunk, int splits, int ws_splits, int direct, int n_items, float scale_log2, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, __bf16* __restrict__ out, const int32_t* __restrict__ counts,
-    int32_t* __restrict__ tickets) {
+    int32_t* __restrict__ tickets, const uint16_t* __restrict__ k_res, const uint16_t* __restrict__ v_res,
+    int res_stride, int n_res) {
+    static_assert(!kWin || kTicket, "the window part joins the one-launch merge");
     constexpr int NG = D / 32;  // 32-channel groups: key K blocks and value scale groups
     constexpr int NT = D / 16;  // 16-channel value tiles
     constexpr int GPL = NG * R / 4 > 1 ? NG * R / 4 : 1;  // value groups per lane in the weight prep
@@ -331,6 +426,7 @@ __global__ __launch_bounds__(64 * NW, (!kTicket && R == 1) ? 4 : 1) void decode_
     // ticket mode: the waves' parts (sum 2^(l - m) v per channel, then m and the
     // sum of 2^(l - m)) and the last-ticket flag
     __shared__ float s_tp[kTicket ? NW : 1][R][D + 2];
+    __shared__ float s_win[kWin ? R : 1][D + 2];  // the window part, in the same form
     __shared__ int s_last;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: keeps bases scalar
@@ -673,8 +769,28 @@ __global__ __launch_bounds__(64 * NW, (!kTicket && R == 1) ? 4 : 1) void decode_
                     s_tp[wave][blk][D + 1] = lsum;
                 }
             }
-            ticket_merge<D, R, NW>(s_tp, &s_last, ps.unit, blockIdx.x % ws_splits, ws_splits, ws_acc, ws_ml, out,
-                                   tickets);
+            const int wg = blockIdx.x % ws_splits;  // this workgroup's place among the head's
+            const bool win = kWin && wg == ws_splits - 1;
+            if constexpr (kWin) {
+                if (win && wave >= NW - R) {  // wave-uniform: one query head per wave
+                    const int r = wave - (NW - R);
+                    const int nr = counts ? max(0, min(n_res, counts[1])) : n_res;
+                    float m_r, l_r, x[2];
+                    // with Hq = R and Hkv = 1 the row's KV unit is row / R
+                    residual_part<D>(q, k_res, v_res, res_stride, nr, R, 1, scale_log2, ps.unit * R + r, lane, m_r,
+                                     l_r, x);
+                    if (2 * lane < D) {
+                        s_win[r][2 * lane] = x[0];
+                        s_win[r][2 * lane + 1] = x[1];
+                    }
+                    if (lane == 0) {
+                        s_win[r][D] = m_r;
+                        s_win[r][D + 1] = l_r;
+                    }
+                }
+            }
+            ticket_merge<D, R, NW, kWin>(s_tp, win ? s_win : nullptr, &s_last, ps.unit, wg, ws_splits, ws_acc, ws_ml,
+                                         out, tickets);
             break;  // one item per wave
         }
         if (blk < R) {
@@ -697,78 +813,6 @@ __global__ __launch_bounds__(64 * NW, (!kTicket && R == 1) ? 4 : 1) void decode_
         item = next_item;
         ps = first_next;
     }
-}
-
-// Exact part of a streaming decode for one (sequence, query head) row, by one
-// wave: the residual tokens (bf16 K / V, at most 31, slots [B][Hkv][res_stride][D]).
-// Lane l holds channels 2l and 2l + 1 (lanes >= D / 2 carry zeros).  Every
-// window row is requested at once, one dword per lane and row, through buffer
-// resources sized to the n_res valid slots (slots past it read as zeros, no
-// branch); then one wave-wide sum per token.  The result: m, the sum of
-// 2^(l - m) (l = q.k in log2 units) and x[c] = sum of 2^(l - m) v[2 lane + c].
-constexpr int kResSlots = kGroup - 1;  // window slots that can hold a token
-struct ResRows {
-    uint32_t k[kResSlots], v[kResSlots];  // the lane's channel pair of every window row
-    uint32_t q;                           // the lane's channel pair of the query
-};
-template <int D>
-__device__ __forceinline__ void residual_load(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_res,
-                                              const uint16_t* __restrict__ v_res, int res_stride, int n_res, int Hq,
-                                              int Hkv, int row, int lane, ResRows& rr) {
-    const int b = row / Hq, h = row % Hq;
-    const int g = h / (Hq / Hkv);
-    const size_t unit = (size_t)b * Hkv + g;
-    const bool act = 2 * lane < D;
-    const int off = act ? 4 * lane : 0;  // byte offset of the lane's channel pair within a row
-    const int bytes = n_res * D * 2;
-    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k_res + unit * res_stride * D), 0, bytes,
-                                                      0x00020000);
-    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(v_res + unit * res_stride * D), 0, bytes,
-                                                      0x00020000);
-#pragma unroll
-    for (int t = 0; t < kResSlots; ++t) rr.k[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, off + t * D * 2, 0, 0);
-#pragma unroll
-    for (int t = 0; t < kResSlots; ++t) rr.v[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, off + t * D * 2, 0, 0);
-    rr.q = act ? *reinterpret_cast<const uint32_t*>(q + (size_t)row * D + 2 * lane) : 0u;
-}
-__device__ __forceinline__ void residual_reduce(const ResRows& rr, int n_res, float scale_log2, float& m_out,
-                                                float& l_out, float (&x)[2]) {
-    const float q0 = bf16_bits_to_f32(rr.q & 0xFFFFu), q1 = bf16_bits_to_f32(rr.q >> 16);
-    float l[kResSlots];
-    float m = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < kResSlots; ++t) {
-        l[t] = -INFINITY;
-        if (t < n_res) {  // wave-uniform
-            const float d = fmaf(q0, bf16_bits_to_f32(rr.k[t] & 0xFFFFu), q1 * bf16_bits_to_f32(rr.k[t] >> 16));
-            l[t] = dpp_sum<kWave>(d) * scale_log2;
-            m = fmaxf(m, l[t]);
-        }
-    }
-    float lsum = 0.0f;
-    x[0] = 0.0f;
-    x[1] = 0.0f;
-#pragma unroll
-    for (int t = 0; t < kResSlots; ++t) {
-        if (t < n_res) {
-            const float p = exp2f(l[t] - m);
-            lsum += p;
-            x[0] = fmaf(p, bf16_bits_to_f32(rr.v[t] & 0xFFFFu), x[0]);
-            x[1] = fmaf(p, bf16_bits_to_f32(rr.v[t] >> 16), x[1]);
-        }
-    }
-    m_out = m;
-    l_out = lsum;
-}
-
-template <int D>
-__device__ __forceinline__ void residual_part(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_res,
-                                              const uint16_t* __restrict__ v_res, int res_stride, int n_res, int Hq,
-                                              int Hkv, float scale_log2, int row, int lane, float& m_out,
-                                              float& l_out, float (&x)[2]) {
-    ResRows rr;
-    residual_load<D>(q, k_res, v_res, res_stride, n_res, Hq, Hkv, row, lane, rr);
-    residual_reduce(rr, n_res, scale_log2, m_out, l_out, x);
 }
 
 // Merge the token ranges of one (sequence, query head): the range maxima and
@@ -891,7 +935,7 @@ template <int D, int R>
 int resident_workgroups() {
     static const int per_cu = [] {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partial_kernel<D, R, 4, false>, 256, 0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partial_kernel<D, R, 4, false, false>, 256, 0) != hipSuccess ||
             nb < 1)
             nb = 1;
         return nb;
@@ -940,23 +984,25 @@ hipError_t launch_dr(const void* q, const DecodeSrc& src, int B, int Hq, int Hkv
     float* ws_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kTicketBytes);
     const int parts = plan.splits;
     const long items = (long)B * Hkv * plan.splits;
-    if (plan.ticket && !res && !src.counts) {
+    if (plan.ticket && (res || !src.counts)) {
         // one launch: one item per wave, plan.nw ranges of a head per
         // workgroup, the last workgroup of each head merges (plan.splits %
-        // plan.nw == 0)
+        // plan.nw == 0); a residual window (res: always with device-side
+        // counts) is computed and merged by the head's last workgroup
         const int nwg = parts / plan.nw;
         float* ws_ml = ws_acc + (size_t)B * Hq * nwg * D;
-        if (plan.nw == 8)
-            hipLaunchKernelGGL((decode_partial_kernel<D, R, 8, true>), dim3((unsigned)(items / 8)), dim3(512), 0,
-                               stream, qq, src.k_codes, src.k_sz, src.v_codes, src.v_sz, src.n, src.tok_stride,
-                               src.grp_stride, plan.chunk, plan.splits, nwg, 0, (int)items, scale_log2, ws_acc, ws_ml,
-                               o, src.counts, tickets);
-        else
-            hipLaunchKernelGGL((decode_partial_kernel<D, R, 4, true>), dim3((unsigned)(items / 4)), dim3(256), 0,
-                               stream, qq, src.k_codes, src.k_sz, src.v_codes, src.v_sz, src.n, src.tok_stride,
-                               src.grp_stride, plan.chunk, plan.splits, nwg, 0, (int)items, scale_log2, ws_acc, ws_ml,
-                               o, src.counts, tickets);
-        return hipGetLastError();
+        auto go = [&](auto kernel, int nw) {
+            hipLaunchKernelGGL(kernel, dim3((unsigned)(items / nw)), dim3(64 * nw), 0, stream, qq, src.k_codes,
+                               src.k_sz, src.v_codes, src.v_sz, src.n, src.tok_stride, src.grp_stride, plan.chunk,
+                               plan.splits, nwg, 0, (int)items, scale_log2, ws_acc, ws_ml, o, src.counts, tickets,
+                               src.k_res, src.v_res, src.res_stride, src.n_res);
+            return hipGetLastError();
+        };
+        if (res)
+            return plan.nw == 8 ? go(decode_partial_kernel<D, R, 8, true, true>, 8)
+                                : go(decode_partial_kernel<D, R, 4, true, true>, 4);
+        return plan.nw == 8 ? go(decode_partial_kernel<D, R, 8, true, false>, 8)
+                            : go(decode_partial_kernel<D, R, 4, true, false>, 4);
     }
     // packed ranges: plan.splits parts in the workspace (the output itself when
     // it is the only part); the window, if any, is computed and merged by the
@@ -964,10 +1010,10 @@ hipError_t launch_dr(const void* q, const DecodeSrc& src, int B, int Hq, int Hkv
     const bool direct = parts == 1 && !res;
     float* ws_ml = ws_acc + (size_t)B * Hq * parts * D;
     const long grid = std::min<long>((items + 3) / 4, resident_workgroups<D, R>());
-    hipLaunchKernelGGL((decode_partial_kernel<D, R, 4, false>), dim3((unsigned)grid), dim3(256), 0, stream, qq,
-                       src.k_codes, src.k_sz, src.v_codes, src.v_sz, src.n, src.tok_stride, src.grp_stride, plan.chunk,
-                       plan.splits, parts, direct ? 1 : 0, (int)items, scale_log2, ws_acc, ws_ml, o, src.counts,
-                       tickets);
+    hipLaunchKernelGGL((decode_partial_kernel<D, R, 4, false, false>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       qq, src.k_codes, src.k_sz, src.v_codes, src.v_sz, src.n, src.tok_stride, src.grp_stride,
+                       plan.chunk, plan.splits, parts, direct ? 1 : 0, (int)items, scale_log2, ws_acc, ws_ml, o,
+                       src.counts, tickets, nullptr, nullptr, 0, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(B * Hq), dim3(D + (res ? kWave : 0)), 0, stream, ws_acc,

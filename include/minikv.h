@@ -261,7 +261,11 @@ int minikv_stream_append(const void *k, const void *v, const int32_t *idx, int i
  * Single-query decode over a streaming cache: the softmax runs over the
  * n_packed packed tokens (dequantised in registers, as minikv_decode_attn)
  * and the n_res residual tokens (exact) together.  q bf16 [B][Hq][D] -> out
- * bf16 [B][Hq][D].  ws: at least minikv_stream_decode_ws_bytes(...) bytes.
+ * bf16 [B][Hq][D].  ws: at least minikv_stream_decode_ws_bytes(...) bytes,
+ * whose first MINIKV_DECODE_TICKET_BYTES bytes hold zeros before the buffer's
+ * first use, as for minikv_decode_attn (when a KV head's tokens are split over
+ * a few workgroups the window's exact part is merged in the same launch as
+ * the packed tokens, by the head's last workgroup).
  * sm_scale <= 0 means 1/sqrt(D).
  * Errors: NULL; SHAPE (Hq % Hkv, n_packed not a multiple of 32 or > cap,
  * n_res outside 0..31, n_packed + n_res < 1); UNSUPPORTED (D, Hq/Hkv not 1,
@@ -328,7 +332,9 @@ int minikv_stream_append_token(const void *k_new, const void *v_new, int B, int 
  * minikv_stream_step_decode is minikv_stream_decode with the counts read on
  * the device: the split plan covers all cap tokens (token ranges past n_packed
  * contribute empty parts) and the window is always a part (empty at n_res 0).
- * Workspace: minikv_stream_step_decode_ws_bytes (0 for invalid sizes).
+ * Workspace: minikv_stream_step_decode_ws_bytes (0 for invalid sizes), its
+ * first MINIKV_DECODE_TICKET_BYTES bytes zero before first use (every call
+ * leaves them zero).
  * Errors: NULL (any pointer, ws included); SHAPE; UNSUPPORTED (D, Hq/Hkv not
  * 1, 2 or 4); ALIGN; WORKSPACE; LAUNCH.  Calls that overlap on one counts
  * buffer race.

@@ -174,6 +174,38 @@ def test_device_step_matches_oracle(dev, Hq, Hkv, D, n_sel, steps):
             _check_state(c, st)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,n_sel", [(8, 2, 128, 3001), (4, 4, 64, 2097), (2, 1, 128, 4010)])
+def test_stream_split_heads_with_window(dev, Hq, Hkv, D, n_sel):
+    """KV heads whose packed tokens span several workgroups of the one-launch plan, plus a
+    window: the head's last workgroup computes the window's exact part and merges it with its
+    ranges before the cross-workgroup merge.  Host-side counts, then 40 device-side steps
+    (plans over the whole capacity, whose last ranges are empty) against the oracle."""
+    say("stream split heads + window, Hq", Hq, "Hkv", Hkv, "D", D, "selection", n_sel)
+    B, T, steps = 1, n_sel + 300, 40
+    cap = 32 * ((n_sel + steps) // 32 + 2)
+    rng, c, st = _start(dev, 3 * n_sel + D, B, Hkv, T, D, n_sel, cap)
+    assert c.n_res == n_sel % 32 > 0
+    # the plan has two to eight workgroup parts per head (a one-launch plan split over workgroups)
+    parts = (mk.decode_ws_bytes(B, Hq, Hkv, c.n_packed, D) - 16384) // (B * Hq * (D + 2) * 4)
+    assert 2 <= parts <= 8, parts
+    q = _token(rng, B, Hq, D)
+    assert_attn_close(to_np(c.decode(torch.from_numpy(q).to(dev).to(torch.bfloat16))),
+                      oracle.stream_decode_ref(q, st), "host counts")
+    c.to_device_counts()
+    ws = torch.zeros(c.step_ws_bytes(Hq), dtype=torch.uint8, device=dev)
+    for step in range(steps):
+        kn, vn = _token(rng, B, Hkv, D), _token(rng, B, Hkv, D, 0.5)
+        c.step_append(torch.from_numpy(kn).to(dev).to(torch.bfloat16), torch.from_numpy(vn).to(dev).to(torch.bfloat16))
+        st = oracle.stream_append_ref(st, kn, vn)
+        q = _token(rng, B, Hq, D)
+        out = c.step_decode(torch.from_numpy(q).to(dev).to(torch.bfloat16), ws=ws)
+        torch.cuda.synchronize()
+        assert_attn_close(to_np(out), oracle.stream_decode_ref(q, st), f"device step {step}")
+    assert ws[:16384].count_nonzero().item() == 0  # every call leaves the tickets zero
+    c.from_device_counts()
+    _check_state(c, st)
+
+
 def test_device_step_graph_replays(dev):
     """One captured generation step over two layers (append + decode each), replayed 40 times with
     new inputs copied in and eager work between replays; every replay against the oracle."""
