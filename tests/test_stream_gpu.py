@@ -206,6 +206,33 @@ def test_stream_split_heads_with_window(dev, Hq, Hkv, D, n_sel):
     _check_state(c, st)
 
 
+# (B, Hq, Hkv, D, selection): query heads per KV head 1, 2 and 4 at D = 64 and 128; windows of 1,
+# 5, 9, 13 and 31 tokens; plans of one 4-wave or 8-wave workgroup per KV head and of 2, 3, 5 and 8
+# workgroups per head (the device-side plans cover the capacity, one more group than is packed)
+_PLAN_SWEEP = [(1, 4, 1, 64, 7917), (1, 2, 1, 64, 4543), (2, 4, 1, 128, 1505), (3, 2, 2, 64, 325),
+               (2, 8, 2, 64, 2057), (1, 4, 2, 128, 1055)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,n_sel", _PLAN_SWEEP)
+def test_stream_window_plan_sweep(dev, B, Hq, Hkv, D, n_sel):
+    """The window part in every kind of one-launch plan: one decode with host-side counts and one
+    with the counts on the device, each against the oracle; the ticket area is zero afterwards."""
+    say("stream window plan sweep B", B, "Hq", Hq, "Hkv", Hkv, "D", D, "selection", n_sel)
+    cap = 32 * (n_sel // 32 + 2)
+    rng, c, st = _start(dev, 7 * n_sel + B, B, Hkv, n_sel + 100, D, n_sel, cap)
+    assert c.n_res == n_sel % 32
+    q = _token(rng, B, Hq, D)
+    qd = torch.from_numpy(q).to(dev).to(torch.bfloat16)
+    ref = oracle.stream_decode_ref(q, st)
+    ws = torch.zeros(c.ws_bytes(Hq), dtype=torch.uint8, device=dev)
+    assert_attn_close(to_np(c.decode(qd, ws=ws)), ref, "host counts")
+    c.to_device_counts()
+    ws_d = torch.zeros(c.step_ws_bytes(Hq), dtype=torch.uint8, device=dev)
+    assert_attn_close(to_np(c.step_decode(qd, ws=ws_d)), ref, "device counts")
+    torch.cuda.synchronize()
+    assert ws[:16384].count_nonzero().item() == 0 and ws_d[:16384].count_nonzero().item() == 0
+
+
 def test_device_step_graph_replays(dev):
     """One captured generation step over two layers (append + decode each), replayed 40 times with
     new inputs copied in and eager work between replays; every replay against the oracle."""
