@@ -579,6 +579,47 @@ def calibration_copy(torch, mb):
     torch.cuda.empty_cache()
 
 
+def measured_peaks(torch, mk, read_gib=8, gemm_n=8192, reps=10):
+    """Reference rates of this GPU, the denominators beside the vendor peaks: a
+    streaming read (the library's read probe: every 16-byte piece of a buffer
+    once, non-temporal), a device copy (bytes read + written), and a large bf16
+    GEMM (torch.matmul, which hipBLASLt serves; contiguous 2-D operands)."""
+    dev = torch.device("cuda:0")
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    n = read_gib * (1 << 30) // 2
+    x = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    sink = torch.zeros(mk.api.READ_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+    read_s = timed(lambda: mk.read_probe(x, sink))
+    y = torch.empty_like(x)
+    copy_s = timed(lambda: y.copy_(x))
+    del x, y, sink
+    g = torch.Generator(device=dev).manual_seed(11)
+    a = torch.randn((gemm_n, gemm_n), generator=g, device=dev).to(torch.bfloat16)
+    b = torch.randn((gemm_n, gemm_n), generator=g, device=dev).to(torch.bfloat16)
+    gemm_s = timed(lambda: torch.matmul(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+    nbytes = n * 2
+    return {"hbm_read_GBs": nbytes / read_s / 1e9,
+            "read_kind": f"minikv_read_probe over {read_gib} GiB (16-byte non-temporal loads, grid-stride)",
+            "hbm_copy_GBs": 2 * nbytes / copy_s / 1e9,
+            "copy_kind": f"device copy of {read_gib} GiB (bytes read + written)",
+            "bf16_gemm_TFLOPs": 2.0 * gemm_n ** 3 / gemm_s / 1e12,
+            "gemm_kind": f"torch.matmul {gemm_n} x {gemm_n} x {gemm_n} bf16 (hipBLASLt)"}
+
+
 def chain(torch, mk, synth, args):
     """The whole path on the LLaMA2-7B-shaped workload; returns (chain, prefill
     roofline, single-layer decode) objects."""
@@ -793,6 +834,11 @@ def main():
         print(json.dumps({"decode_stream": decode_stream(torch, mk, synth, gw, args.steps)}), flush=True)
         return
 
+    # reference rates of this GPU (before anything else holds device memory)
+    peaks = None if args.headline_only else measured_peaks(torch, mk)
+    if peaks:
+        print(f"# measured peaks: {json.dumps(peaks)}", file=sys.stderr, flush=True)
+
     # ---- headline: 40-layer pyramid decode at the ~250 GB batch ----
     head, sample = pyramid_headline(torch, mk, synth, args.pyramid_batch, args.steps, args.warmup,
                                     sample_seqs=0 if args.no_cpu_baseline else 4)
@@ -862,6 +908,11 @@ def main():
     if not args.no_variants:
         res["variants"] = variants(torch, mk, synth)
         print(f"# variants: {json.dumps(res['variants'])}", file=sys.stderr, flush=True)
+    if peaks:
+        # the headline decode and the chain's prefill against the measured rates
+        peaks["decode_frac_of_read"] = achieved / peaks["hbm_read_GBs"]
+        peaks["prefill_frac_of_gemm"] = res["prefill_roofline"]["achieved"] / peaks["bf16_gemm_TFLOPs"]
+        res["measured_peaks"] = peaks
     if sample is not None:
         res["cpu_baseline"] = cpu_baseline_pyramid(sample)
         res["chain"]["cpu_baseline"] = cpu_baseline(synth.WORKLOADS["llama7b_decode"])

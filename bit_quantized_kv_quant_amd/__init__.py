@@ -20,6 +20,7 @@ from .api import (  # noqa: F401
     window_scores,
     pyramid_keep,
     quant_pack,
+    read_probe,
     select_topk,
     select_ws_bytes,
     split_heavy_recent,

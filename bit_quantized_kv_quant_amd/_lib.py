@@ -75,6 +75,7 @@ SIGNATURES = {
     "minikv_split_heavy_recent": (_i, [_i, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]),
     "minikv_status_string": (ctypes.c_char_p, [_i]),
     "minikv_build_id": (ctypes.c_char_p, []),
+    "minikv_read_probe": (_i, [_vp, _sz, _vp, _vp]),
 }
 
 _lib = None

@@ -342,6 +342,23 @@ class StreamCache:
         return out
 
 
+READ_PROBE_SINK_WORDS = 8192
+
+
+def read_probe(x, sink=None):
+    """Streaming read of the bytes of a contiguous device tensor (a measurement aid,
+    not a step of the method): returns the int32 sink, whose XOR is the XOR of
+    every 32-bit word of x."""
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.zeros(READ_PROBE_SINK_WORDS, dtype=torch.int32, device=x.device)
+    _need(sink, torch.int32, (READ_PROBE_SINK_WORDS,), "sink")
+    st = _lib.lib().minikv_read_probe(_ptr(x), x.numel() * x.element_size(), _ptr(sink), _stream())
+    _lib.check("minikv_read_probe", st)
+    return sink
+
+
 def packed_bytes(B, Hkv, n_keep, D):
     return int(_lib.lib().minikv_packed_bytes(B, Hkv, n_keep, D))
 

@@ -29,6 +29,13 @@ extern "C" {
 #endif
 const char* minikv_build_id(void) { return MINIKV_BUILD_ID; }
 
+int minikv_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    if (!src || !sink) return MINIKV_ERR_NULL;
+    if (bytes == 0 || bytes % 16) return MINIKV_ERR_SHAPE;
+    if (misaligned(src) || misaligned(sink)) return MINIKV_ERR_ALIGN;
+    return status_of(minikv::launch_read_probe(src, bytes, sink, MINIKV_READ_PROBE_SINK_WORDS, as_stream(stream)));
+}
+
 const char* minikv_status_string(int status) {
     switch (status) {
         case MINIKV_OK: return "ok";

@@ -96,4 +96,7 @@ hipError_t launch_window_scores(const void* q, const void* k, const float* lse, 
                                 int Hq, int Hkv, int D, int window, float sm_scale, float* scores,
                                 hipStream_t stream);
 
+// Streaming-read reference (measurement aid): sink_words / 4 workgroups of 256 threads.
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int sink_words, hipStream_t stream);
+
 }  // namespace minikv

@@ -377,6 +377,19 @@ int minikv_split_heavy_recent(int n_keep, int *n_heavy, int *n_recent);
 /* Static description of a status code. */
 const char *minikv_status_string(int status);
 
+/*
+ * Measurement aid, not a step of the method: a streaming read of `bytes` bytes
+ * at src (device, 16-byte aligned, a multiple of 16 bytes), whose rate is the
+ * measured reference for the HBM-bound kernels' rooflines.  Every 16-byte
+ * piece is read once (non-temporal loads); the XOR of the 32-bit words each
+ * wave read goes to sink (device uint32 [MINIKV_READ_PROBE_SINK_WORDS],
+ * caller-owned, 16-byte aligned), so the XOR of all sink words is the XOR of
+ * every word of the buffer.  Errors: NULL; SHAPE (bytes 0 or not a multiple
+ * of 16); ALIGN; LAUNCH.
+ */
+#define MINIKV_READ_PROBE_SINK_WORDS 8192
+int minikv_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 /* Identity of this build: "sha256:" and the first 16 hex digits of a hash of
  * every kernel and header source it was compiled from (static string). */
 const char *minikv_build_id(void);

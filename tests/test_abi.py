@@ -39,6 +39,16 @@ def test_header_symbols_exported(L):
     assert set(names) == set(_lib.SIGNATURES)
 
 
+def test_read_probe_validation(L):
+    f = L.minikv_read_probe
+    assert f(None, 4096, A, None) == -1
+    assert f(A, 4096, None, None) == -1
+    assert f(A, 0, A, None) == -2
+    assert f(A, 4100, A, None) == -2
+    assert f(A + 4, 4096, A, None) == -4
+    assert f(A, 4096, A + 8, None) == -4
+
+
 def test_status_strings(L):
     for st in range(0, -7, -1):
         assert _lib.status_string(st)
