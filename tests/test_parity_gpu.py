@@ -435,12 +435,13 @@ def _slice_cache(cache, bsel):
                           len(bsel), cache.Hkv, cache.n_keep, cache.D)
 
 
-@pytest.mark.parametrize("B", [64, 256])
+@pytest.mark.parametrize("B", [64, 256, 1133])
 @pytest.mark.parametrize("layer", [0, 39])
 def test_decode_pyramid_layer_sampled(dev, B, layer):
     """LLaMA2-13B-shaped pyramid layer (40 heads, context 8192, budget 30 % -> 5 %): the
     whole batch decoded (several work items per wave; at B = 64 each KV head is split
-    into token ranges), sampled sequences against the oracle."""
+    into token ranges; B = 1133 is the headline's batch and launch, 11 or 12 KV heads per
+    wave, the last sequence in the twelfth round), sampled sequences against the oracle."""
     wl = synth.WORKLOADS["llama13b_pyramid"]
     n = oracle.pyramid_keep(wl.T, wl.layers, layer, *wl.pyramid)
     say("pyramid decode layer", layer, "n", n, "B", B)
