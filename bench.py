@@ -579,7 +579,7 @@ def calibration_copy(torch, mb):
     torch.cuda.empty_cache()
 
 
-def measured_peaks(torch, mk, read_gib=8, gemm_n=8192, reps=10):
+def measured_peaks(torch, mk, read_gib=8, gemm_sizes=(8192, 16384), reps=10):
     """Reference rates of this GPU, the denominators beside the vendor peaks: a
     streaming read (the library's read probe: every 16-byte piece of a buffer
     once, non-temporal), a device copy (bytes read + written), and a large bf16
@@ -606,18 +606,22 @@ def measured_peaks(torch, mk, read_gib=8, gemm_n=8192, reps=10):
     copy_s = timed(lambda: y.copy_(x))
     del x, y, sink
     g = torch.Generator(device=dev).manual_seed(11)
-    a = torch.randn((gemm_n, gemm_n), generator=g, device=dev).to(torch.bfloat16)
-    b = torch.randn((gemm_n, gemm_n), generator=g, device=dev).to(torch.bfloat16)
-    gemm_s = timed(lambda: torch.matmul(a, b))
-    del a, b
+    gemm = {}
+    for m in gemm_sizes:
+        a = torch.randn((m, m), generator=g, device=dev).to(torch.bfloat16)
+        b = torch.randn((m, m), generator=g, device=dev).to(torch.bfloat16)
+        gemm[m] = 2.0 * m ** 3 / timed(lambda: torch.matmul(a, b)) / 1e12
+        del a, b
     torch.cuda.empty_cache()
+    best = max(gemm, key=gemm.get)
     nbytes = n * 2
     return {"hbm_read_GBs": nbytes / read_s / 1e9,
             "read_kind": f"minikv_read_probe over {read_gib} GiB (16-byte non-temporal loads, grid-stride)",
             "hbm_copy_GBs": 2 * nbytes / copy_s / 1e9,
             "copy_kind": f"device copy of {read_gib} GiB (bytes read + written)",
-            "bf16_gemm_TFLOPs": 2.0 * gemm_n ** 3 / gemm_s / 1e12,
-            "gemm_kind": f"torch.matmul {gemm_n} x {gemm_n} x {gemm_n} bf16 (hipBLASLt)"}
+            "bf16_gemm_TFLOPs": gemm[best],
+            "gemm_kind": f"torch.matmul {best} x {best} x {best} bf16 (hipBLASLt), the best of "
+                         + ", ".join(f"{m}^3: {t:.0f}" for m, t in gemm.items())}
 
 
 def chain(torch, mk, synth, args):
