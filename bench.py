@@ -615,13 +615,47 @@ def measured_peaks(torch, mk, read_gib=8, gemm_sizes=(8192, 16384), reps=10):
     torch.cuda.empty_cache()
     best = max(gemm, key=gemm.get)
     nbytes = n * 2
+    # the same probe over a small-batch decode layer's bytes, cold: buffers of that
+    # size rotated over >= 1.2 GB, one launch each, replayed as a HIP graph
+    small = {}
+    for name, size in (("llama7b_decode_layer", mk.packed_bytes(8, 32, 614, 128)),
+                       ("mistral_decode_layer", mk.packed_bytes(4, 8, 6600, 128))):
+        size = (size + 15) // 16 * 16
+        nbuf = max(2, -(-int(1.2e9) // size))
+        bufs = [torch.empty(size // 2, dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(nbuf)]
+        sink = torch.zeros(mk.api.READ_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for x in bufs:
+                mk.read_probe(x, sink)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for x in bufs:
+                mk.read_probe(x, sink)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (3 * nbuf)
+        small[name] = {"bytes": size, "us": us, "GBs": size / us / 1e3}
+        del bufs, sink, graph
+        torch.cuda.empty_cache()
     return {"hbm_read_GBs": nbytes / read_s / 1e9,
             "read_kind": f"minikv_read_probe over {read_gib} GiB (16-byte non-temporal loads, grid-stride)",
             "hbm_copy_GBs": 2 * nbytes / copy_s / 1e9,
             "copy_kind": f"device copy of {read_gib} GiB (bytes read + written)",
             "bf16_gemm_TFLOPs": gemm[best],
             "gemm_kind": f"torch.matmul {best} x {best} x {best} bf16 (hipBLASLt), the best of "
-                         + ", ".join(f"{m}^3: {t:.0f}" for m, t in gemm.items())}
+                         + ", ".join(f"{m}^3: {t:.0f}" for m, t in gemm.items()),
+            "small_reads": small,
+            "small_read_kind": "minikv_read_probe over one small-batch decode layer's packed bytes, cold "
+                               "(buffers rotated over >= 1.2 GB), per launch in a replayed HIP graph"}
 
 
 def chain(torch, mk, synth, args):
