@@ -430,7 +430,12 @@ __global__ __launch_bounds__(128) void quant_pack_kernel(
 // as group n_packed / 32 (the rule of quant_pack_kernel) or, with no capacity
 // left, the overflow flag is raised.  Every workgroup reads the counts before
 // it takes a ticket, so the workgroup that takes the last ticket can advance
-// them: no other launch, no spinning.
+// them: no other launch, no spinning.  The ticket needs no memory fence: each
+// workgroup's reads of the counts have returned before its barrier (every
+// thread's stores depend on them), and what the step writes (rows, packed
+// group, counts) is read by later launches, which the kernel boundary orders.
+// (A device-scope fence here writes back and invalidates the L2 of the
+// workgroup's XCD.)
 template <int D>
 __global__ __launch_bounds__(128) void stream_step_append_kernel(
     const uint32_t* __restrict__ k_new, const uint32_t* __restrict__ v_new, int Hkv, int cap,
@@ -461,7 +466,6 @@ __global__ __launch_bounds__(128) void stream_step_append_kernel(
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        __threadfence();
         const int nwg = (int)(gridDim.y * gridDim.z);
         if (atomicAdd(&counts[3], 1) == nwg - 1) {  // every workgroup has read the counts
             if (ok) {
@@ -475,7 +479,6 @@ __global__ __launch_bounds__(128) void stream_step_append_kernel(
                 }
             }
             counts[3] = 0;
-            __threadfence();
         }
     }
 }
