@@ -842,13 +842,16 @@ def variants(torch, mk, synth):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards per "
-              "(sequence, KV head) with no exchange, but this build measures a single GPU.",
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards per "
+              "(sequence, KV head) with no exchange between GPUs, and only the single-GPU case is timed here.",
               file=sys.stderr)
         sys.exit(2)
 
     import torch
 
+    from bit_quantized_kv_quant_amd import build as _build
+
+    _build.ensure_built()  # only when nothing is built
     import bit_quantized_kv_quant_amd as mk
     import synth
 

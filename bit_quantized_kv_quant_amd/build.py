@@ -103,5 +103,14 @@ def build(verbose=False, extra_flags=(), out=None):
     return lib_path
 
 
+def ensure_built():
+    """Build the library only when none is there (a fresh checkout: the built
+    binary is not version-controlled).  A library built from other sources is
+    left alone; loading it then raises, so stale code is never run silently."""
+    if not os.path.exists(LIB):
+        build()
+    return LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

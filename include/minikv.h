@@ -390,7 +390,7 @@ const char *minikv_status_string(int status);
 #define MINIKV_READ_PROBE_SINK_WORDS 8192
 int minikv_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
-/* Identity of this build: "sha256:" and the first 16 hex digits of a hash of
+/* Identity of the library binary: "sha256:" and the first 16 hex digits of a hash of
  * every kernel and header source it was compiled from (static string). */
 const char *minikv_build_id(void);
 

@@ -8,3 +8,6 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    from bit_quantized_kv_quant_amd import build
+
+    build.ensure_built()  # only when nothing is built
