@@ -342,7 +342,7 @@ class StreamCache:
         return out
 
 
-READ_PROBE_SINK_WORDS = 8192
+READ_PROBE_SINK_WORDS = 131072  # MINIKV_READ_PROBE_SINK_WORDS: one word per wave of the probe's grid
 
 
 def read_probe(x, sink=None):

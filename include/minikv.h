@@ -383,11 +383,11 @@ const char *minikv_status_string(int status);
  * measured reference for the HBM-bound kernels' rooflines.  Every 16-byte
  * piece is read once (non-temporal loads); the XOR of the 32-bit words each
  * wave read goes to sink (device uint32 [MINIKV_READ_PROBE_SINK_WORDS],
- * caller-owned, 16-byte aligned), so the XOR of all sink words is the XOR of
- * every word of the buffer.  Errors: NULL; SHAPE (bytes 0 or not a multiple
+ * caller-owned, 16-byte aligned; words past the launch's waves are left
+ * untouched, so a zeroed sink XORs to the XOR of every word of the buffer).  Errors: NULL; SHAPE (bytes 0 or not a multiple
  * of 16); ALIGN; LAUNCH.
  */
-#define MINIKV_READ_PROBE_SINK_WORDS 8192
+#define MINIKV_READ_PROBE_SINK_WORDS 131072
 int minikv_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
 /* Identity of the library binary: "sha256:" and the first 16 hex digits of a hash of
